@@ -1,0 +1,335 @@
+/*
+ * fp64 CPU oracle for the fused inference attention forward.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the CPU
+ * baseline leg of the benchmark load this library.  It shares no code, header
+ * or table with the GPU library; it is the plain definition written out, one
+ * output row at a time, in double precision.
+ *
+ * What it computes (page "torch_npu.npu_prompt_flash_attention", function
+ * description formula; page "torch_npu.npu_fused_infer_attention_score_v2",
+ * function description formula and the softmax_lse output description):
+ *
+ *   for every batch b, query head h and valid query row i:
+ *     g      = h / (QN / KVN)                  (GQA: contiguous head groups)
+ *     J(i)   = { j < Lkv_b : allowed(b, i, j) }
+ *     s_j    = scale * sum_d q[b,h,i,d] * k[b,g,j,d]
+ *     m      = max_{j in J} s_j
+ *     l      = sum_{j in J} exp(s_j - m)
+ *     out_e  = sum_{j in J} exp(s_j - m) * v[b,g,j,e] / l
+ *     lse    = m + log(l)                       (natural log)
+ *   J(i) empty  ->  out = 0, lse = +inf        (parity unpinned: convention)
+ *   rows past the valid length of a padded layout -> out = 0, lse = +inf
+ *                                               (parity unpinned: convention)
+ *
+ * Masking is set membership, never the addition of -inf, so no NaN can arise
+ * from a masked position and nothing outside J is ever read.
+ *
+ * allowed(b, i, j) follows the sparse_mode list of the v2 parameter
+ * description, with delta = Lkv_b - Lq_b:
+ *   mode 0, no mask : true
+ *   mode 0, mask    : mask[i][j] == 0 and -pre <= j - i <= next
+ *   mode 1          : mask[i][j] == 0
+ *   mode 2          : j <= i                       (top-left causal)
+ *   mode 3          : j <= i + delta               (bottom-right causal)
+ *   mode 4          : -pre <= j - i - delta <= next (bottom-right band)
+ * Decode (query S == 1 outside TND) ignores sparse_mode, pre and next (v2
+ * parameter description of sparse_mode, pre_tokens, next_tokens).
+ * A mask value of nonzero means "masked" (PFA parameter description of
+ * atten_mask: padding is filled with 1).
+ *
+ * Block-sparse (page "aclnnBlockSparseAttentionV2", function description
+ * formula and constraints): allowed(b, h, i, j) =
+ *   M[b, h, i / X, j / Y] != 0 and i < Lq_b and j < Lkv_b,
+ * with no causal mask and no atten_mask; the mask's head axis is the query
+ * head.  The compacted schedule lists, per (b, h, q-block), the selected
+ * kv-blocks kb < ceil(Lkv_b / Y) in ascending order (tail -1).
+ *
+ * Inputs are fp16/bf16 bit patterns, each read as its exact value in double.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+enum { OR_F16 = 0, OR_BF16 = 1 };
+enum { OR_BNSD = 0, OR_BSND = 1, OR_TND = 2 };
+
+/* Exact value of an IEEE binary16 / bfloat16 bit pattern. */
+static double half_bits_to_double(uint16_t h)
+{
+    int sign = (h >> 15) & 1;
+    int e = (h >> 10) & 0x1f;
+    int m = h & 0x3ff;
+    double v;
+    if (e == 0)
+        v = ldexp((double)m, -24);               /* subnormal: m * 2^-24 */
+    else if (e == 31)
+        v = m ? NAN : INFINITY;
+    else
+        v = ldexp((double)(1024 + m), e - 25);   /* (1 + m/1024) * 2^(e-15) */
+    return sign ? -v : v;
+}
+
+static double bf16_bits_to_double(uint16_t h)
+{
+    uint32_t u = ((uint32_t)h) << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+static double elem(const uint16_t* p, int64_t idx, int dtype)
+{
+    return dtype == OR_BF16 ? bf16_bits_to_double(p[idx]) : half_bits_to_double(p[idx]);
+}
+
+/* Exported so a test can check the element reader against a library cast. */
+double oracle_read_half(uint16_t bits, int dtype) { return elem(&bits, 0, dtype); }
+
+typedef struct {
+    int32_t layout;          /* OR_BNSD, OR_BSND (also BSH), OR_TND */
+    int32_t dtype;           /* OR_F16 or OR_BF16 (q, k, v alike) */
+    int64_t B, QN, KVN;
+    int64_t Sq, Skv;         /* padded S axes; TND: total rows */
+    int64_t Dqk, Dv;
+    const int64_t* lq;       /* [B] valid query lengths */
+    const int64_t* lkv;      /* [B] valid kv lengths */
+    const int64_t* q_start;  /* [B] TND first query row of each sequence */
+    const int64_t* kv_start; /* [B] TND first kv row of each sequence */
+    double scale;
+    int32_t sparse_mode;
+    int32_t decode;          /* 1: query S == 1 outside TND */
+    int64_t pre_tokens, next_tokens;
+    const uint8_t* mask;     /* explicit mask or NULL; nonzero = masked */
+    int64_t mask_bstride;    /* elements between batches (0 = broadcast) */
+    int64_t mask_rstride;    /* elements between mask rows */
+    const int32_t* block_table; /* paged KV or NULL */
+    int64_t bt_stride;
+    int64_t block_size;
+    int32_t pool_layout;     /* 0: (NB, KVN, bs, D)  1: (NB, bs, KVN*D) */
+    /* block-sparse */
+    const uint8_t* block_mask;  /* [B, QN, nqb, nkb], nonzero = selected */
+    int64_t nqb, nkb, X, Y;
+    /* optional row subset: n_rows triples (b, h, i); NULL = every row */
+    const int64_t* rows;
+    int64_t n_rows;
+} oracle_args;
+
+static int64_t q_off(const oracle_args* a, int64_t b, int64_t h, int64_t i, int64_t D)
+{
+    switch (a->layout) {
+    case OR_BNSD: return ((b * a->QN + h) * a->Sq + i) * D;
+    case OR_BSND: return ((b * a->Sq + i) * a->QN + h) * D;
+    default:      return ((a->q_start[b] + i) * a->QN + h) * D;
+    }
+}
+
+static int64_t kv_off(const oracle_args* a, int64_t b, int64_t g, int64_t j, int64_t D)
+{
+    if (a->block_table) {
+        int64_t blk = a->block_table[b * a->bt_stride + j / a->block_size];
+        int64_t t = j % a->block_size;
+        if (a->pool_layout == 0)
+            return ((blk * a->KVN + g) * a->block_size + t) * D;
+        return ((blk * a->block_size + t) * a->KVN + g) * D;
+    }
+    switch (a->layout) {
+    case OR_BNSD: return ((b * a->KVN + g) * a->Skv + j) * D;
+    case OR_BSND: return ((b * a->Skv + j) * a->KVN + g) * D;
+    default:      return ((a->kv_start[b] + j) * a->KVN + g) * D;
+    }
+}
+
+static int allowed_dense(const oracle_args* a, int64_t b, int64_t i, int64_t j)
+{
+    if (a->decode)
+        return 1;
+    int64_t delta = a->lkv[b] - a->lq[b];
+    int masked_by_tensor = 0;
+    if (a->mask && (a->sparse_mode == 0 || a->sparse_mode == 1))
+        masked_by_tensor = a->mask[b * a->mask_bstride + i * a->mask_rstride + j] != 0;
+    switch (a->sparse_mode) {
+    case 0:
+        if (!a->mask)
+            return 1;
+        return !masked_by_tensor && (j - i >= -a->pre_tokens) && (j - i <= a->next_tokens);
+    case 1:
+        return !masked_by_tensor;
+    case 2:
+        return j <= i;
+    case 3:
+        return j <= i + delta;
+    case 4:
+        return (j - i - delta >= -a->pre_tokens) && (j - i - delta <= a->next_tokens);
+    default:
+        return 0;
+    }
+}
+
+static int allowed_bsa(const oracle_args* a, int64_t b, int64_t h, int64_t i, int64_t j)
+{
+    int64_t qb = i / a->X, kb = j / a->Y;
+    return a->block_mask[((b * a->QN + h) * a->nqb + qb) * a->nkb + kb] != 0;
+}
+
+/* One output row: out[0..Dv) and *lse.  Returns 0, or -1 on allocation failure. */
+static int one_row(const oracle_args* a, const uint16_t* q, const uint16_t* k,
+                   const uint16_t* v, int bsa, int64_t b, int64_t h, int64_t i,
+                   double* out, double* lse)
+{
+    int64_t e;
+    for (e = 0; e < a->Dv; ++e)
+        out[e] = 0.0;
+    *lse = INFINITY;
+    if (i >= (a->decode ? 1 : a->lq[b]))
+        return 0;                                   /* padding row */
+    int64_t L = a->lkv[b];
+    if (L <= 0)
+        return 0;                                   /* empty kv */
+    int64_t G = a->QN / a->KVN;
+    int64_t g = h / G;
+    double* s = (double*)malloc(sizeof(double) * (size_t)L);
+    unsigned char* in = (unsigned char*)malloc((size_t)L);
+    if (!s || !in) {
+        free(s);
+        free(in);
+        return -1;
+    }
+    const int64_t qo = q_off(a, b, h, i, a->Dqk);
+    double m = -INFINITY;
+    int64_t n_in = 0, j, d;
+    for (j = 0; j < L; ++j) {
+        in[j] = (unsigned char)(bsa ? allowed_bsa(a, b, h, i, j) : allowed_dense(a, b, i, j));
+        if (!in[j])
+            continue;
+        const int64_t ko = kv_off(a, b, g, j, a->Dqk);
+        double acc = 0.0;
+        for (d = 0; d < a->Dqk; ++d)
+            acc += elem(q, qo + d, a->dtype) * elem(k, ko + d, a->dtype);
+        s[j] = a->scale * acc;
+        if (s[j] > m)
+            m = s[j];
+        ++n_in;
+    }
+    if (n_in > 0) {
+        double l = 0.0;
+        for (j = 0; j < L; ++j) {
+            if (!in[j])
+                continue;
+            const double p = exp(s[j] - m);
+            const int64_t vo = kv_off(a, b, g, j, a->Dv);
+            l += p;
+            for (e = 0; e < a->Dv; ++e)
+                out[e] += p * elem(v, vo + e, a->dtype);
+        }
+        for (e = 0; e < a->Dv; ++e)
+            out[e] /= l;
+        *lse = m + log(l);
+    }
+    free(s);
+    free(in);
+    return 0;
+}
+
+/* Output addressing: out follows the query layout with D = Dv; lse is
+ * [B, QN, Sq] (TND: [T, QN]).  With a row subset, out is [n_rows, Dv] and
+ * lse is [n_rows]. */
+static int run(const oracle_args* a, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+               int bsa, double* out, double* lse)
+{
+    int failed = 0;
+    if (a->rows) {
+        int64_t r;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : failed)
+        for (r = 0; r < a->n_rows; ++r) {
+            const int64_t* t = a->rows + 3 * r;
+            failed |= one_row(a, q, k, v, bsa, t[0], t[1], t[2], out + r * a->Dv, lse + r) != 0;
+        }
+        return failed ? -1 : 0;
+    }
+    int64_t n_units, u;
+    int64_t Sq_rows = a->decode ? 1 : a->Sq;
+    if (a->layout == OR_TND)
+        n_units = a->Sq * a->QN;                     /* every (row, head) */
+    else
+        n_units = a->B * a->QN * Sq_rows;
+#pragma omp parallel for schedule(dynamic, 16) reduction(| : failed)
+    for (u = 0; u < n_units; ++u) {
+        int64_t b, h, i, oo, lo;
+        if (a->layout == OR_TND) {
+            int64_t row = u / a->QN;
+            h = u % a->QN;
+            for (b = 0; b + 1 < a->B && a->q_start[b + 1] <= row; ++b) {
+            }
+            i = row - a->q_start[b];
+            if (i >= a->lq[b])
+                continue;                             /* rows past the last sequence */
+            oo = (row * a->QN + h) * a->Dv;
+            lo = row * a->QN + h;
+        } else {
+            b = u / (a->QN * Sq_rows);
+            h = (u / Sq_rows) % a->QN;
+            i = u % Sq_rows;
+            oo = a->layout == OR_BNSD ? ((b * a->QN + h) * a->Sq + i) * a->Dv
+                                      : ((b * a->Sq + i) * a->QN + h) * a->Dv;
+            lo = (b * a->QN + h) * a->Sq + i;
+        }
+        failed |= one_row(a, q, k, v, bsa, b, h, i, out + oo, lse + lo) != 0;
+    }
+    return failed ? -1 : 0;
+}
+
+int oracle_attention(const oracle_args* a, const uint16_t* q, const uint16_t* k,
+                     const uint16_t* v, double* out, double* lse)
+{
+    if (!a || !q || !k || !v || !out || !lse || a->KVN <= 0 || a->QN % a->KVN)
+        return -2;
+    return run(a, q, k, v, 0, out, lse);
+}
+
+int oracle_block_sparse(const oracle_args* a, const uint16_t* q, const uint16_t* k,
+                        const uint16_t* v, double* out, double* lse)
+{
+    if (!a || !q || !k || !v || !out || !lse || !a->block_mask || a->X <= 0 || a->Y <= 0 ||
+        a->KVN <= 0 || a->QN % a->KVN)
+        return -2;
+    return run(a, q, k, v, 1, out, lse);
+}
+
+/* Compacted block schedule: cnt[b,h,qb] and idx[b,h,qb,0..nkb) ascending,
+ * tail -1.  q-blocks at or past ceil(Lq_b / X) get an empty list. */
+int oracle_bsa_compact(const uint8_t* mask, int64_t B, int64_t N, int64_t nqb, int64_t nkb,
+                       const int64_t* lq, const int64_t* lkv, int64_t X, int64_t Y,
+                       int32_t* idx, int32_t* cnt)
+{
+    int64_t b, h, qb, kb;
+    for (b = 0; b < B; ++b) {
+        const int64_t qlim = (lq[b] + X - 1) / X;
+        const int64_t klim = (lkv[b] + Y - 1) / Y;
+        for (h = 0; h < N; ++h) {
+            for (qb = 0; qb < nqb; ++qb) {
+                const int64_t row = (b * N + h) * nqb + qb;
+                int32_t c = 0;
+                for (kb = 0; kb < nkb; ++kb)
+                    idx[row * nkb + kb] = -1;
+                if (qb < qlim)
+                    for (kb = 0; kb < nkb && kb < klim; ++kb)
+                        if (mask[row * nkb + kb])
+                            idx[row * nkb + c++] = (int32_t)kb;
+                cnt[row] = c;
+            }
+        }
+    }
+    return 0;
+}
+
+int oracle_num_threads(void)
+{
+#ifdef _OPENMP
+    extern int omp_get_max_threads(void);
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

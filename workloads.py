@@ -1,0 +1,370 @@
+"""Seeded synthetic inputs for the fused inference attention forward.
+
+This module only draws random numbers and lays them out: lengths, query/key/
+value tensors, paged block tables, block-sparse masks.  It computes nothing of
+the attention method itself.  Both the fp64 oracle (tests) and the HIP path
+read the tensors it returns, so both sides see the same rounded values.
+
+Recipe (one numpy SeedSequence per workload, spawned into six streams in a
+fixed order: lengths, Q, K, V, block table / pool permutation, block mask):
+
+* values: float32 standard normal, rounded to fp16/bf16 (round to nearest
+  even, by torch's dtype conversion).  Large value tensors are drawn with a
+  torch generator seeded from the stream, on the device they are meant for.
+* padded layouts (BNSD/BSND) fill the padding with the same N(0,1) draws, or
+  with NaN when ``nan_padding`` is set (a padding row must never be read).
+* decode block tables take a seeded permutation of the physical pool
+  consecutively; unused entries are -1.
+* block-sparse masks: iid Bernoulli(p) per (q-block, kv-block), then the
+  diagonal block forced on.
+
+The five named workloads follow the workload list of the fused inference
+attention pages' use cases (dense causal prefill, GQA causal prefill, paged GQA
+decode, varlen TND prefill, block-sparse prefill).
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+from typing import Optional
+
+import numpy as np
+import torch
+
+INT_MAX = 2147483647
+
+STREAM_LENGTHS, STREAM_Q, STREAM_K, STREAM_V, STREAM_TABLE, STREAM_MASK = range(6)
+
+
+def _streams(seed: int):
+    return np.random.SeedSequence(seed).spawn(6)
+
+
+def _torch_seed(ss: np.random.SeedSequence) -> int:
+    return int(ss.generate_state(1, dtype=np.uint64)[0] & ((1 << 63) - 1))
+
+
+def normal_tensor(shape, dtype: torch.dtype, ss: np.random.SeedSequence,
+                  device: str = "cpu") -> torch.Tensor:
+    """iid N(0,1) float32 draws rounded to ``dtype`` on ``device``."""
+    g = torch.Generator(device=device)
+    g.manual_seed(_torch_seed(ss))
+    x = torch.randn(*shape, generator=g, device=device, dtype=torch.float32)
+    return x.to(dtype)
+
+
+@dataclass
+class FiaCase:
+    """One fused-infer-attention invocation with its inputs."""
+    name: str
+    layout: str                 # "BNSD" | "BSND" | "BSH" | "TND"
+    dtype: torch.dtype
+    B: int
+    QN: int
+    KVN: int
+    Sq: int                     # padded query S (TND: total query rows T)
+    Skv: int                    # padded kv S (TND: T_kv; paged: unused)
+    Dqk: int
+    Dv: int
+    scale: float
+    sparse_mode: int = 0
+    pre_tokens: int = INT_MAX
+    next_tokens: int = INT_MAX
+    lq: Optional[np.ndarray] = None       # per-batch valid query lengths
+    lkv: Optional[np.ndarray] = None      # per-batch valid kv lengths
+    q: Optional[torch.Tensor] = None
+    k: Optional[torch.Tensor] = None
+    v: Optional[torch.Tensor] = None
+    atten_mask: Optional[torch.Tensor] = None   # uint8/bool, nonzero = masked
+    block_table: Optional[torch.Tensor] = None  # int32 [B, max_blocks]
+    block_size: int = 0
+    pool_layout: int = 0        # 0: (NB, KVN, bs, D)   1: (NB, bs, KVN*D)
+    return_lse: bool = True
+    meta: dict = field(default_factory=dict)
+
+    @property
+    def decode(self) -> bool:
+        return self.layout != "TND" and self.Sq == 1
+
+    def seq_qlen_arg(self):
+        """actual_seq_qlen as the API takes it (cumulative for TND)."""
+        if self.lq is None:
+            return None
+        if self.layout == "TND":
+            return np.cumsum(self.lq).astype(np.int64)
+        return self.lq.astype(np.int64)
+
+    def seq_kvlen_arg(self):
+        if self.lkv is None:
+            return None
+        if self.layout == "TND":
+            return np.cumsum(self.lkv).astype(np.int64)
+        return self.lkv.astype(np.int64)
+
+
+@dataclass
+class BsaCase:
+    """One block-sparse attention invocation with its inputs."""
+    name: str
+    layout: str                 # "BNSD" | "BSND" | "TND"
+    dtype: torch.dtype
+    B: int
+    QN: int
+    KVN: int
+    Sq: int
+    Skv: int
+    D: int
+    X: int
+    Y: int
+    scale: float
+    lq: Optional[np.ndarray] = None
+    lkv: Optional[np.ndarray] = None
+    q: Optional[torch.Tensor] = None
+    k: Optional[torch.Tensor] = None
+    v: Optional[torch.Tensor] = None
+    block_mask: Optional[torch.Tensor] = None   # uint8 [B, QN, nqb, nkb], nonzero = selected
+    return_lse: bool = True
+    meta: dict = field(default_factory=dict)
+
+    def seq_qlen_arg(self):
+        if self.lq is None:
+            return None
+        if self.layout == "TND":
+            return np.cumsum(self.lq).astype(np.int64)
+        return self.lq.astype(np.int64)
+
+    def seq_kvlen_arg(self):
+        if self.lkv is None:
+            return None
+        if self.layout == "TND":
+            return np.cumsum(self.lkv).astype(np.int64)
+        return self.lkv.astype(np.int64)
+
+
+def _shape(layout, B, N, S, D):
+    if layout == "BNSD":
+        return (B, N, S, D)
+    if layout in ("BSND",):
+        return (B, S, N, D)
+    if layout == "BSH":
+        return (B, S, N * D)
+    if layout == "TND":
+        return (S, N, D)
+    raise ValueError(layout)
+
+
+def _fill_padding_nan(t: torch.Tensor, layout: str, lens: np.ndarray, N: int, D: int):
+    """Overwrite every row past a batch's valid length with NaN."""
+    if layout == "TND":
+        return t
+    for b, L in enumerate(lens):
+        L = int(L)
+        if layout == "BNSD":
+            t[b, :, L:, :] = float("nan")
+        elif layout == "BSND":
+            t[b, L:, :, :] = float("nan")
+        elif layout == "BSH":
+            t[b, L:, :] = float("nan")
+    return t
+
+
+def make_fia(name="custom", *, layout="BNSD", dtype=torch.bfloat16, B=1, QN=2, KVN=None,
+             Sq=64, Skv=None, Dqk=64, Dv=None, scale=None, sparse_mode=0,
+             pre_tokens=INT_MAX, next_tokens=INT_MAX, lq=None, lkv=None,
+             mask_kind=None, seed=0, device="cpu", nan_padding=False,
+             return_lse=True) -> FiaCase:
+    """General contiguous-KV case.  ``lq``/``lkv`` are per-batch valid lengths
+    (None = full).  For TND ``Sq``/``Skv`` are recomputed as the totals.
+    ``mask_kind``: None, "template" (2048x2048 lower-triangular template for
+    modes 2/3/4), "random" (iid 0/1 full mask), "zeros", or a callable
+    (b, i, j) -> bool giving "masked"."""
+    KVN = QN if KVN is None else KVN
+    Skv = Sq if Skv is None else Skv
+    Dv = Dqk if Dv is None else Dv
+    scale = 1.0 / math.sqrt(Dqk) if scale is None else scale
+    ss = _streams(seed)
+    if lq is not None:
+        lq = np.asarray(lq, dtype=np.int64)
+    if lkv is not None:
+        lkv = np.asarray(lkv, dtype=np.int64)
+    if layout == "TND":
+        assert lq is not None and lkv is not None
+        Sq, Skv = int(lq.sum()), int(lkv.sum())
+    q = normal_tensor(_shape(layout, B, QN, Sq, Dqk), dtype, ss[STREAM_Q], device)
+    k = normal_tensor(_shape(layout, B, KVN, Skv, Dqk), dtype, ss[STREAM_K], device)
+    v = normal_tensor(_shape(layout, B, KVN, Skv, Dv), dtype, ss[STREAM_V], device)
+    if nan_padding and layout != "TND":
+        if lq is not None:
+            _fill_padding_nan(q, layout, lq, QN, Dqk)
+        if lkv is not None:
+            _fill_padding_nan(k, layout, lkv, KVN, Dqk)
+            _fill_padding_nan(v, layout, lkv, KVN, Dv)
+    mask = None
+    if mask_kind == "template":
+        mask = torch.triu(torch.ones(2048, 2048, dtype=torch.uint8), diagonal=1).to(device)
+    elif mask_kind == "random":
+        rng = np.random.default_rng(ss[STREAM_MASK])
+        mask = torch.from_numpy(rng.integers(0, 2, size=(B, 1, Sq, Skv), dtype=np.uint8)).to(device)
+    elif mask_kind == "zeros":
+        mask = torch.zeros(B, 1, Sq, Skv, dtype=torch.uint8, device=device)
+    elif callable(mask_kind):
+        m = np.zeros((B, 1, Sq, Skv), dtype=np.uint8)
+        for b in range(B):
+            for i in range(Sq):
+                for j in range(Skv):
+                    m[b, 0, i, j] = 1 if mask_kind(b, i, j) else 0
+        mask = torch.from_numpy(m).to(device)
+    return FiaCase(name=name, layout=layout, dtype=dtype, B=B, QN=QN, KVN=KVN, Sq=Sq, Skv=Skv,
+                   Dqk=Dqk, Dv=Dv, scale=scale, sparse_mode=sparse_mode,
+                   pre_tokens=pre_tokens, next_tokens=next_tokens, lq=lq, lkv=lkv,
+                   q=q, k=k, v=v, atten_mask=mask, return_lse=return_lse)
+
+
+def make_paged_decode(name="custom", *, dtype=torch.bfloat16, B=2, QN=4, KVN=2, D=64,
+                      lkv=(100, 37), block_size=16, pool_layout=0, scale=None, seed=0,
+                      device="cpu", q_layout="BNSD", extra_blocks=0, table_cols=None,
+                      return_lse=True) -> FiaCase:
+    """Paged decode: Q_S = 1, K/V in a shared physical pool addressed through a
+    block table holding a seeded permutation of the pool's block ids."""
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    ss = _streams(seed)
+    lkv = np.asarray(lkv, dtype=np.int64)
+    nblk = [(int(L) + block_size - 1) // block_size for L in lkv]
+    NB = sum(nblk) + extra_blocks
+    cols = max(max(nblk), 1) if table_cols is None else table_cols
+    rng = np.random.default_rng(ss[STREAM_TABLE])
+    perm = rng.permutation(NB).astype(np.int32)
+    table = np.full((B, cols), -1, dtype=np.int32)
+    pos = 0
+    for b in range(B):
+        table[b, :nblk[b]] = perm[pos:pos + nblk[b]]
+        pos += nblk[b]
+    qshape = (B, QN, 1, D) if q_layout == "BNSD" else ((B, 1, QN, D) if q_layout == "BSND" else (B, 1, QN * D))
+    q = normal_tensor(qshape, dtype, ss[STREAM_Q], device)
+    pshape = (NB, KVN, block_size, D) if pool_layout == 0 else (NB, block_size, KVN * D)
+    k = normal_tensor(pshape, dtype, ss[STREAM_K], device)
+    v = normal_tensor(pshape, dtype, ss[STREAM_V], device)
+    return FiaCase(name=name, layout=q_layout, dtype=dtype, B=B, QN=QN, KVN=KVN, Sq=1,
+                   Skv=cols * block_size, Dqk=D, Dv=D, scale=scale, lq=None, lkv=lkv,
+                   q=q, k=k, v=v, block_table=torch.from_numpy(table).to(device),
+                   block_size=block_size, pool_layout=pool_layout, return_lse=return_lse,
+                   meta={"NB": NB})
+
+
+def make_bsa(name="custom", *, layout="BNSD", dtype=torch.bfloat16, B=1, QN=2, KVN=1,
+             Sq=256, Skv=None, D=64, X=128, Y=128, p=0.25, lq=None, lkv=None, scale=None,
+             seed=0, device="cpu", mask_kind="bernoulli", return_lse=True) -> BsaCase:
+    """Block-sparse case; ``mask_kind``: "bernoulli" (iid p, diagonal forced),
+    "ones", "diag", "lower" (block lower-triangular), or an explicit array."""
+    Skv = Sq if Skv is None else Skv
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    ss = _streams(seed)
+    if lq is not None:
+        lq = np.asarray(lq, dtype=np.int64)
+    if lkv is not None:
+        lkv = np.asarray(lkv, dtype=np.int64)
+    if layout == "TND":
+        Sq, Skv = int(lq.sum()), int(lkv.sum())
+        maxq, maxkv = int(lq.max()), int(lkv.max())
+    else:
+        maxq, maxkv = Sq, Skv
+    nqb, nkb = -(-maxq // X), -(-maxkv // Y)
+    q = normal_tensor(_shape(layout, B, QN, Sq, D), dtype, ss[STREAM_Q], device)
+    k = normal_tensor(_shape(layout, B, KVN, Skv, D), dtype, ss[STREAM_K], device)
+    v = normal_tensor(_shape(layout, B, KVN, Skv, D), dtype, ss[STREAM_V], device)
+    if isinstance(mask_kind, np.ndarray):
+        m = mask_kind.astype(np.uint8)
+    elif mask_kind == "bernoulli":
+        rng = np.random.default_rng(ss[STREAM_MASK])
+        m = (rng.random((B, QN, nqb, nkb)) < p).astype(np.uint8)
+        for i in range(min(nqb, nkb)):
+            m[:, :, i, i] = 1
+    elif mask_kind == "ones":
+        m = np.ones((B, QN, nqb, nkb), dtype=np.uint8)
+    elif mask_kind == "diag":
+        m = np.zeros((B, QN, nqb, nkb), dtype=np.uint8)
+        for i in range(min(nqb, nkb)):
+            m[:, :, i, i] = 1
+    elif mask_kind == "lower":
+        m = np.tril(np.ones((nqb, nkb), dtype=np.uint8))[None, None].repeat(B, 0).repeat(QN, 1)
+    else:
+        raise ValueError(mask_kind)
+    return BsaCase(name=name, layout=layout, dtype=dtype, B=B, QN=QN, KVN=KVN, Sq=Sq, Skv=Skv,
+                   D=D, X=X, Y=Y, scale=scale, lq=lq, lkv=lkv, q=q, k=k, v=v,
+                   block_mask=torch.from_numpy(np.ascontiguousarray(m)).to(device),
+                   return_lse=return_lse)
+
+
+# ---------------------------------------------------------------------------
+# The five named workloads.
+# ---------------------------------------------------------------------------
+
+def c1_dense_causal_fp16(device="cpu") -> FiaCase:
+    """B=1, Q_N=KV_N=2, S=128, D=64, fp16, BNSD, causal (sparse_mode 3 with the
+    2048x2048 lower-triangular template), scale 1/8, LSE on."""
+    return make_fia("dense_causal_prefill_fp16_b1_n2_s128_d64", layout="BNSD",
+                    dtype=torch.float16, B=1, QN=2, KVN=2, Sq=128, Dqk=64,
+                    scale=1.0 / 8.0, sparse_mode=3, mask_kind="template", seed=1001,
+                    device=device)
+
+
+def c2_lengths():
+    rng = np.random.default_rng(_streams(1002)[STREAM_LENGTHS])
+    return rng.integers(1024, 4096, size=4, endpoint=True).astype(np.int64)
+
+
+def c2_gqa_causal_bf16(device="cpu", nan_padding=False) -> FiaCase:
+    """B=4, Q_N=32, KV_N=8, max S=4096, D=128, bf16, BSND, per-batch
+    actual_seq_qlen = actual_seq_kvlen ~ U{1024..4096}, causal (mode 3)."""
+    L = c2_lengths()
+    return make_fia("gqa_causal_prefill_bf16_b4_n32_kv8_s4096_d128", layout="BSND",
+                    dtype=torch.bfloat16, B=4, QN=32, KVN=8, Sq=4096, Dqk=128,
+                    scale=1.0 / math.sqrt(128), sparse_mode=3, mask_kind="template",
+                    lq=L, lkv=L, seed=1002, device=device, nan_padding=nan_padding)
+
+
+def c3_lengths():
+    rng = np.random.default_rng(_streams(1003)[STREAM_LENGTHS])
+    return rng.integers(512, 32768, size=64, endpoint=True).astype(np.int64)
+
+
+def c3_paged_decode_bf16(device="cpu") -> FiaCase:
+    """B=64, Q_S=1, Q_N=32, KV_N=8, D=128, bf16, KV lengths ~ U{512..32768},
+    page 128 tokens, pool layout (NB, KV_N, 128, 128), LSE on."""
+    L = c3_lengths()
+    return make_paged_decode("paged_gqa_decode_bf16_b64_n32_kv8_d128_bs128", dtype=torch.bfloat16,
+                             B=64, QN=32, KVN=8, D=128, lkv=L, block_size=128, pool_layout=0,
+                             seed=1003, device=device)
+
+
+def c4_lengths():
+    rng = np.random.default_rng(_streams(1004)[STREAM_LENGTHS])
+    x = np.exp(rng.normal(math.log(1024.0), 1.0, size=16))
+    return np.clip(np.rint(x), 64, 8192).astype(np.int64)
+
+
+def c4_varlen_tnd_bf16(device="cpu") -> FiaCase:
+    """16 sequences, lengths lognormal(median 1024, sigma 1) clipped to
+    [64, 8192], TND, Q_N=KV_N=16, D_qk=192, D_v=128, causal, bf16."""
+    L = c4_lengths()
+    return make_fia("varlen_tnd_prefill_bf16_16seq_n16_d192_dv128", layout="TND",
+                    dtype=torch.bfloat16, B=16, QN=16, KVN=16, Dqk=192, Dv=128,
+                    scale=1.0 / math.sqrt(192), sparse_mode=3, mask_kind="template",
+                    lq=L, lkv=L, seed=1004, device=device)
+
+
+def c5_block_sparse_bf16(device="cpu") -> BsaCase:
+    """B=1, Q_N=32, KV_N=8, S=32768, D=128, BNSD, block [128,128], mask
+    Bernoulli(0.25) with the diagonal forced on, bf16, LSE on."""
+    return make_bsa("block_sparse_prefill_bf16_b1_n32_kv8_s32768_d128", layout="BNSD",
+                    dtype=torch.bfloat16, B=1, QN=32, KVN=8, Sq=32768, D=128, X=128, Y=128,
+                    p=0.25, seed=1005, device=device)
+
+
+WORKLOADS = {
+    "c1": c1_dense_causal_fp16,
+    "c2": c2_gqa_causal_bf16,
+    "c3": c3_paged_decode_bf16,
+    "c4": c4_varlen_tnd_bf16,
+    "c5": c5_block_sparse_bf16,
+}
