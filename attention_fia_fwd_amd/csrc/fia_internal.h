@@ -1,0 +1,143 @@
+// Internal definitions shared by the host planner (fia_plan.cpp) and the
+// gfx950 kernels (fia_kernels.hip).  Not part of the public ABI.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+#include <vector>
+
+#include "fia.h"
+
+namespace fia {
+
+enum Kind : int32_t { KIND_EMPTY = 0, KIND_PREFILL = 1, KIND_DECODE = 2, KIND_BSA = 3 };
+enum Layout : int32_t { LAYOUT_BNSD = 0, LAYOUT_BSND = 1, LAYOUT_TND = 2 };
+
+// Rows of the attention tiles (query rows per workgroup) and kv tokens per
+// inner step of the prefill / block-sparse kernel.
+constexpr int kBlockM = 128;
+constexpr int kBlockN = 64;
+// Tokens per inner step of the decode kernel; a decode split is a multiple.
+constexpr int kDecodeStep = 32;
+// Query heads one decode wave serves (a GQA group is cut into chunks of this).
+constexpr int kDecodeHeads = 16;
+// Compute units of one MI355X, used only to size the decode split plan.
+constexpr int kNumCUs = 256;
+
+// Per-batch addressing, 24 bytes.  row0 is the first row of batch b on the
+// tensor's row axis: b * S for BNSD/BSND, the cumulative start for TND.
+struct BatchInfo {
+    int64_t q_row0;
+    int64_t kv_row0;
+    int32_t lq;
+    int32_t lkv;
+};
+
+// One prefill / block-sparse workgroup: query rows [q0, q1) of head h of
+// batch b.  Rows at or past the batch's length (padding of BNSD/BSND) are
+// written as out = 0, lse = +inf; rows at or past q1 are not touched.
+struct Tile {
+    int32_t b, h, q0, q1;
+};
+
+struct AttnArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* o;
+    float* lse;
+    const uint8_t* mask;           // explicit mask (modes 0/1), nonzero = masked
+    int64_t mask_bstride;          // elements between batches (0 = broadcast)
+    int64_t mask_rstride;          // elements between rows
+    const Tile* tiles;             // workspace
+    const BatchInfo* batch;        // workspace
+    const int32_t* bsa_cnt;        // block-sparse schedule (workspace)
+    const int32_t* bsa_idx;
+    int32_t nqb, nkb, bx, by;      // block-sparse block counts and shape
+    // element strides: head axis (sH) and sequence axis (sS)
+    int64_t q_sH, q_sS, k_sH, k_sS, v_sH, v_sS, o_sH, o_sS, lse_sH, lse_sS;
+    // row0 multipliers: base offset of batch b = row0 * mult
+    int64_t q_rowmul, k_rowmul, v_rowmul, o_rowmul, lse_rowmul;
+    int32_t QN, KVN, G;
+    float scale_log2;              // scale_value * log2(e)
+    int32_t mode;                  // sparse_mode 0..4
+    int32_t has_mask;
+    int64_t pre, next;
+    int32_t return_lse;
+    int32_t n_tiles;
+};
+
+// Decode: one wave per work item (batch b, kv head, head chunk, kv split).
+struct DecBatch {
+    int64_t kv_row0;     // contiguous KV: first row of batch b
+    int32_t lkv;
+    int32_t item0;       // first work item of batch b
+    int32_t nsplit;      // kv splits of batch b
+    int32_t pad;
+};
+
+struct DecodeArgs {
+    const void* q;                 // [B, QN, 1, D] / [B, 1, QN, D] / [B, 1, QN*D]
+    const void* k;
+    const void* v;
+    void* o;
+    float* lse;                    // [B, QN, 1, 1]
+    const int32_t* block_table;    // paged only
+    int64_t bt_stride;
+    int32_t block_size;            // paged only
+    int32_t paged;
+    // paged pool strides (elements): block, kv head, token
+    int64_t p_blk, p_head, p_tok;
+    // contiguous strides (elements): head, token, and row0 multiplier
+    int64_t c_head, c_tok, c_rowmul;
+    const DecBatch* batch;         // workspace
+    float* part_o;                 // [n_items, Gc, Dv]
+    float* part_lse;               // [n_items, Gc]
+    int32_t B, QN, KVN, G, Gc, nhc;
+    int32_t chunk;                 // kv tokens per split
+    int32_t n_items;
+    float scale_log2;
+    int32_t return_lse;
+};
+
+}  // namespace fia
+
+struct fia_plan {
+    int32_t kind = fia::KIND_EMPTY;
+    int32_t dtype = FIA_BF16;
+    int32_t layout = fia::LAYOUT_BNSD;
+    int64_t B = 0, QN = 0, KVN = 0, G = 0, Sq = 0, Skv = 0, Dqk = 0, Dv = 0;
+
+    // Schedule tables, copied to the head of the workspace by each run.
+    std::vector<unsigned char> host_tables;
+    void* pinned_tables = nullptr;   // pinned copy of host_tables when available
+    void* copy_done = nullptr;       // event recorded after the last schedule copy
+    uint64_t tables_bytes = 0;
+    uint64_t workspace_bytes = 0;
+
+    // byte offsets inside the workspace
+    uint64_t off_batch = 0, off_tiles = 0;
+    uint64_t off_part_o = 0, off_part_lse = 0;
+    uint64_t off_cnt = 0, off_idx = 0;
+
+    int64_t n_tiles = 0;     // prefill / block-sparse workgroups
+    int64_t n_items = 0;     // decode waves
+    int64_t n_rows = 0;      // block-sparse compaction rows (B * N1 * nqb)
+
+    fia::AttnArgs attn{};
+    fia::DecodeArgs dec{};
+    const uint8_t* bsa_mask = nullptr;
+    int64_t bsa_nqb = 0, bsa_nkb = 0;
+};
+
+namespace fia {
+// Kernel launchers (fia_kernels.hip).  Return 0 on success, else a HIP error.
+int launch_prefill(const fia_plan& p, const AttnArgs& a, void* stream);
+int launch_decode(const fia_plan& p, const DecodeArgs& a, void* stream);
+int launch_bsa(const fia_plan& p, const AttnArgs& a, void* stream);
+int copy_tables(void* dst, const void* src, uint64_t bytes, void* stream);
+void* alloc_pinned(uint64_t bytes);
+void free_pinned(void* ptr);
+int record_copy_done(void** event, void* stream);
+void wait_and_release(void* event);
+}  // namespace fia

@@ -1,0 +1,765 @@
+// gfx950 (CDNA4) kernels of the fused inference attention forward.
+//
+//   attn_fwd        prefill and block-sparse prefill: one workgroup of 4
+//                   waves per 128 query rows of one head; K and V tiles of 64
+//                   tokens staged through LDS (double buffered); S^T = K Q^T
+//                   and O^T = V^T P^T on v_mfma_f32_32x32x16_{bf16,f16}; fp32
+//                   online softmax in registers; optional LSE.
+//   decode_split    decode: one wave per (batch, kv head, head chunk, kv
+//                   split); the GQA heads sharing a kv head are the 16
+//                   columns of v_mfma_f32_16x16x32, so every K/V byte is read
+//                   once; pages are gathered through the block table.
+//   decode_combine  merges the splits of one (batch, head) by their LSE.
+//   bsa_compact     compacts the block-sparse mask into ascending kv-block
+//                   lists per (batch, head, q block).
+//
+// The method: pages "torch_npu.npu_prompt_flash_attention" (formula),
+// "torch_npu.npu_fused_infer_attention_score_v2" (formula, sparse_mode,
+// softmax_lse), "aclnnBlockSparseAttentionV2" (formula, constraints).  The
+// online-softmax rescaling and the split-KV merge by LSE rest on the identity
+// the softmax_lse output description gives: a row's log-sum-exp lets partial
+// results over disjoint key sets be merged exactly.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "fia_internal.h"
+
+namespace fia {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
+typedef _Float16 f16x8 __attribute__((__vector_size__(8 * sizeof(_Float16))));
+typedef __bf16 bf16x2 __attribute__((__vector_size__(2 * sizeof(__bf16))));
+typedef _Float16 f16x2 __attribute__((__vector_size__(2 * sizeof(_Float16))));
+typedef float f32x2 __attribute__((__vector_size__(2 * sizeof(float))));
+typedef float f32x4 __attribute__((__vector_size__(4 * sizeof(float))));
+typedef float f32x16 __attribute__((__vector_size__(16 * sizeof(float))));
+
+constexpr float kLn2 = 0.69314718055994530942f;
+
+// Per-dtype MFMA and conversions (round to nearest even).
+template <int DT>
+struct Ops;
+
+template <>
+struct Ops<FIA_BF16> {
+    static __device__ __forceinline__ f32x16 mma32(uint4 a, uint4 b, f32x16 c)
+    {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ f32x4 mma16(uint4 a, uint4 b, f32x4 c)
+    {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ uint32_t pack2(float x, float y)
+    {
+        f32x2 v = {x, y};
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+    }
+};
+
+template <>
+struct Ops<FIA_F16> {
+    static __device__ __forceinline__ f32x16 mma32(uint4 a, uint4 b, f32x16 c)
+    {
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                      __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ f32x4 mma16(uint4 a, uint4 b, f32x4 c)
+    {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                      __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ uint32_t pack2(float x, float y)
+    {
+        f32x2 v = {x, y};
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
+    }
+};
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ uint32_t sel_lo(uint32_t a, uint32_t b)
+{
+    // {a.lo16, b.lo16}
+    return __builtin_amdgcn_perm(b, a, 0x05040100u);
+}
+__device__ __forceinline__ uint32_t sel_hi(uint32_t a, uint32_t b)
+{
+    // {a.hi16, b.hi16}
+    return __builtin_amdgcn_perm(b, a, 0x07060302u);
+}
+
+__device__ __forceinline__ uint32_t dw(const uint4& v, int i)
+{
+    return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w));
+}
+
+// Position of kv token t inside a transposed V tile row.  Within each group
+// of 16 tokens, bits 2 and 3 of the index are swapped, so that the 8 tokens
+// one MFMA lane needs for P V are contiguous (16-byte LDS read).
+__device__ __forceinline__ int vpos16(int t)
+{
+    return (t & ~15) | (((t >> 2) & 1) << 3) | (((t >> 3) & 1) << 2) | (t & 3);
+}
+
+// Position of token t (0..31) in a decode V tile row: tokens 16a + 4c + r
+// go to 8c + 4a + r.
+__device__ __forceinline__ int vpos32(int t)
+{
+    return (((t >> 2) & 3) << 3) | (((t >> 4) & 1) << 2) | (t & 3);
+}
+
+// Whether key j may be attended by query row i (sparse_mode list of the v2
+// parameter description; delta = Lkv - Lq).  Rows >= qend and keys >= lkv are
+// never allowed.
+__device__ __forceinline__ bool allowed(const AttnArgs& a, int mode, int64_t i, int64_t j,
+                                        int64_t delta, const uint8_t* mrow)
+{
+    switch (mode) {
+    case 0:
+        if (!mrow) return true;
+        return mrow[j] == 0 && (j - i >= -a.pre) && (j - i <= a.next);
+    case 1: return mrow[j] == 0;
+    case 2: return j <= i;
+    case 3: return j <= i + delta;
+    case 4: return (j - i - delta >= -a.pre) && (j - i - delta <= a.next);
+    default: return false;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Prefill / block-sparse attention.
+// ---------------------------------------------------------------------------
+template <int DT, int DQK, int DV, bool BSA>
+__global__ __launch_bounds__(256, 2) void attn_fwd(AttnArgs a)
+{
+    constexpr int BN = kBlockN;            // 64 kv tokens per tile
+    constexpr int KP = DQK + 8;            // K tile row pitch (elements)
+    constexpr int VP = BN + 8;             // transposed V tile row pitch
+    constexpr int KT = BN * KP;
+    constexpr int STAGE = KT + DV * VP;
+    constexpr int NQ = DQK / 16;           // k-steps of S^T = K Q^T
+    constexpr int NO = DV / 32;            // 32-row d tiles of O^T
+    constexpr int NKS = DQK / 32;          // 16-byte K chunks staged per thread
+    constexpr int NVU = 2 * DV;            // V staging units (4 rows x 8 d)
+    using O = Ops<DT>;
+
+    extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
+
+    const int tid = threadIdx.x;
+    const int w = tid >> 6;
+    const int lane = tid & 63;
+    const int l32 = lane & 31;
+    const int hh = lane >> 5;
+
+    const Tile t = a.tiles[blockIdx.x];
+    const BatchInfo bi = a.batch[t.b];
+    const int h = t.h;
+    const int q0 = t.q0, q1 = t.q1;
+    const int Lq = bi.lq, Lkv = bi.lkv;
+    const int g = h / a.G;
+    const int qend = min(q1, Lq);
+    const int64_t delta = (int64_t)Lkv - Lq;
+    const int mode = a.mode;
+
+    const uint16_t* qp = (const uint16_t*)a.q + bi.q_row0 * a.q_rowmul + (int64_t)h * a.q_sH;
+    const uint16_t* kp = (const uint16_t*)a.k + bi.kv_row0 * a.k_rowmul + (int64_t)g * a.k_sH;
+    const uint16_t* vp = (const uint16_t*)a.v + bi.kv_row0 * a.v_rowmul + (int64_t)g * a.v_sH;
+    const uint8_t* mbase = a.has_mask ? a.mask + (int64_t)t.b * a.mask_bstride : nullptr;
+
+    const int wr0 = q0 + 32 * w;           // first row of this wave
+    const int row = wr0 + l32;             // this lane's query row
+    const int wend = min(wr0 + 32, qend);  // rows < wend are computed
+
+    // Q as the B operand of S^T = K Q^T: lane (row, hh) holds d = 16s + 8hh.
+    uint4 qf[NQ];
+    if (row < qend) {
+        const uint16_t* src = qp + (int64_t)row * a.q_sS + 8 * hh;
+#pragma unroll
+        for (int s = 0; s < NQ; ++s) qf[s] = *(const uint4*)(src + 16 * s);
+    } else {
+#pragma unroll
+        for (int s = 0; s < NQ; ++s) qf[s] = make_uint4(0, 0, 0, 0);
+    }
+
+    // kv tiles of this workgroup
+    int ntiles = 0;
+    int64_t kv_lo = 0;
+    const int32_t* blist = nullptr;
+    int per = 1;
+    if (BSA) {
+        const int qb = q0 / a.bx;
+        const int64_t rowi = ((int64_t)t.b * a.QN + h) * a.nqb + qb;
+        per = a.by / BN;
+        ntiles = qend > q0 ? a.bsa_cnt[rowi] * per : 0;
+        blist = a.bsa_idx + rowi * a.nkb;
+    } else if (qend > q0 && Lkv > 0) {
+        const int64_t last = qend - 1;
+        int64_t lo = 0, hi = Lkv;
+        if (mode == 0 && mbase) {
+            lo = max((int64_t)0, (int64_t)q0 - a.pre);
+            hi = min((int64_t)Lkv, last + a.next + 1);
+        } else if (mode == 2) {
+            hi = min((int64_t)Lkv, last + 1);
+        } else if (mode == 3) {
+            hi = min((int64_t)Lkv, last + delta + 1);
+        } else if (mode == 4) {
+            lo = max((int64_t)0, (int64_t)q0 + delta - a.pre);
+            hi = min((int64_t)Lkv, last + delta + a.next + 1);
+        }
+        if (hi > lo) {
+            kv_lo = lo / BN * BN;
+            ntiles = (int)((hi - kv_lo + BN - 1) / BN);
+        }
+    }
+    auto tile_c0 = [&](int it) -> int64_t {
+        if (BSA) return (int64_t)blist[it / per] * a.by + (int64_t)BN * (it % per);
+        return kv_lo + (int64_t)BN * it;
+    };
+
+    // staging registers
+    uint4 kst[NKS];
+    uint4 vst[4];
+    const bool vunit = tid < NVU;
+    const int kv4 = tid & 15, vdc = tid >> 4;
+
+    auto load_tile = [&](int64_t c0) {
+#pragma unroll
+        for (int u = 0; u < NKS; ++u) {
+            const int ci = tid + 256 * u;
+            const int r = ci / (DQK / 8), cc = ci % (DQK / 8);
+            const int64_t j = c0 + r;
+            kst[u] = j < Lkv ? *(const uint4*)(kp + j * a.k_sS + 8 * cc) : make_uint4(0, 0, 0, 0);
+        }
+        if (vunit) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int64_t j = c0 + 4 * kv4 + r;
+                vst[r] = j < Lkv ? *(const uint4*)(vp + j * a.v_sS + 8 * vdc) : make_uint4(0, 0, 0, 0);
+            }
+        }
+    };
+    auto store_tile = [&](int buf) {
+        uint16_t* ks = smem + buf * STAGE;
+        uint16_t* vs = ks + KT;
+#pragma unroll
+        for (int u = 0; u < NKS; ++u) {
+            const int ci = tid + 256 * u;
+            const int r = ci / (DQK / 8), cc = ci % (DQK / 8);
+            *(uint4*)(ks + r * KP + 8 * cc) = kst[u];
+        }
+        if (vunit) {
+            const int pos = vpos16(4 * kv4);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const uint32_t d0 = dw(vst[0], e >> 1), d1 = dw(vst[1], e >> 1);
+                const uint32_t d2 = dw(vst[2], e >> 1), d3 = dw(vst[3], e >> 1);
+                uint2 pr;
+                pr.x = (e & 1) ? sel_hi(d0, d1) : sel_lo(d0, d1);
+                pr.y = (e & 1) ? sel_hi(d2, d3) : sel_lo(d2, d3);
+                *(uint2*)(vs + (8 * vdc + e) * VP + pos) = pr;
+            }
+        }
+    };
+
+    f32x16 acc[NO];
+#pragma unroll
+    for (int o = 0; o < NO; ++o)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[o][r] = 0.f;
+    float m = -INFINITY, l = 0.f;
+
+    if (ntiles > 0) load_tile(tile_c0(0));
+    for (int it = 0; it < ntiles; ++it) {
+        const int buf = it & 1;
+        store_tile(buf);
+        __syncthreads();
+        const int64_t c0 = tile_c0(it);
+        if (it + 1 < ntiles) load_tile(tile_c0(it + 1));
+
+        // Which part of this tile the wave's rows may see.
+        bool skip = wend <= wr0 || c0 >= Lkv;
+        bool full = !skip && (c0 + BN <= Lkv) && (wend - wr0 == 32);
+        if (!BSA && !skip) {
+            const int64_t r0 = wr0, r1 = wend - 1, cl = c0 + BN - 1;
+            switch (mode) {
+            case 0:
+                if (mbase) {
+                    full = false;
+                    skip = cl < r0 - a.pre || c0 > r1 + a.next;
+                }
+                break;
+            case 1: full = false; break;
+            case 2: skip = c0 > r1; full = full && cl <= r0; break;
+            case 3: skip = c0 > r1 + delta; full = full && cl <= r0 + delta; break;
+            case 4:
+                skip = cl < r0 + delta - a.pre || c0 > r1 + delta + a.next;
+                full = full && c0 >= r1 + delta - a.pre && cl <= r0 + delta + a.next;
+                break;
+            default: break;
+            }
+        }
+        if (!skip) {
+            const uint16_t* ks = smem + buf * STAGE;
+            const uint16_t* vs = ks + KT;
+            f32x16 s0, s1;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) s0[r] = s1[r] = 0.f;
+#pragma unroll
+            for (int s = 0; s < NQ; ++s) {
+                const uint4 ka0 = *(const uint4*)(ks + l32 * KP + 16 * s + 8 * hh);
+                const uint4 ka1 = *(const uint4*)(ks + (32 + l32) * KP + 16 * s + 8 * hh);
+                s0 = O::mma32(ka0, qf[s], s0);
+                s1 = O::mma32(ka1, qf[s], s1);
+            }
+            float x[32];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                x[r] = s0[r] * a.scale_log2;
+                x[16 + r] = s1[r] * a.scale_log2;
+            }
+            if (!full) {
+                const uint8_t* mrow = mbase ? mbase + (int64_t)row * a.mask_rstride : nullptr;
+#pragma unroll
+                for (int r = 0; r < 32; ++r) {
+                    const int rr = r & 15;
+                    const int64_t j = c0 + 32 * (r >> 4) + 8 * (rr >> 2) + 4 * hh + (rr & 3);
+                    bool ok = row < qend && j < Lkv;
+                    if (!BSA && ok) ok = allowed(a, mode, row, j, delta, mrow);
+                    if (!ok) x[r] = -INFINITY;
+                }
+            }
+            float mt = x[0];
+#pragma unroll
+            for (int r = 1; r < 32; ++r) mt = fmaxf(mt, x[r]);
+            mt = fmaxf(mt, __shfl_xor(mt, 32));
+            const float mn = fmaxf(m, mt);
+            const float mu = mn == -INFINITY ? 0.f : mn;
+            const float alpha = fast_exp2(m - mu);
+            float ps = 0.f;
+#pragma unroll
+            for (int r = 0; r < 32; ++r) {
+                x[r] = fast_exp2(x[r] - mu);
+                ps += x[r];
+            }
+            l = l * alpha + ps;
+            m = mn;
+#pragma unroll
+            for (int o = 0; o < NO; ++o)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[o][r] *= alpha;
+            uint4 pb[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                pb[k].x = O::pack2(x[8 * k + 0], x[8 * k + 1]);
+                pb[k].y = O::pack2(x[8 * k + 2], x[8 * k + 3]);
+                pb[k].z = O::pack2(x[8 * k + 4], x[8 * k + 5]);
+                pb[k].w = O::pack2(x[8 * k + 6], x[8 * k + 7]);
+            }
+#pragma unroll
+            for (int o = 0; o < NO; ++o)
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const uint4 va = *(const uint4*)(vs + (32 * o + l32) * VP + 16 * k + 8 * hh);
+                    acc[o] = O::mma32(va, pb[k], acc[o]);
+                }
+        }
+    }
+
+    // epilogue: rows < q1 are written; rows in [qend, q1) and rows with no
+    // allowed key get out = 0 and lse = +inf.
+    const float lt = l + __shfl_xor(l, 32);
+    if (row < q1) {
+        const bool valid = row < qend && lt > 0.f;
+        const float inv = valid ? 1.f / lt : 0.f;
+        uint16_t* op = (uint16_t*)a.o + bi.q_row0 * a.o_rowmul + (int64_t)h * a.o_sH +
+                       (int64_t)row * a.o_sS;
+#pragma unroll
+        for (int o = 0; o < NO; ++o)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                uint2 v;
+                v.x = O::pack2(acc[o][4 * g4 + 0] * inv, acc[o][4 * g4 + 1] * inv);
+                v.y = O::pack2(acc[o][4 * g4 + 2] * inv, acc[o][4 * g4 + 3] * inv);
+                *(uint2*)(op + 32 * o + 8 * g4 + 4 * hh) = v;
+            }
+        if (a.return_lse && hh == 0) {
+            float* lp = a.lse + bi.q_row0 * a.lse_rowmul + (int64_t)h * a.lse_sH +
+                        (int64_t)row * a.lse_sS;
+            *lp = valid ? (m + __log2f(lt)) * kLn2 : INFINITY;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Decode: split-KV attention over (optionally paged) K/V.
+// ---------------------------------------------------------------------------
+template <int DT, int D>
+__global__ __launch_bounds__(64) void decode_split(DecodeArgs a)
+{
+    constexpr int ST = kDecodeStep;       // 32 tokens per step
+    constexpr int VP = ST + 8;            // transposed V row pitch (elements)
+    constexpr int NK = D / 32;            // k-steps of S^T = K Q^T
+    constexpr int NO = D / 16;            // 16-row d tiles of O^T
+    constexpr int NVU = D / 64;           // V staging units per lane (4 tokens x 8 d)
+    using O = Ops<DT>;
+    __shared__ __attribute__((aligned(16))) uint16_t vt[2][D * VP];
+
+    const int lane = threadIdx.x;
+    const int n = lane & 15, qd = lane >> 4;
+    const int item = blockIdx.x;
+
+    // batch of this item: last b with item0 <= item
+    int lo = 0, hi = a.B - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (a.batch[mid].item0 <= item) lo = mid; else hi = mid - 1;
+    }
+    const int b = lo;
+    const DecBatch db = a.batch[b];
+    const int rel = item - db.item0;
+    const int split = rel % db.nsplit;
+    const int rest = rel / db.nsplit;
+    const int hc = rest % a.nhc;
+    const int kvh = rest / a.nhc;
+    const int t0 = split * a.chunk;
+    const int t1 = min(t0 + a.chunk, db.lkv);
+    const int nh = min(kDecodeHeads, a.G - kDecodeHeads * hc);
+    const int hq = kvh * a.G + kDecodeHeads * hc + n;
+
+    // Q^T as the B operand: column n = head hq, d = 32s + 8qd.
+    uint4 qf[NK];
+    if (n < nh) {
+        const uint16_t* src = (const uint16_t*)a.q + ((int64_t)b * a.QN + hq) * D + 8 * qd;
+#pragma unroll
+        for (int s = 0; s < NK; ++s) qf[s] = *(const uint4*)(src + 32 * s);
+    } else {
+#pragma unroll
+        for (int s = 0; s < NK; ++s) qf[s] = make_uint4(0, 0, 0, 0);
+    }
+
+    const uint16_t* kbase = (const uint16_t*)a.k;
+    const uint16_t* vbase = (const uint16_t*)a.v;
+    const int32_t* bt = a.paged ? a.block_table + (int64_t)b * a.bt_stride : nullptr;
+    auto tok_off = [&](int tk) -> int64_t {
+        if (a.paged) {
+            const int64_t blk = bt[tk / a.block_size];
+            return blk * a.p_blk + (int64_t)kvh * a.p_head + (int64_t)(tk % a.block_size) * a.p_tok;
+        }
+        return db.kv_row0 * a.c_rowmul + (int64_t)kvh * a.c_head + (int64_t)tk * a.c_tok;
+    };
+
+    uint4 kf[2][NK];
+    uint4 vst[NVU][4];
+    auto load_step = [&](int tt0) {
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            const int tk = tt0 + 16 * c + n;
+            if (tk < t1) {
+                const uint16_t* src = kbase + tok_off(tk) + 8 * qd;
+#pragma unroll
+                for (int s = 0; s < NK; ++s) kf[c][s] = *(const uint4*)(src + 32 * s);
+            } else {
+#pragma unroll
+                for (int s = 0; s < NK; ++s) kf[c][s] = make_uint4(0, 0, 0, 0);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < NVU; ++u) {
+            const int unit = lane + 64 * u;
+            const int tok4 = unit & 7, dc = unit >> 3;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int tk = tt0 + 4 * tok4 + r;
+                vst[u][r] = tk < t1 ? *(const uint4*)(vbase + tok_off(tk) + 8 * dc)
+                                    : make_uint4(0, 0, 0, 0);
+            }
+        }
+    };
+    auto store_v = [&](int buf) {
+#pragma unroll
+        for (int u = 0; u < NVU; ++u) {
+            const int unit = lane + 64 * u;
+            const int tok4 = unit & 7, dc = unit >> 3;
+            const int pos = vpos32(4 * tok4);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const uint32_t d0 = dw(vst[u][0], e >> 1), d1 = dw(vst[u][1], e >> 1);
+                const uint32_t d2 = dw(vst[u][2], e >> 1), d3 = dw(vst[u][3], e >> 1);
+                uint2 pr;
+                pr.x = (e & 1) ? sel_hi(d0, d1) : sel_lo(d0, d1);
+                pr.y = (e & 1) ? sel_hi(d2, d3) : sel_lo(d2, d3);
+                *(uint2*)(&vt[buf][(8 * dc + e) * VP + pos]) = pr;
+            }
+        }
+    };
+
+    f32x4 acc[NO];
+#pragma unroll
+    for (int o = 0; o < NO; ++o) acc[o] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m = -INFINITY, l = 0.f;
+
+    const int nsteps = (t1 - t0 + ST - 1) / ST;
+    if (nsteps > 0) load_step(t0);
+    for (int st = 0; st < nsteps; ++st) {
+        const int buf = st & 1;
+        const int tt0 = t0 + ST * st;
+        store_v(buf);
+        f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < NK; ++s) {
+            s0 = O::mma16(kf[0][s], qf[s], s0);
+            s1 = O::mma16(kf[1][s], qf[s], s1);
+        }
+        __syncthreads();
+        if (st + 1 < nsteps) load_step(tt0 + ST);
+
+        float x[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            x[i] = s0[i] * a.scale_log2;
+            x[4 + i] = s1[i] * a.scale_log2;
+        }
+        if (tt0 + ST > t1) {
+#pragma unroll
+            for (int r = 0; r < 8; ++r) {
+                const int tk = tt0 + 16 * (r >> 2) + 4 * qd + (r & 3);
+                if (tk >= t1) x[r] = -INFINITY;
+            }
+        }
+        float mt = x[0];
+#pragma unroll
+        for (int r = 1; r < 8; ++r) mt = fmaxf(mt, x[r]);
+        mt = fmaxf(mt, __shfl_xor(mt, 16));
+        mt = fmaxf(mt, __shfl_xor(mt, 32));
+        const float mn = fmaxf(m, mt);
+        const float mu = mn == -INFINITY ? 0.f : mn;
+        const float alpha = fast_exp2(m - mu);
+        float ps = 0.f;
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            x[r] = fast_exp2(x[r] - mu);
+            ps += x[r];
+        }
+        l = l * alpha + ps;
+        m = mn;
+        uint4 pb;
+        pb.x = O::pack2(x[0], x[1]);
+        pb.y = O::pack2(x[2], x[3]);
+        pb.z = O::pack2(x[4], x[5]);
+        pb.w = O::pack2(x[6], x[7]);
+#pragma unroll
+        for (int o = 0; o < NO; ++o) {
+            acc[o] *= alpha;
+            const uint4 va = *(const uint4*)(&vt[buf][(16 * o + n) * VP + 8 * qd]);
+            acc[o] = O::mma16(va, pb, acc[o]);
+        }
+    }
+
+    // partial: normalised O and natural-log LSE of this split
+    float lt = l + __shfl_xor(l, 16);
+    lt += __shfl_xor(lt, 32);
+    if (n < nh) {
+        const float inv = lt > 0.f ? 1.f / lt : 0.f;
+        float* po = a.part_o + ((int64_t)item * a.Gc + n) * D;
+#pragma unroll
+        for (int o = 0; o < NO; ++o) {
+            f32x4 v = acc[o] * inv;
+            *(f32x4*)(po + 16 * o + 4 * qd) = v;
+        }
+        if (qd == 0)
+            a.part_lse[(int64_t)item * a.Gc + n] = lt > 0.f ? (m + __log2f(lt)) * kLn2 : -INFINITY;
+    }
+}
+
+// Merge the kv splits of one (batch, head): weights exp(lse_s - max lse).
+template <int DT, int D>
+__global__ __launch_bounds__(64) void decode_combine(DecodeArgs a)
+{
+    using O = Ops<DT>;
+    const int bh = blockIdx.x;
+    const int b = bh / a.QN, h = bh % a.QN;
+    const int kvh = h / a.G, r = h % a.G;
+    const int hc = r / kDecodeHeads, n = r % kDecodeHeads;
+    const DecBatch db = a.batch[b];
+    const int ns = db.nsplit;
+    const int64_t slot0 = db.item0 + (int64_t)(kvh * a.nhc + hc) * ns;
+    const int lane = threadIdx.x;
+    uint16_t* op = (uint16_t*)a.o + ((int64_t)b * a.QN + h) * D;
+
+    float M = -INFINITY;
+    for (int s = 0; s < ns; ++s) M = fmaxf(M, a.part_lse[(slot0 + s) * a.Gc + n]);
+    float wsum = 0.f;
+    constexpr int PER = D / 64;
+    float accv[PER];
+#pragma unroll
+    for (int e = 0; e < PER; ++e) accv[e] = 0.f;
+    if (M != -INFINITY) {
+        for (int s = 0; s < ns; ++s) {
+            const float ws = __expf(a.part_lse[(slot0 + s) * a.Gc + n] - M);
+            wsum += ws;
+            const float* po = a.part_o + ((slot0 + s) * a.Gc + n) * D;
+#pragma unroll
+            for (int e = 0; e < PER; ++e) accv[e] += ws * po[lane + 64 * e];
+        }
+    }
+    const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+        const uint32_t pk = O::pack2(accv[e] * inv, 0.f);
+        op[lane + 64 * e] = (uint16_t)(pk & 0xffffu);
+    }
+    if (a.return_lse && lane == 0)
+        a.lse[(int64_t)b * a.QN + h] = wsum > 0.f ? M + __logf(wsum) : INFINITY;
+}
+
+// ---------------------------------------------------------------------------
+// Block-sparse schedule compaction: one wave per (batch, head, q block).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void bsa_compact(const uint8_t* mask, const BatchInfo* batch,
+                                                   int32_t* cnt, int32_t* idx, int N1, int nqb,
+                                                   int nkb, int X, int Y, int64_t n_rows)
+{
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= n_rows) return;
+    const int64_t b = row / ((int64_t)N1 * nqb);
+    const int qb = (int)(row % nqb);
+    const BatchInfo bi = batch[b];
+    const int64_t klim = ((int64_t)bi.lkv + Y - 1) / Y;
+    const bool qok = (int64_t)qb * X < bi.lq;
+    const uint8_t* mrow = mask + row * nkb;
+    int32_t* irow = idx + row * nkb;
+    int base = 0;
+    for (int c0 = 0; c0 < nkb; c0 += 64) {
+        const int kb = c0 + lane;
+        const bool sel = kb < nkb && qok && kb < klim && mrow[kb] != 0;
+        const unsigned long long bal = __ballot(sel);
+        const int pos = base + __popcll(bal & ((1ull << lane) - 1ull));
+        if (sel) irow[pos] = kb;
+        base += __popcll(bal);
+    }
+    for (int kb = base + lane; kb < nkb; kb += 64) irow[kb] = -1;
+    if (lane == 0) cnt[row] = base;
+}
+
+template <int DT, int DQK, int DV, bool BSA>
+int launch_attn(const fia_plan& p, const AttnArgs& a, hipStream_t stream)
+{
+    constexpr int STAGE = kBlockN * (DQK + 8) + DV * (kBlockN + 8);
+    const size_t lds = 2 * STAGE * sizeof(uint16_t);
+    static bool configured = false;
+    if (!configured) {
+        hipError_t e = hipFuncSetAttribute((const void*)attn_fwd<DT, DQK, DV, BSA>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return (int)e;
+        configured = true;
+    }
+    if (p.n_tiles == 0) return 0;
+    hipLaunchKernelGGL((attn_fwd<DT, DQK, DV, BSA>), dim3((unsigned)p.n_tiles), dim3(256), lds,
+                       stream, a);
+    return (int)hipGetLastError();
+}
+
+template <int DT, int D>
+int launch_dec(const fia_plan& p, const DecodeArgs& a, hipStream_t stream)
+{
+    if (p.n_items > 0)
+        hipLaunchKernelGGL((decode_split<DT, D>), dim3((unsigned)p.n_items), dim3(64), 0, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return (int)e;
+    hipLaunchKernelGGL((decode_combine<DT, D>), dim3((unsigned)(p.B * p.QN)), dim3(64), 0, stream, a);
+    return (int)hipGetLastError();
+}
+
+}  // namespace
+
+int launch_prefill(const fia_plan& p, const AttnArgs& a, void* stream)
+{
+    hipStream_t s = (hipStream_t)stream;
+    const bool bf = p.dtype == FIA_BF16;
+    if (p.Dqk == 64 && p.Dv == 64)
+        return bf ? launch_attn<FIA_BF16, 64, 64, false>(p, a, s) : launch_attn<FIA_F16, 64, 64, false>(p, a, s);
+    if (p.Dqk == 128 && p.Dv == 128)
+        return bf ? launch_attn<FIA_BF16, 128, 128, false>(p, a, s) : launch_attn<FIA_F16, 128, 128, false>(p, a, s);
+    if (p.Dqk == 192 && p.Dv == 128)
+        return bf ? launch_attn<FIA_BF16, 192, 128, false>(p, a, s) : launch_attn<FIA_F16, 192, 128, false>(p, a, s);
+    return (int)hipErrorInvalidValue;
+}
+
+int launch_bsa(const fia_plan& p, const AttnArgs& a, void* stream)
+{
+    hipStream_t s = (hipStream_t)stream;
+    if (p.n_rows > 0) {
+        hipLaunchKernelGGL(bsa_compact, dim3((unsigned)((p.n_rows + 3) / 4)), dim3(256), 0, s,
+                           p.bsa_mask, a.batch, (int32_t*)a.bsa_cnt, (int32_t*)a.bsa_idx,
+                           (int)p.QN, (int)p.bsa_nqb, (int)p.bsa_nkb, a.bx, a.by, p.n_rows);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return (int)e;
+    }
+    const bool bf = p.dtype == FIA_BF16;
+    if (p.Dqk == 64)
+        return bf ? launch_attn<FIA_BF16, 64, 64, true>(p, a, s) : launch_attn<FIA_F16, 64, 64, true>(p, a, s);
+    if (p.Dqk == 128)
+        return bf ? launch_attn<FIA_BF16, 128, 128, true>(p, a, s) : launch_attn<FIA_F16, 128, 128, true>(p, a, s);
+    return (int)hipErrorInvalidValue;
+}
+
+int launch_decode(const fia_plan& p, const DecodeArgs& a, void* stream)
+{
+    hipStream_t s = (hipStream_t)stream;
+    const bool bf = p.dtype == FIA_BF16;
+    if (p.Dqk == 64) return bf ? launch_dec<FIA_BF16, 64>(p, a, s) : launch_dec<FIA_F16, 64>(p, a, s);
+    if (p.Dqk == 128) return bf ? launch_dec<FIA_BF16, 128>(p, a, s) : launch_dec<FIA_F16, 128>(p, a, s);
+    return (int)hipErrorInvalidValue;
+}
+
+int copy_tables(void* dst, const void* src, uint64_t bytes, void* stream)
+{
+    return (int)hipMemcpyAsync(dst, src, bytes, hipMemcpyHostToDevice, (hipStream_t)stream);
+}
+
+void* alloc_pinned(uint64_t bytes)
+{
+    int n = 0;
+    if (hipGetDeviceCount(&n) != hipSuccess || n == 0) {
+        (void)hipGetLastError();
+        return nullptr;
+    }
+    void* ptr = nullptr;
+    if (hipHostMalloc(&ptr, bytes, hipHostMallocDefault) != hipSuccess) {
+        (void)hipGetLastError();
+        return nullptr;
+    }
+    return ptr;
+}
+
+void free_pinned(void* ptr)
+{
+    if (ptr) (void)hipHostFree(ptr);
+}
+
+int record_copy_done(void** event, void* stream)
+{
+    if (!*event) {
+        hipEvent_t e;
+        hipError_t rc = hipEventCreateWithFlags(&e, hipEventDisableTiming);
+        if (rc != hipSuccess) return (int)rc;
+        *event = (void*)e;
+    }
+    return (int)hipEventRecord((hipEvent_t)*event, (hipStream_t)stream);
+}
+
+void wait_and_release(void* event)
+{
+    if (!event) return;
+    (void)hipEventSynchronize((hipEvent_t)event);
+    (void)hipEventDestroy((hipEvent_t)event);
+}
+
+}  // namespace fia

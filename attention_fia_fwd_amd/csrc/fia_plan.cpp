@@ -1,0 +1,850 @@
+// Phase 1 of the fused inference attention and the block-sparse attention:
+// input validation, dispatch, schedule tables and workspace sizing.  Pure
+// host code; the only HIP call is the optional pinned allocation of the
+// schedule copy.
+//
+// Validation follows the parameter descriptions and constraints of pages
+// "torch_npu.npu_fused_infer_attention_score_v2", "torch_npu.npu_prompt_flash_
+// attention", "aclnnFusedInferAttentionScoreV5" and "aclnnBlockSparse
+// AttentionV2"; the reading taken where they are silent is stated inline.
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <memory>
+#include <numeric>
+#include <string>
+
+#include "fia_internal.h"
+
+using namespace fia;
+
+namespace {
+
+constexpr int64_t kIntMax = 2147483647;
+constexpr double kLog2e = 1.4426950408889634;
+
+uint64_t align_up(uint64_t x, uint64_t a) { return (x + a - 1) / a * a; }
+
+int64_t numel(const fia_tensor* t)
+{
+    int64_t n = 1;
+    for (int i = 0; i < t->ndim; ++i) n *= t->dims[i];
+    return n;
+}
+
+bool valid_rank(const fia_tensor* t) { return t->ndim >= 1 && t->ndim <= 8; }
+
+bool is_half(int32_t d) { return d == FIA_F16 || d == FIA_BF16; }
+
+bool dims_are(const fia_tensor* t, std::initializer_list<int64_t> d)
+{
+    if (t->ndim != (int32_t)d.size()) return false;
+    int i = 0;
+    for (int64_t x : d)
+        if (t->dims[i++] != x) return false;
+    return true;
+}
+
+// Parses an input layout string.  Output-layout variants the pages list
+// (e.g. "BNSD_BSND") are recognised and reported as unsupported.
+fia_status parse_layout(const char* s, int32_t* layout, bool* bsh)
+{
+    if (!s) return FIA_ERR_NULLPTR;
+    std::string v(s);
+    *bsh = false;
+    if (v == "BNSD") { *layout = LAYOUT_BNSD; return FIA_OK; }
+    if (v == "BSND") { *layout = LAYOUT_BSND; return FIA_OK; }
+    if (v == "BSH") { *layout = LAYOUT_BSND; *bsh = true; return FIA_OK; }
+    if (v == "TND") { *layout = LAYOUT_TND; return FIA_OK; }
+    static const char* variants[] = {"BNSD_BSND", "BSH_NBSD", "BSND_NBSD", "BNSD_NBSD", "TND_NTD",
+                                     "NTD_TND", "NTD", "BSH_BNSD", "BSND_BNSD"};
+    for (const char* x : variants)
+        if (v == x) return FIA_ERR_UNSUPPORTED;
+    return FIA_ERR_LAYOUT;
+}
+
+// Query/key/value geometry of one tensor under a layout: batch, heads, S, D.
+struct Geo {
+    int64_t B = 0, N = 0, S = 0, D = 0;
+};
+
+fia_status geometry(const fia_tensor* t, int32_t layout, bool bsh, int64_t heads, Geo* g)
+{
+    if (!valid_rank(t)) return FIA_ERR_SHAPE;
+    if (bsh) {
+        if (t->ndim != 3 || heads <= 0 || t->dims[2] % heads) return FIA_ERR_SHAPE;
+        *g = {t->dims[0], heads, t->dims[1], t->dims[2] / heads};
+        return FIA_OK;
+    }
+    if (layout == LAYOUT_TND) {
+        if (t->ndim != 3) return FIA_ERR_SHAPE;
+        *g = {0, t->dims[1], t->dims[0], t->dims[2]};
+        return FIA_OK;
+    }
+    if (t->ndim != 4) return FIA_ERR_SHAPE;
+    if (layout == LAYOUT_BNSD)
+        *g = {t->dims[0], t->dims[1], t->dims[2], t->dims[3]};
+    else
+        *g = {t->dims[0], t->dims[2], t->dims[1], t->dims[3]};
+    return FIA_OK;
+}
+
+// actual_seq lengths for padded layouts: count 1 broadcasts, count >= B takes
+// the first B, other counts are rejected; NULL = the tensor's S.
+fia_status resolve_lengths(const int64_t* arr, int64_t n, int64_t B, int64_t S,
+                           std::vector<int64_t>* out)
+{
+    out->assign((size_t)B, S);
+    if (!arr) return FIA_OK;
+    if (n != 1 && n < B) return FIA_ERR_PARAM;
+    for (int64_t b = 0; b < B; ++b) {
+        int64_t v = arr[n == 1 ? 0 : b];
+        if (v < 0 || v > S) return FIA_ERR_SHAPE;
+        (*out)[(size_t)b] = v;
+    }
+    return FIA_OK;
+}
+
+// TND cumulative lengths: non-decreasing, non-negative, last <= T.
+fia_status resolve_cumulative(const int64_t* arr, int64_t n, int64_t T,
+                              std::vector<int64_t>* len, std::vector<int64_t>* start)
+{
+    if (!arr || n <= 0) return FIA_ERR_PARAM;
+    len->resize((size_t)n);
+    start->resize((size_t)n);
+    int64_t prev = 0;
+    for (int64_t b = 0; b < n; ++b) {
+        if (arr[b] < prev) return FIA_ERR_SHAPE;
+        (*start)[(size_t)b] = prev;
+        (*len)[(size_t)b] = arr[b] - prev;
+        prev = arr[b];
+    }
+    if (prev > T) return FIA_ERR_SHAPE;
+    return FIA_OK;
+}
+
+bool mask_dtype_ok(int32_t d) { return d == FIA_BOOL || d == FIA_I8 || d == FIA_U8; }
+
+bool is_template_2048(const fia_tensor* m)
+{
+    return dims_are(m, {2048, 2048}) || dims_are(m, {1, 2048, 2048}) ||
+           dims_are(m, {1, 1, 2048, 2048});
+}
+
+// Scheduling weight of a prefill tile: number of kv tiles it visits.
+int64_t kv_tiles_of(int32_t mode, bool has_mask, int64_t pre, int64_t next, int64_t lq,
+                    int64_t lkv, int64_t q0, int64_t q1)
+{
+    const int64_t last = std::min(q1, lq) - 1;
+    if (last < q0 || lkv <= 0) return 0;
+    const int64_t delta = lkv - lq;
+    int64_t lo = 0, hi = lkv;
+    switch (mode) {
+    case 0:
+        if (has_mask) {
+            lo = std::max<int64_t>(0, q0 - pre);
+            hi = std::min<int64_t>(lkv, last + next + 1);
+        }
+        break;
+    case 2: hi = std::min<int64_t>(lkv, last + 1); break;
+    case 3: hi = std::min<int64_t>(lkv, last + delta + 1); break;
+    case 4:
+        lo = std::max<int64_t>(0, q0 + delta - pre);
+        hi = std::min<int64_t>(lkv, last + delta + next + 1);
+        break;
+    default: break;
+    }
+    if (hi <= lo) return 0;
+    const int64_t start = lo / kBlockN * kBlockN;
+    return (hi - start + kBlockN - 1) / kBlockN;
+}
+
+template <class T>
+uint64_t put(std::vector<unsigned char>& buf, uint64_t off, const std::vector<T>& v)
+{
+    const uint64_t bytes = v.size() * sizeof(T);
+    if (buf.size() < off + bytes) buf.resize(off + bytes);
+    if (bytes) std::memcpy(buf.data() + off, v.data(), bytes);
+    return off + bytes;
+}
+
+void finish_tables(fia_plan* p)
+{
+    p->tables_bytes = align_up(p->host_tables.size(), 256);
+    p->host_tables.resize(p->tables_bytes);
+    if (p->tables_bytes) {
+        p->pinned_tables = alloc_pinned(p->tables_bytes);
+        if (p->pinned_tables)
+            std::memcpy(p->pinned_tables, p->host_tables.data(), p->tables_bytes);
+    }
+}
+
+}  // namespace
+
+extern "C" {
+
+void fia_params_init(fia_params* p)
+{
+    if (!p) return;
+    std::memset(p, 0, sizeof(*p));
+    p->input_layout = "BSH";
+    p->scale_value = 1.0;
+    p->pre_tokens = kIntMax;
+    p->next_tokens = kIntMax;
+}
+
+void bsa_params_init(bsa_params* p)
+{
+    if (!p) return;
+    std::memset(p, 0, sizeof(*p));
+    p->q_input_layout = "BNSD";
+    p->kv_input_layout = "BNSD";
+    p->scale_value = 1.0;
+    p->block_shape[0] = 128;
+    p->block_shape[1] = 128;
+    p->inner_precise = 4;
+    p->pre_tokens = kIntMax;
+    p->next_tokens = kIntMax;
+}
+
+const char* fia_status_string(fia_status s)
+{
+    switch (s) {
+    case FIA_OK: return "FIA_OK";
+    case FIA_ERR_NULLPTR: return "FIA_ERR_NULLPTR: a required tensor or pointer is missing";
+    case FIA_ERR_DTYPE: return "FIA_ERR_DTYPE: dtype not allowed or q/k/v dtypes differ";
+    case FIA_ERR_SHAPE: return "FIA_ERR_SHAPE: shape inconsistent with layout, heads or lengths";
+    case FIA_ERR_LAYOUT: return "FIA_ERR_LAYOUT: unknown or mismatched layout";
+    case FIA_ERR_PARAM: return "FIA_ERR_PARAM: parameter outside its allowed range";
+    case FIA_ERR_UNSUPPORTED: return "FIA_ERR_UNSUPPORTED: legal on the pages but not provided";
+    case FIA_ERR_WORKSPACE: return "FIA_ERR_WORKSPACE: workspace missing or too small";
+    case FIA_ERR_HIP: return "FIA_ERR_HIP: a HIP copy or launch failed";
+    }
+    return "unknown fia_status";
+}
+
+void fia_plan_destroy(fia_plan* plan)
+{
+    if (!plan) return;
+    // the last run's schedule copy may still read the pinned buffer
+    if (plan->copy_done) wait_and_release(plan->copy_done);
+    if (plan->pinned_tables) free_pinned(plan->pinned_tables);
+    delete plan;
+}
+
+fia_status fia_get_workspace_size(const fia_tensor* query, const fia_tensor* key,
+                                  const fia_tensor* value, const fia_tensor* atten_mask,
+                                  const fia_tensor* block_table, const fia_params* prm,
+                                  const fia_tensor* attention_out,
+                                  const fia_tensor* softmax_lse, uint64_t* workspace_size,
+                                  fia_plan** plan_out)
+{
+    if (!query || !key || !value || !prm || !attention_out || !workspace_size || !plan_out)
+        return FIA_ERR_NULLPTR;
+    *plan_out = nullptr;
+    *workspace_size = 0;
+    if (!valid_rank(query) || !valid_rank(key) || !valid_rank(value) || !valid_rank(attention_out))
+        return FIA_ERR_SHAPE;
+
+    std::unique_ptr<fia_plan> p(new fia_plan());
+
+    // Empty query or empty output: nothing to compute (constraints: empty
+    // input handling).
+    if (numel(query) == 0 || numel(attention_out) == 0) {
+        p->kind = KIND_EMPTY;
+        *plan_out = p.release();
+        return FIA_OK;
+    }
+    if (!query->data || !key->data || !value->data || !attention_out->data) return FIA_ERR_NULLPTR;
+
+    // dtypes: q/k/v fp16 or bf16 and equal; output in the query dtype.
+    if (!is_half(query->dtype)) return FIA_ERR_DTYPE;
+    if (key->dtype != query->dtype || value->dtype != query->dtype) return FIA_ERR_DTYPE;
+    if (attention_out->dtype != query->dtype) return FIA_ERR_DTYPE;
+
+    int32_t layout;
+    bool bsh;
+    fia_status st = parse_layout(prm->input_layout, &layout, &bsh);
+    if (st != FIA_OK) return st;
+
+    const int64_t QN = prm->num_heads;
+    if (QN <= 0 || QN > 256) return FIA_ERR_PARAM;
+    const int64_t KVN = prm->num_key_value_heads == 0 ? QN : prm->num_key_value_heads;
+    if (KVN <= 0 || QN % KVN != 0 || QN / KVN > 64) return FIA_ERR_PARAM;
+    if (prm->sparse_mode < 0 || prm->sparse_mode > 4) return FIA_ERR_PARAM;
+    if (prm->inner_precise < 0 || prm->inner_precise > 3) return FIA_ERR_PARAM;
+    if (!(std::isfinite(prm->scale_value))) return FIA_ERR_PARAM;
+
+    Geo gq;
+    if ((st = geometry(query, layout, bsh, QN, &gq)) != FIA_OK) return st;
+    if (gq.N != QN) return FIA_ERR_SHAPE;
+    const bool decode = layout != LAYOUT_TND && gq.S == 1;
+    const bool paged = block_table != nullptr;
+
+    p->dtype = query->dtype;
+    p->layout = layout;
+    p->QN = QN;
+    p->KVN = KVN;
+    p->G = QN / KVN;
+    p->Dqk = gq.D;
+    p->Sq = gq.S;
+
+    // ----- key / value -----
+    Geo gk, gv;
+    int64_t B = 0, Skv = 0, Dv = 0;
+    int64_t pool_blocks = 0;
+    int32_t pool_layout = 0;
+    if (paged) {
+        // PageAttention (constraints, page attention scenario): decode only
+        // here; paged prefill is not provided.
+        if (!decode) return FIA_ERR_UNSUPPORTED;
+        if (!block_table->data) return FIA_ERR_NULLPTR;
+        if (block_table->dtype != FIA_I32) return FIA_ERR_DTYPE;
+        if (block_table->ndim != 2 || block_table->dims[0] != gq.B) return FIA_ERR_SHAPE;
+        if (prm->block_size <= 0 || prm->block_size % 16 != 0) return FIA_ERR_PARAM;
+        if (!prm->actual_seq_kvlen) return FIA_ERR_PARAM;
+        if (key->ndim != value->ndim) return FIA_ERR_SHAPE;
+        for (int i = 0; i < key->ndim; ++i)
+            if (key->dims[i] != value->dims[i]) return FIA_ERR_SHAPE;
+        const int64_t bs = prm->block_size;
+        if (key->ndim == 4) {          // (blocknum, KV_N, block_size, D)
+            if (key->dims[1] != KVN || key->dims[2] != bs) return FIA_ERR_SHAPE;
+            gk.D = key->dims[3];
+            pool_layout = 0;
+        } else if (key->ndim == 3) {   // (blocknum, block_size, KV_N*D)
+            if (key->dims[1] != bs || key->dims[2] % KVN) return FIA_ERR_SHAPE;
+            gk.D = key->dims[2] / KVN;
+            pool_layout = 1;
+        } else {
+            return FIA_ERR_SHAPE;
+        }
+        pool_blocks = key->dims[0];
+        B = gq.B;
+        Skv = block_table->dims[1] * bs;
+        Dv = gk.D;
+    } else {
+        if ((st = geometry(key, layout, bsh, KVN, &gk)) != FIA_OK) return st;
+        if ((st = geometry(value, layout, bsh, KVN, &gv)) != FIA_OK) return st;
+        if (gk.N != KVN || gv.N != KVN) return FIA_ERR_SHAPE;
+        if (layout != LAYOUT_TND && (gk.B != gq.B || gv.B != gq.B)) return FIA_ERR_SHAPE;
+        if (gk.S != gv.S) return FIA_ERR_SHAPE;
+        B = gq.B;
+        Skv = gk.S;
+        Dv = gv.D;
+    }
+    if (gk.D != gq.D) return FIA_ERR_SHAPE;
+    p->Dv = Dv;
+    p->Skv = Skv;
+
+    // ----- lengths -----
+    std::vector<int64_t> lq, lkv, qstart, kvstart;
+    if (layout == LAYOUT_TND) {
+        if (!prm->actual_seq_qlen || !prm->actual_seq_kvlen) return FIA_ERR_PARAM;
+        if (prm->n_actual_seq_qlen != prm->n_actual_seq_kvlen) return FIA_ERR_PARAM;
+        if ((st = resolve_cumulative(prm->actual_seq_qlen, prm->n_actual_seq_qlen, gq.S, &lq,
+                                     &qstart)) != FIA_OK)
+            return st;
+        if ((st = resolve_cumulative(prm->actual_seq_kvlen, prm->n_actual_seq_kvlen, Skv, &lkv,
+                                     &kvstart)) != FIA_OK)
+            return st;
+        B = prm->n_actual_seq_qlen;
+    } else {
+        if (decode)
+            lq.assign((size_t)B, 1);   // actual_seq_qlen has no effect at S == 1
+        else if ((st = resolve_lengths(prm->actual_seq_qlen, prm->n_actual_seq_qlen, B, gq.S,
+                                       &lq)) != FIA_OK)
+            return st;
+        if ((st = resolve_lengths(prm->actual_seq_kvlen, prm->n_actual_seq_kvlen, B, Skv,
+                                  &lkv)) != FIA_OK)
+            return st;
+    }
+    p->B = B;
+    for (int64_t b = 0; b < B; ++b)
+        if (lq[(size_t)b] > INT32_MAX || lkv[(size_t)b] > INT32_MAX) return FIA_ERR_UNSUPPORTED;
+
+    int64_t max_blocks = 0;
+    if (paged) {
+        const int64_t bs = prm->block_size;
+        int64_t need = 0;
+        for (int64_t b = 0; b < B; ++b) {
+            const int64_t nb = (lkv[(size_t)b] + bs - 1) / bs;
+            max_blocks = std::max(max_blocks, nb);
+            need += nb;
+        }
+        if (block_table->dims[1] < max_blocks) return FIA_ERR_SHAPE;
+        if (pool_blocks < need) return FIA_ERR_SHAPE;
+    }
+
+    // ----- output / lse shapes -----
+    {
+        Geo go;
+        if ((st = geometry(attention_out, layout, bsh, QN, &go)) != FIA_OK) return st;
+        if (go.N != QN || go.S != gq.S || go.D != Dv) return FIA_ERR_SHAPE;
+        if (layout != LAYOUT_TND && go.B != gq.B) return FIA_ERR_SHAPE;
+    }
+    const bool want_lse = prm->return_softmax_lse != 0;
+    if (want_lse) {
+        if (!softmax_lse || !softmax_lse->data) return FIA_ERR_NULLPTR;
+        if (softmax_lse->dtype != FIA_F32) return FIA_ERR_DTYPE;
+        bool ok = layout == LAYOUT_TND ? dims_are(softmax_lse, {gq.S, QN, 1})
+                                       : dims_are(softmax_lse, {gq.B, QN, gq.S, 1});
+        if (!ok) return FIA_ERR_SHAPE;
+    }
+
+    // ----- mask -----
+    const int32_t mode = (int32_t)prm->sparse_mode;
+    const uint8_t* mask = nullptr;
+    int64_t mask_bstride = 0, mask_rstride = 0;
+    if (!decode) {
+        if (layout == LAYOUT_TND && (mode == 1 || (mode == 0 && atten_mask)))
+            return FIA_ERR_PARAM;      // TND: mode 0 without mask, or modes 2/3/4
+        if (mode == 1 && !atten_mask) return FIA_ERR_NULLPTR;
+        if (atten_mask) {
+            if (!mask_dtype_ok(atten_mask->dtype)) return FIA_ERR_DTYPE;
+            if (mode >= 2) {
+                if (!is_template_2048(atten_mask)) return FIA_ERR_SHAPE;
+            } else {
+                if (!atten_mask->data) return FIA_ERR_NULLPTR;
+                const fia_tensor* m = atten_mask;
+                const int64_t rows = m->dims[m->ndim - 2 < 0 ? 0 : m->ndim - 2];
+                const int64_t cols = m->dims[m->ndim - 1];
+                int64_t mb = 1;
+                if (m->ndim == 2) {
+                    mb = 1;
+                } else if (m->ndim == 3) {
+                    mb = m->dims[0];
+                } else if (m->ndim == 4) {
+                    if (m->dims[1] != 1) return FIA_ERR_SHAPE;
+                    mb = m->dims[0];
+                } else {
+                    return FIA_ERR_SHAPE;
+                }
+                if (m->ndim < 2 || rows < gq.S || cols < Skv) return FIA_ERR_SHAPE;
+                if (mb != 1 && mb != B) return FIA_ERR_SHAPE;
+                mask = (const uint8_t*)m->data;
+                mask_rstride = cols;
+                mask_bstride = mb == 1 ? 0 : rows * cols;
+            }
+        }
+    } else if (prm->inner_precise > 1) {
+        return FIA_ERR_PARAM;           // Q_S == 1: inner_precise 0 or 1 only
+    }
+
+    // ----- supported head dims -----
+    if (decode) {
+        if (!((gq.D == 64 || gq.D == 128) && Dv == gq.D)) return FIA_ERR_UNSUPPORTED;
+    } else {
+        const bool ok = (gq.D == 64 && Dv == 64) || (gq.D == 128 && Dv == 128) ||
+                        (gq.D == 192 && Dv == 128);
+        if (!ok) return FIA_ERR_UNSUPPORTED;
+    }
+
+    const double scale_log2 = prm->scale_value * kLog2e;
+
+    if (decode) {
+        p->kind = KIND_DECODE;
+        DecodeArgs& d = p->dec;
+        d.q = query->data;
+        d.k = key->data;
+        d.v = value->data;
+        d.o = attention_out->data;
+        d.lse = want_lse ? (float*)softmax_lse->data : nullptr;
+        d.return_lse = want_lse;
+        d.paged = paged;
+        const int64_t D = gq.D;
+        if (paged) {
+            const int64_t bs = prm->block_size;
+            d.block_table = (const int32_t*)block_table->data;
+            d.bt_stride = block_table->dims[1];
+            d.block_size = (int32_t)bs;
+            d.p_blk = bs * KVN * D;
+            d.p_head = pool_layout == 0 ? bs * D : D;
+            d.p_tok = pool_layout == 0 ? D : KVN * D;
+        } else {
+            d.c_rowmul = KVN * D;
+            d.c_head = layout == LAYOUT_BNSD ? Skv * D : D;
+            d.c_tok = layout == LAYOUT_BNSD ? D : KVN * D;
+        }
+        const int64_t G = QN / KVN;
+        const int64_t Gc = std::min<int64_t>(G, kDecodeHeads);
+        const int64_t nhc = (G + kDecodeHeads - 1) / kDecodeHeads;
+        // Split plan: kv tokens per wave item, a multiple of the decode step,
+        // sized so the grid holds several waves per wave slot of the chip.
+        int64_t tok_heads = 0;
+        for (int64_t b = 0; b < B; ++b) tok_heads += lkv[(size_t)b] * KVN * nhc;
+        const int64_t target_items = (int64_t)kNumCUs * 8 * 4;
+        int64_t chunk = tok_heads / std::max<int64_t>(1, target_items);
+        chunk = (chunk + 255) / 256 * 256;
+        chunk = std::max<int64_t>(256, std::min<int64_t>(chunk, 4096));
+        std::vector<DecBatch> db((size_t)B);
+        int64_t items = 0;
+        for (int64_t b = 0; b < B; ++b) {
+            const int64_t L = lkv[(size_t)b];
+            const int64_t ns = (L + chunk - 1) / chunk;
+            db[(size_t)b].kv_row0 = paged ? 0 : b * Skv;
+            db[(size_t)b].lkv = (int32_t)L;
+            db[(size_t)b].item0 = (int32_t)items;
+            db[(size_t)b].nsplit = (int32_t)ns;
+            db[(size_t)b].pad = 0;
+            items += KVN * nhc * ns;
+        }
+        if (items > INT32_MAX / 2) return FIA_ERR_UNSUPPORTED;
+        d.B = (int32_t)B;
+        d.QN = (int32_t)QN;
+        d.KVN = (int32_t)KVN;
+        d.G = (int32_t)G;
+        d.Gc = (int32_t)Gc;
+        d.nhc = (int32_t)nhc;
+        d.chunk = (int32_t)chunk;
+        d.n_items = (int32_t)items;
+        d.scale_log2 = (float)scale_log2;
+        p->n_items = items;
+        p->off_batch = 0;
+        put(p->host_tables, 0, db);
+        finish_tables(p.get());
+        p->off_part_o = p->tables_bytes;
+        p->off_part_lse = align_up(p->off_part_o + (uint64_t)items * Gc * Dv * 4, 256);
+        p->workspace_bytes = align_up(p->off_part_lse + (uint64_t)items * Gc * 4, 256);
+        *workspace_size = p->workspace_bytes;
+        *plan_out = p.release();
+        return FIA_OK;
+    }
+
+    // ----- prefill -----
+    p->kind = KIND_PREFILL;
+    AttnArgs& a = p->attn;
+    a.q = query->data;
+    a.k = key->data;
+    a.v = value->data;
+    a.o = attention_out->data;
+    a.lse = want_lse ? (float*)softmax_lse->data : nullptr;
+    a.return_lse = want_lse;
+    a.mask = mask;
+    a.mask_bstride = mask_bstride;
+    a.mask_rstride = mask_rstride;
+    a.has_mask = mask != nullptr;
+    a.mode = mode;
+    // Modes 1, 2 and 3 ignore pre/next; mode 0 without a mask ignores them
+    // (sparse_mode parameter description).
+    a.pre = (mode == 4 || (mode == 0 && mask)) ? prm->pre_tokens : kIntMax;
+    a.next = (mode == 4 || (mode == 0 && mask)) ? prm->next_tokens : kIntMax;
+    a.QN = (int32_t)QN;
+    a.KVN = (int32_t)KVN;
+    a.G = (int32_t)(QN / KVN);
+    a.scale_log2 = (float)scale_log2;
+    const int64_t Dq = gq.D;
+    if (layout == LAYOUT_BNSD) {
+        a.q_sH = gq.S * Dq;  a.q_sS = Dq;
+        a.k_sH = Skv * Dq;   a.k_sS = Dq;
+        a.v_sH = Skv * Dv;   a.v_sS = Dv;
+        a.o_sH = gq.S * Dv;  a.o_sS = Dv;
+        a.lse_sH = gq.S;     a.lse_sS = 1;
+    } else {
+        a.q_sH = Dq;  a.q_sS = QN * Dq;
+        a.k_sH = Dq;  a.k_sS = KVN * Dq;
+        a.v_sH = Dv;  a.v_sS = KVN * Dv;
+        a.o_sH = Dv;  a.o_sS = QN * Dv;
+        if (layout == LAYOUT_TND) { a.lse_sH = 1; a.lse_sS = QN; }
+        else { a.lse_sH = gq.S; a.lse_sS = 1; }
+    }
+    a.q_rowmul = QN * Dq;
+    a.k_rowmul = KVN * Dq;
+    a.v_rowmul = KVN * Dv;
+    a.o_rowmul = QN * Dv;
+    a.lse_rowmul = QN;
+
+    std::vector<BatchInfo> bi((size_t)B);
+    for (int64_t b = 0; b < B; ++b) {
+        bi[(size_t)b].q_row0 = layout == LAYOUT_TND ? qstart[(size_t)b] : b * gq.S;
+        bi[(size_t)b].kv_row0 = layout == LAYOUT_TND ? kvstart[(size_t)b] : b * Skv;
+        bi[(size_t)b].lq = (int32_t)lq[(size_t)b];
+        bi[(size_t)b].lkv = (int32_t)lkv[(size_t)b];
+    }
+    // Tiles of 128 query rows per (batch, head); padded layouts also cover
+    // the padding rows (written as zeros).  Longest-first order.
+    struct W { int64_t work; Tile t; };
+    std::vector<W> tl;
+    for (int64_t b = 0; b < B; ++b) {
+        const int64_t rows = layout == LAYOUT_TND ? lq[(size_t)b] : gq.S;
+        for (int64_t q0 = 0; q0 < rows; q0 += kBlockM) {
+            const int64_t q1 = std::min<int64_t>(q0 + kBlockM, rows);
+            const int64_t w = kv_tiles_of(mode, mask != nullptr, a.pre, a.next, lq[(size_t)b],
+                                          lkv[(size_t)b], q0, q1);
+            for (int64_t h = 0; h < QN; ++h)
+                tl.push_back({w, Tile{(int32_t)b, (int32_t)h, (int32_t)q0, (int32_t)q1}});
+        }
+    }
+    std::stable_sort(tl.begin(), tl.end(), [](const W& x, const W& y) { return x.work > y.work; });
+    std::vector<Tile> tiles;
+    tiles.reserve(tl.size());
+    for (auto& w : tl) tiles.push_back(w.t);
+    if (tiles.size() > (size_t)INT32_MAX) return FIA_ERR_UNSUPPORTED;
+    p->n_tiles = (int64_t)tiles.size();
+    a.n_tiles = (int32_t)tiles.size();
+    p->off_batch = 0;
+    uint64_t end = put(p->host_tables, 0, bi);
+    p->off_tiles = align_up(end, 256);
+    put(p->host_tables, p->off_tiles, tiles);
+    finish_tables(p.get());
+    p->workspace_bytes = p->tables_bytes;
+    *workspace_size = p->workspace_bytes;
+    *plan_out = p.release();
+    return FIA_OK;
+}
+
+fia_status bsa_get_workspace_size(const fia_tensor* query, const fia_tensor* key,
+                                  const fia_tensor* value, const fia_tensor* block_sparse_mask,
+                                  const fia_tensor* atten_mask, const fia_tensor* block_table,
+                                  const bsa_params* prm, const fia_tensor* attention_out,
+                                  const fia_tensor* softmax_lse, uint64_t* workspace_size,
+                                  fia_plan** plan_out)
+{
+    if (!query || !key || !value || !prm || !attention_out || !workspace_size || !plan_out)
+        return FIA_ERR_NULLPTR;
+    *plan_out = nullptr;
+    *workspace_size = 0;
+    if (!block_sparse_mask) return FIA_ERR_NULLPTR;
+    if (!valid_rank(query) || !valid_rank(key) || !valid_rank(value) ||
+        !valid_rank(attention_out) || !valid_rank(block_sparse_mask))
+        return FIA_ERR_SHAPE;
+    // Constraints of the block-sparse page: no atten_mask, no paged cache,
+    // fixed mask_type / inner_precise / pre / next.
+    if (atten_mask || block_table) return FIA_ERR_PARAM;
+    if (prm->mask_type != 0 || prm->block_size != 0 || prm->inner_precise != 4) return FIA_ERR_PARAM;
+    if (prm->pre_tokens != kIntMax || prm->next_tokens != kIntMax) return FIA_ERR_PARAM;
+    if (prm->softmax_lse_flag != 0 && prm->softmax_lse_flag != 1) return FIA_ERR_PARAM;
+    if (!std::isfinite(prm->scale_value)) return FIA_ERR_PARAM;
+
+    std::unique_ptr<fia_plan> p(new fia_plan());
+    if (numel(query) == 0 || numel(attention_out) == 0) {
+        p->kind = KIND_EMPTY;
+        *plan_out = p.release();
+        return FIA_OK;
+    }
+    if (!query->data || !key->data || !value->data || !attention_out->data ||
+        !block_sparse_mask->data)
+        return FIA_ERR_NULLPTR;
+    if (!is_half(query->dtype) || key->dtype != query->dtype || value->dtype != query->dtype ||
+        attention_out->dtype != query->dtype)
+        return FIA_ERR_DTYPE;
+    if (block_sparse_mask->dtype != FIA_U8 && block_sparse_mask->dtype != FIA_BOOL)
+        return FIA_ERR_DTYPE;
+
+    int32_t layout, kvlayout;
+    bool bsh, kvbsh;
+    fia_status st;
+    if (!prm->q_input_layout || !prm->kv_input_layout) return FIA_ERR_NULLPTR;
+    if ((st = parse_layout(prm->q_input_layout, &layout, &bsh)) != FIA_OK)
+        return st == FIA_ERR_UNSUPPORTED ? FIA_ERR_LAYOUT : st;
+    if ((st = parse_layout(prm->kv_input_layout, &kvlayout, &kvbsh)) != FIA_OK)
+        return st == FIA_ERR_UNSUPPORTED ? FIA_ERR_LAYOUT : st;
+    if (bsh || kvbsh) return FIA_ERR_LAYOUT;          // TND, BNSD, BSND only
+    if (std::strcmp(prm->q_input_layout, prm->kv_input_layout) != 0) return FIA_ERR_LAYOUT;
+
+    const int64_t N1 = prm->num_heads;
+    const int64_t N2 = prm->num_key_value_heads == 0 ? N1 : prm->num_key_value_heads;
+    if (N1 <= 0 || N2 <= 0 || N1 < N2 || N1 % N2 != 0) return FIA_ERR_PARAM;
+    const int64_t X = prm->block_shape[0], Y = prm->block_shape[1];
+    if (X <= 0 || Y <= 0 || Y % 128 != 0) return FIA_ERR_PARAM;
+    const bool have_q = prm->actual_seq_lengths != nullptr;
+    const bool have_kv = prm->actual_seq_lengths_kv != nullptr;
+    if (have_q != have_kv) return FIA_ERR_PARAM;
+    if (layout == LAYOUT_TND && !have_q) return FIA_ERR_PARAM;
+
+    Geo gq, gk, gv, go;
+    if ((st = geometry(query, layout, false, N1, &gq)) != FIA_OK) return st;
+    if ((st = geometry(key, layout, false, N2, &gk)) != FIA_OK) return st;
+    if ((st = geometry(value, layout, false, N2, &gv)) != FIA_OK) return st;
+    if ((st = geometry(attention_out, layout, false, N1, &go)) != FIA_OK) return st;
+    if (gq.N != N1 || gk.N != N2 || gv.N != N2 || go.N != N1) return FIA_ERR_SHAPE;
+    if (gk.S != gv.S || go.S != gq.S) return FIA_ERR_SHAPE;
+    if (gq.D != gk.D || gq.D != gv.D || go.D != gq.D) return FIA_ERR_SHAPE;
+    if (layout != LAYOUT_TND && (gk.B != gq.B || gv.B != gq.B || go.B != gq.B)) return FIA_ERR_SHAPE;
+    if (gq.D != 64 && gq.D != 128) return FIA_ERR_UNSUPPORTED;   // D of 64 or 128
+
+    std::vector<int64_t> lq, lkv, qstart, kvstart;
+    int64_t B;
+    if (layout == LAYOUT_TND) {
+        if (prm->n_actual_seq_lengths != prm->n_actual_seq_lengths_kv) return FIA_ERR_PARAM;
+        if ((st = resolve_cumulative(prm->actual_seq_lengths, prm->n_actual_seq_lengths, gq.S, &lq,
+                                     &qstart)) != FIA_OK)
+            return st;
+        if ((st = resolve_cumulative(prm->actual_seq_lengths_kv, prm->n_actual_seq_lengths_kv,
+                                     gk.S, &lkv, &kvstart)) != FIA_OK)
+            return st;
+        B = prm->n_actual_seq_lengths;
+    } else {
+        B = gq.B;
+        if ((st = resolve_lengths(prm->actual_seq_lengths, prm->n_actual_seq_lengths, B, gq.S,
+                                  &lq)) != FIA_OK)
+            return st;
+        if ((st = resolve_lengths(prm->actual_seq_lengths_kv, prm->n_actual_seq_lengths_kv, B,
+                                  gk.S, &lkv)) != FIA_OK)
+            return st;
+    }
+    // Mask shape [B, N1, ceil(maxQS / X), ceil(maxKVS / Y)], maxQS/maxKVS the
+    // tensors' S for BNSD/BSND and the longest sequence for TND.
+    int64_t maxq = gq.S, maxkv = gk.S;
+    if (layout == LAYOUT_TND) {
+        maxq = *std::max_element(lq.begin(), lq.end());
+        maxkv = *std::max_element(lkv.begin(), lkv.end());
+    }
+    const int64_t nqb = (maxq + X - 1) / X, nkb = (maxkv + Y - 1) / Y;
+    if (!dims_are(block_sparse_mask, {B, N1, nqb, nkb})) return FIA_ERR_SHAPE;
+    const bool want_lse = prm->softmax_lse_flag != 0;
+    if (want_lse) {
+        if (!softmax_lse || !softmax_lse->data) return FIA_ERR_NULLPTR;
+        if (softmax_lse->dtype != FIA_F32) return FIA_ERR_DTYPE;
+        bool ok = layout == LAYOUT_TND ? dims_are(softmax_lse, {gq.S, N1, 1})
+                                       : dims_are(softmax_lse, {B, N1, gq.S, 1});
+        if (!ok) return FIA_ERR_SHAPE;
+    }
+
+    p->kind = KIND_BSA;
+    p->dtype = query->dtype;
+    p->layout = layout;
+    p->B = B;
+    p->QN = N1;
+    p->KVN = N2;
+    p->G = N1 / N2;
+    p->Sq = gq.S;
+    p->Skv = gk.S;
+    p->Dqk = p->Dv = gq.D;
+    p->bsa_mask = (const uint8_t*)block_sparse_mask->data;
+    p->bsa_nqb = nqb;
+    p->bsa_nkb = nkb;
+    p->n_rows = B * N1 * nqb;
+
+    AttnArgs& a = p->attn;
+    a.q = query->data;
+    a.k = key->data;
+    a.v = value->data;
+    a.o = attention_out->data;
+    a.lse = want_lse ? (float*)softmax_lse->data : nullptr;
+    a.return_lse = want_lse;
+    a.mode = 0;
+    a.has_mask = 0;
+    a.pre = a.next = kIntMax;
+    a.QN = (int32_t)N1;
+    a.KVN = (int32_t)N2;
+    a.G = (int32_t)(N1 / N2);
+    a.scale_log2 = (float)(prm->scale_value * kLog2e);
+    a.nqb = (int32_t)nqb;
+    a.nkb = (int32_t)nkb;
+    a.bx = (int32_t)X;
+    a.by = (int32_t)Y;
+    const int64_t D = gq.D;
+    if (layout == LAYOUT_BNSD) {
+        a.q_sH = gq.S * D; a.q_sS = D;
+        a.k_sH = gk.S * D; a.k_sS = D;
+        a.v_sH = gk.S * D; a.v_sS = D;
+        a.o_sH = gq.S * D; a.o_sS = D;
+        a.lse_sH = gq.S;   a.lse_sS = 1;
+    } else {
+        a.q_sH = D; a.q_sS = N1 * D;
+        a.k_sH = D; a.k_sS = N2 * D;
+        a.v_sH = D; a.v_sS = N2 * D;
+        a.o_sH = D; a.o_sS = N1 * D;
+        if (layout == LAYOUT_TND) { a.lse_sH = 1; a.lse_sS = N1; }
+        else { a.lse_sH = gq.S; a.lse_sS = 1; }
+    }
+    a.q_rowmul = N1 * D;
+    a.k_rowmul = N2 * D;
+    a.v_rowmul = N2 * D;
+    a.o_rowmul = N1 * D;
+    a.lse_rowmul = N1;
+
+    std::vector<BatchInfo> bi((size_t)B);
+    for (int64_t b = 0; b < B; ++b) {
+        bi[(size_t)b].q_row0 = layout == LAYOUT_TND ? qstart[(size_t)b] : b * gq.S;
+        bi[(size_t)b].kv_row0 = layout == LAYOUT_TND ? kvstart[(size_t)b] : b * gk.S;
+        bi[(size_t)b].lq = (int32_t)lq[(size_t)b];
+        bi[(size_t)b].lkv = (int32_t)lkv[(size_t)b];
+    }
+    // One tile per (batch, q block, 128-row slice of the block, head); a tile
+    // never straddles two q blocks.  Padded layouts also cover padding rows.
+    std::vector<Tile> tiles;
+    for (int64_t b = 0; b < B; ++b) {
+        const int64_t rows = layout == LAYOUT_TND ? lq[(size_t)b] : gq.S;
+        for (int64_t qb = 0; qb * X < rows; ++qb) {
+            const int64_t bend = std::min<int64_t>((qb + 1) * X, rows);
+            for (int64_t q0 = qb * X; q0 < bend; q0 += kBlockM) {
+                const int64_t q1 = std::min<int64_t>(q0 + kBlockM, bend);
+                for (int64_t h = 0; h < N1; ++h)
+                    tiles.push_back(Tile{(int32_t)b, (int32_t)h, (int32_t)q0, (int32_t)q1});
+            }
+        }
+    }
+    if (tiles.size() > (size_t)INT32_MAX) return FIA_ERR_UNSUPPORTED;
+    p->n_tiles = (int64_t)tiles.size();
+    a.n_tiles = (int32_t)tiles.size();
+    p->off_batch = 0;
+    uint64_t end = put(p->host_tables, 0, bi);
+    p->off_tiles = align_up(end, 256);
+    put(p->host_tables, p->off_tiles, tiles);
+    finish_tables(p.get());
+    p->off_cnt = p->tables_bytes;
+    p->off_idx = align_up(p->off_cnt + (uint64_t)p->n_rows * 4, 256);
+    p->workspace_bytes = align_up(p->off_idx + (uint64_t)p->n_rows * nkb * 4, 256);
+    *workspace_size = p->workspace_bytes;
+    *plan_out = p.release();
+    return FIA_OK;
+}
+
+fia_status bsa_schedule_layout(const fia_plan* plan, uint64_t* cnt_offset, uint64_t* idx_offset,
+                               int64_t* nqb, int64_t* nkb)
+{
+    if (!plan || !cnt_offset || !idx_offset || !nqb || !nkb) return FIA_ERR_NULLPTR;
+    if (plan->kind != KIND_BSA) return FIA_ERR_PARAM;
+    *cnt_offset = plan->off_cnt;
+    *idx_offset = plan->off_idx;
+    *nqb = plan->bsa_nqb;
+    *nkb = plan->bsa_nkb;
+    return FIA_OK;
+}
+
+static fia_status run_common(void* ws, uint64_t ws_size, fia_plan* p, void* stream, bool bsa)
+{
+    if (!p) return FIA_ERR_NULLPTR;
+    if (bsa != (p->kind == KIND_BSA) && p->kind != KIND_EMPTY) return FIA_ERR_PARAM;
+    if (p->kind == KIND_EMPTY) return FIA_OK;
+    if (ws_size < p->workspace_bytes || (!ws && p->workspace_bytes)) return FIA_ERR_WORKSPACE;
+    unsigned char* w = (unsigned char*)ws;
+    const void* src = p->pinned_tables ? p->pinned_tables : (const void*)p->host_tables.data();
+    if (p->tables_bytes) {
+        if (copy_tables(w, src, p->tables_bytes, stream)) return FIA_ERR_HIP;
+        if (p->pinned_tables && record_copy_done(&p->copy_done, stream)) return FIA_ERR_HIP;
+    }
+    int rc = 0;
+    if (p->kind == KIND_DECODE) {
+        DecodeArgs d = p->dec;
+        d.batch = (const DecBatch*)(w + p->off_batch);
+        d.part_o = (float*)(w + p->off_part_o);
+        d.part_lse = (float*)(w + p->off_part_lse);
+        rc = launch_decode(*p, d, stream);
+    } else {
+        AttnArgs a = p->attn;
+        a.batch = (const BatchInfo*)(w + p->off_batch);
+        a.tiles = (const Tile*)(w + p->off_tiles);
+        if (p->kind == KIND_BSA) {
+            a.bsa_cnt = (const int32_t*)(w + p->off_cnt);
+            a.bsa_idx = (const int32_t*)(w + p->off_idx);
+            rc = launch_bsa(*p, a, stream);
+        } else {
+            rc = launch_prefill(*p, a, stream);
+        }
+    }
+    return rc ? FIA_ERR_HIP : FIA_OK;
+}
+
+fia_status fia_run(void* workspace, uint64_t workspace_size, fia_plan* plan, void* stream)
+{
+    return run_common(workspace, workspace_size, plan, stream, false);
+}
+
+fia_status bsa_run(void* workspace, uint64_t workspace_size, fia_plan* plan, void* stream)
+{
+    return run_common(workspace, workspace_size, plan, stream, true);
+}
+
+}  // extern "C"

@@ -1,0 +1,289 @@
+"""C-ABI boundary checks that need no GPU: the library loads, exports every
+function include/fia.h declares, and phase 1 validates inputs with the
+status codes the header documents (constraints of the fused-infer-attention
+and block-sparse pages).  Phase 1 never launches or reads device data, so
+CPU tensors stand in for device tensors here."""
+import os
+import re
+
+import numpy as np
+import pytest
+import torch
+
+import attention_fia_fwd_amd as fia
+from attention_fia_fwd_amd import _abi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+INT_MAX = 2147483647
+
+
+def declared_functions():
+    names = set()
+    for fn in os.listdir(os.path.join(ROOT, "include")):
+        if fn.endswith(".h"):
+            src = open(os.path.join(ROOT, "include", fn)).read()
+            src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+            for m in re.finditer(r"^[\w\s\*]*?\b(\w+)\s*\([^;{]*\)\s*;", src, flags=re.M):
+                if m.group(1) not in ("if", "while", "sizeof"):
+                    names.add(m.group(1))
+    return names
+
+
+@pytest.fixture(scope="module", autouse=True)
+def built():
+    if not os.path.exists(_abi.LIB_PATH):
+        fia.build()
+
+
+def test_header_declares_the_two_phase_api():
+    names = declared_functions()
+    for n in ["fia_get_workspace_size", "fia_run", "bsa_get_workspace_size", "bsa_run",
+              "fia_plan_destroy", "fia_status_string", "fia_params_init", "bsa_params_init",
+              "bsa_schedule_layout"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _abi.lib()
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing
+
+
+def test_status_strings():
+    for s in range(9):
+        assert fia.fia_status_string(s).startswith(["FIA_OK", "FIA_ERR"][s > 0])
+
+
+def _desc(shape, dtype=torch.bfloat16):
+    t = torch.zeros(shape, dtype=dtype)
+    return t, fia.describe(t)
+
+
+def _params(**kw):
+    p = fia.fia_params()
+    fia.fia_params_init(p)
+    layout = kw.pop("input_layout", "BNSD").encode()
+    p.input_layout = layout
+    for k, v in kw.items():
+        setattr(p, k, v)
+    p._layout_ref = layout
+    return p
+
+
+def _phase1(q, k, v, p, out=None, lse=None, mask=None, bt=None):
+    keep = [q, k, v, out, lse, mask, bt]
+    dq = fia.describe(q)
+    o = out if out is not None else torch.zeros(*q.shape[:-1], v.shape[-1], dtype=q.dtype)
+    keep.append(o)
+    st, ws, plan = fia.fia_get_workspace_size(dq, fia.describe(k), fia.describe(v),
+                                              fia.describe(mask), fia.describe(bt), p,
+                                              fia.describe(o), fia.describe(lse))
+    fia.fia_plan_destroy(plan)
+    return st, ws
+
+
+def test_defaults_of_params_init():
+    p = fia.fia_params()
+    fia.fia_params_init(p)
+    assert p.input_layout == b"BSH" and p.scale_value == 1.0
+    assert p.pre_tokens == INT_MAX and p.next_tokens == INT_MAX
+    assert p.sparse_mode == 0 and p.block_size == 0 and p.return_softmax_lse == 0
+    b = fia.bsa_params()
+    fia.bsa_params_init(b)
+    assert tuple(b.block_shape) == (128, 128) and b.inner_precise == 4
+
+
+def test_valid_prefill_plan_and_workspace():
+    q = torch.zeros(2, 4, 300, 128, dtype=torch.bfloat16)
+    k = torch.zeros(2, 2, 300, 128, dtype=torch.bfloat16)
+    st, ws = _phase1(q, k, k, _params(num_heads=4, num_key_value_heads=2, sparse_mode=3))
+    assert st == _abi.FIA_OK
+    # tables: per-batch info + one tile per (b, h, 128 rows); 256-aligned
+    ntiles = 2 * 4 * 3
+    assert ws >= 2 * 24 + ntiles * 16 and ws % 256 == 0
+
+
+@pytest.mark.parametrize("case, code", [
+    ("kdtype", _abi.FIA_ERR_DTYPE),
+    ("f32", _abi.FIA_ERR_DTYPE),
+    ("layout", _abi.FIA_ERR_LAYOUT),
+    ("variant_layout", _abi.FIA_ERR_UNSUPPORTED),
+    ("gqa_indivisible", _abi.FIA_ERR_PARAM),
+    ("gqa_ratio", _abi.FIA_ERR_PARAM),
+    ("mode5", _abi.FIA_ERR_PARAM),
+    ("mode1_no_mask", _abi.FIA_ERR_NULLPTR),
+    ("template_shape", _abi.FIA_ERR_SHAPE),
+    ("mask_dtype", _abi.FIA_ERR_DTYPE),
+    ("heads_mismatch", _abi.FIA_ERR_SHAPE),
+    ("len_too_long", _abi.FIA_ERR_SHAPE),
+    ("len_count", _abi.FIA_ERR_PARAM),
+    ("lse_missing", _abi.FIA_ERR_NULLPTR),
+    ("lse_shape", _abi.FIA_ERR_SHAPE),
+    ("head_dim", _abi.FIA_ERR_UNSUPPORTED),
+    ("inner_precise", _abi.FIA_ERR_PARAM),
+])
+def test_prefill_validation_codes(case, code):
+    B, N, S, D = 2, 4, 64, 128
+    q = torch.zeros(B, N, S, D, dtype=torch.bfloat16)
+    k = torch.zeros(B, 2, S, D, dtype=torch.bfloat16)
+    v = k
+    kw = dict(num_heads=N, num_key_value_heads=2, sparse_mode=3)
+    mask = lse = None
+    layout = "BNSD"
+    if case == "kdtype":
+        k = k.to(torch.float16)
+    elif case == "f32":
+        q, k, v = q.float(), k.float(), v.float()
+    elif case == "layout":
+        layout = "SBH"
+    elif case == "variant_layout":
+        layout = "BNSD_BSND"
+    elif case == "gqa_indivisible":
+        kw["num_key_value_heads"] = 3
+    elif case == "gqa_ratio":
+        q = torch.zeros(B, 128, S, D, dtype=torch.bfloat16)
+        k = v = torch.zeros(B, 1, S, D, dtype=torch.bfloat16)
+        kw.update(num_heads=128, num_key_value_heads=1)
+        q = q[:, :, :1]  # keep it small: the ratio check comes first
+        q = torch.zeros(B, 128, 2, D, dtype=torch.bfloat16)
+        k = v = torch.zeros(B, 1, 2, D, dtype=torch.bfloat16)
+    elif case == "mode5":
+        kw["sparse_mode"] = 5
+    elif case == "mode1_no_mask":
+        kw["sparse_mode"] = 1
+    elif case == "template_shape":
+        mask = torch.zeros(1024, 1024, dtype=torch.uint8)
+    elif case == "mask_dtype":
+        kw["sparse_mode"] = 1
+        mask = torch.zeros(S, S, dtype=torch.float32)
+    elif case == "heads_mismatch":
+        kw["num_heads"] = 8
+    elif case == "len_too_long":
+        arr = np.array([64, 65], dtype=np.int64)
+        kw["actual_seq_qlen"] = arr.ctypes.data
+        kw["n_actual_seq_qlen"] = 2
+        kw["_keep"] = arr
+    elif case == "len_count":
+        arr = np.array([64, 65, 3], dtype=np.int64)[:2]
+        arr = np.ascontiguousarray(arr)
+        kw["actual_seq_qlen"] = arr.ctypes.data
+        kw["n_actual_seq_qlen"] = 0
+        kw["_keep"] = arr
+        # count 0 with a pointer: neither 1 nor >= B
+    elif case == "lse_missing":
+        kw["return_softmax_lse"] = 1
+    elif case == "lse_shape":
+        kw["return_softmax_lse"] = 1
+        lse = torch.zeros(B, N, S, dtype=torch.float32)
+    elif case == "head_dim":
+        q = torch.zeros(B, N, S, 96, dtype=torch.bfloat16)
+        k = v = torch.zeros(B, 2, S, 96, dtype=torch.bfloat16)
+    elif case == "inner_precise":
+        kw["inner_precise"] = 4
+    keep = kw.pop("_keep", None)
+    p = _params(input_layout=layout, **kw)
+    st, _ = _phase1(q, k, v, p, lse=lse, mask=mask)
+    assert st == code, (case, fia.fia_status_string(st))
+
+
+def test_paged_decode_validation():
+    B, QN, KVN, D, bs = 2, 8, 2, 128, 16
+    lkv = np.array([40, 17], dtype=np.int64)
+    nblk = 3 + 2
+    q = torch.zeros(B, QN, 1, D, dtype=torch.bfloat16)
+    pool = torch.zeros(nblk, KVN, bs, D, dtype=torch.bfloat16)
+    bt = torch.zeros(B, 3, dtype=torch.int32)
+
+    def run(pool=pool, bt=bt, lkv=lkv, block_size=bs, q=q):
+        p = _params(num_heads=QN, num_key_value_heads=KVN, block_size=block_size)
+        if lkv is not None:
+            p.actual_seq_kvlen = lkv.ctypes.data
+            p.n_actual_seq_kvlen = lkv.size
+        return _phase1(q, pool, pool, p, bt=bt)[0]
+
+    assert run() == _abi.FIA_OK
+    assert run(block_size=8) == _abi.FIA_ERR_PARAM
+    assert run(lkv=None) == _abi.FIA_ERR_PARAM
+    assert run(bt=torch.zeros(B, 2, dtype=torch.int32)) == _abi.FIA_ERR_SHAPE
+    assert run(bt=torch.zeros(B, 3, dtype=torch.int64)) == _abi.FIA_ERR_DTYPE
+    assert run(pool=torch.zeros(4, KVN, bs, D, dtype=torch.bfloat16)) == _abi.FIA_ERR_SHAPE
+    # paged prefill is not provided
+    q2 = torch.zeros(B, QN, 4, D, dtype=torch.bfloat16)
+    assert run(q=q2) == _abi.FIA_ERR_UNSUPPORTED
+
+
+def test_tnd_requires_cumulative_lengths():
+    q = torch.zeros(30, 4, 128, dtype=torch.bfloat16)
+    k = torch.zeros(30, 4, 128, dtype=torch.bfloat16)
+    p = _params(input_layout="TND", num_heads=4, sparse_mode=3)
+    assert _phase1(q, k, k, p)[0] == _abi.FIA_ERR_PARAM
+    bad = np.array([10, 5], dtype=np.int64)       # decreasing
+    p.actual_seq_qlen, p.n_actual_seq_qlen = bad.ctypes.data, 2
+    p.actual_seq_kvlen, p.n_actual_seq_kvlen = bad.ctypes.data, 2
+    assert _phase1(q, k, k, p)[0] == _abi.FIA_ERR_SHAPE
+    good = np.array([10, 30], dtype=np.int64)
+    p.actual_seq_qlen, p.actual_seq_kvlen = good.ctypes.data, good.ctypes.data
+    assert _phase1(q, k, k, p)[0] == _abi.FIA_OK
+    p.sparse_mode = 1
+    assert _phase1(q, k, k, p)[0] == _abi.FIA_ERR_PARAM
+
+
+def test_empty_query_is_ok_with_zero_workspace():
+    q = torch.zeros(2, 4, 0, 128, dtype=torch.bfloat16)
+    k = torch.zeros(2, 4, 8, 128, dtype=torch.bfloat16)
+    st, ws = _phase1(q, k, k, _params(num_heads=4))
+    assert st == _abi.FIA_OK and ws == 0
+
+
+def test_run_rejects_small_workspace_without_touching_the_gpu():
+    q = torch.zeros(1, 2, 64, 64, dtype=torch.float16)
+    p = _params(num_heads=2, sparse_mode=3)
+    o = torch.zeros_like(q)
+    st, ws, plan = fia.fia_get_workspace_size(fia.describe(q), fia.describe(q), fia.describe(q),
+                                              None, None, p, fia.describe(o), None)
+    assert st == _abi.FIA_OK and ws > 0
+    assert fia.fia_run(0, 0, plan, 0) == _abi.FIA_ERR_WORKSPACE
+    assert fia.fia_run(1 << 20, ws - 1, plan, 0) == _abi.FIA_ERR_WORKSPACE
+    # a prefill plan is not a block-sparse plan
+    assert fia.bsa_run(1 << 20, ws, plan, 0) == _abi.FIA_ERR_PARAM
+    fia.fia_plan_destroy(plan)
+
+
+def _bsa_phase1(q, k, v, m, **kw):
+    p = fia.bsa_params()
+    fia.bsa_params_init(p)
+    lay = kw.pop("layout", "BNSD").encode()
+    p.q_input_layout = p.kv_input_layout = lay
+    for key, val in kw.items():
+        setattr(p, key, val)
+    o = torch.zeros_like(q)
+    st, ws, plan = fia.bsa_get_workspace_size(fia.describe(q), fia.describe(k), fia.describe(v),
+                                              fia.describe(m), None, None, p, fia.describe(o),
+                                              None)
+    fia.fia_plan_destroy(plan)
+    return st, ws
+
+
+def test_bsa_validation():
+    q = torch.zeros(1, 4, 300, 128, dtype=torch.bfloat16)
+    k = torch.zeros(1, 2, 260, 128, dtype=torch.bfloat16)
+    m = torch.zeros(1, 4, 3, 3, dtype=torch.uint8)
+    assert _bsa_phase1(q, k, k, m, num_heads=4, num_key_value_heads=2)[0] == _abi.FIA_OK
+    assert _bsa_phase1(q, k, k, torch.zeros(1, 4, 3, 2, dtype=torch.uint8), num_heads=4,
+                       num_key_value_heads=2)[0] == _abi.FIA_ERR_SHAPE
+    st = _bsa_phase1(q, k, k, m, num_heads=4, num_key_value_heads=2)
+    bad = fia.bsa_params()
+    for field, val, code in [("inner_precise", 0, _abi.FIA_ERR_PARAM),
+                             ("mask_type", 1, _abi.FIA_ERR_PARAM),
+                             ("pre_tokens", 5, _abi.FIA_ERR_PARAM),
+                             ("num_key_value_heads", 3, _abi.FIA_ERR_PARAM)]:
+        kw = dict(num_heads=4, num_key_value_heads=2)
+        kw[field] = val
+        assert _bsa_phase1(q, k, k, m, **kw)[0] == code, field
+    # Y must be a multiple of 128
+    p_shape = dict(num_heads=4, num_key_value_heads=2)
+    pp = fia.bsa_params()
+    fia.bsa_params_init(pp)
+    q2 = torch.zeros(1, 4, 300, 96, dtype=torch.bfloat16)
+    k2 = torch.zeros(1, 2, 260, 96, dtype=torch.bfloat16)
+    assert _bsa_phase1(q2, k2, k2, m, **p_shape)[0] == _abi.FIA_ERR_UNSUPPORTED
