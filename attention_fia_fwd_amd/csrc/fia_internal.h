@@ -108,15 +108,16 @@ struct fia_plan {
     int32_t layout = fia::LAYOUT_BNSD;
     int64_t B = 0, QN = 0, KVN = 0, G = 0, Sq = 0, Skv = 0, Dqk = 0, Dv = 0;
 
-    // Schedule tables, copied to the head of the workspace by each run.
+    // Schedule tables: built on the host, uploaded once by phase 1 into a
+    // device buffer the plan owns (dev_tables).
     std::vector<unsigned char> host_tables;
-    void* pinned_tables = nullptr;   // pinned copy of host_tables when available
-    void* copy_done = nullptr;       // event recorded after the last schedule copy
+    void* dev_tables = nullptr;
     uint64_t tables_bytes = 0;
     uint64_t workspace_bytes = 0;
 
-    // byte offsets inside the workspace
+    // byte offsets inside dev_tables
     uint64_t off_batch = 0, off_tiles = 0;
+    // byte offsets inside the caller's workspace
     uint64_t off_part_o = 0, off_part_lse = 0;
     uint64_t off_cnt = 0, off_idx = 0;
 
@@ -135,9 +136,7 @@ namespace fia {
 int launch_prefill(const fia_plan& p, const AttnArgs& a, void* stream);
 int launch_decode(const fia_plan& p, const DecodeArgs& a, void* stream);
 int launch_bsa(const fia_plan& p, const AttnArgs& a, void* stream);
-int copy_tables(void* dst, const void* src, uint64_t bytes, void* stream);
-void* alloc_pinned(uint64_t bytes);
-void free_pinned(void* ptr);
-int record_copy_done(void** event, void* stream);
-void wait_and_release(void* event);
+// Device copy of a plan's schedule tables (synchronous); nullptr on failure.
+void* upload_tables(const void* src, uint64_t bytes);
+void free_tables(void* dev);
 }  // namespace fia

@@ -655,9 +655,10 @@ int launch_attn(const fia_plan& p, const AttnArgs& a, hipStream_t stream)
     const size_t lds = 2 * STAGE * sizeof(uint16_t);
     static bool configured = false;
     if (!configured) {
-        hipError_t e = hipFuncSetAttribute((const void*)attn_fwd<DT, DQK, DV, BSA>,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return (int)e;
+        // raise the dynamic LDS limit past the 64 KB default (gfx950: 160 KB)
+        (void)hipFuncSetAttribute((const void*)attn_fwd<DT, DQK, DV, BSA>,
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        (void)hipGetLastError();
         configured = true;
     }
     if (p.n_tiles == 0) return 0;
@@ -719,47 +720,29 @@ int launch_decode(const fia_plan& p, const DecodeArgs& a, void* stream)
     return (int)hipErrorInvalidValue;
 }
 
-int copy_tables(void* dst, const void* src, uint64_t bytes, void* stream)
-{
-    return (int)hipMemcpyAsync(dst, src, bytes, hipMemcpyHostToDevice, (hipStream_t)stream);
-}
-
-void* alloc_pinned(uint64_t bytes)
+void* upload_tables(const void* src, uint64_t bytes)
 {
     int n = 0;
     if (hipGetDeviceCount(&n) != hipSuccess || n == 0) {
         (void)hipGetLastError();
         return nullptr;
     }
-    void* ptr = nullptr;
-    if (hipHostMalloc(&ptr, bytes, hipHostMallocDefault) != hipSuccess) {
+    void* dev = nullptr;
+    if (hipMalloc(&dev, bytes) != hipSuccess) {
         (void)hipGetLastError();
         return nullptr;
     }
-    return ptr;
-}
-
-void free_pinned(void* ptr)
-{
-    if (ptr) (void)hipHostFree(ptr);
-}
-
-int record_copy_done(void** event, void* stream)
-{
-    if (!*event) {
-        hipEvent_t e;
-        hipError_t rc = hipEventCreateWithFlags(&e, hipEventDisableTiming);
-        if (rc != hipSuccess) return (int)rc;
-        *event = (void*)e;
+    if (hipMemcpy(dev, src, bytes, hipMemcpyHostToDevice) != hipSuccess) {
+        (void)hipGetLastError();
+        (void)hipFree(dev);
+        return nullptr;
     }
-    return (int)hipEventRecord((hipEvent_t)*event, (hipStream_t)stream);
+    return dev;
 }
 
-void wait_and_release(void* event)
+void free_tables(void* dev)
 {
-    if (!event) return;
-    (void)hipEventSynchronize((hipEvent_t)event);
-    (void)hipEventDestroy((hipEvent_t)event);
+    if (dev) (void)hipFree(dev);
 }
 
 }  // namespace fia

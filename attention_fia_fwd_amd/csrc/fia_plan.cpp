@@ -1,7 +1,7 @@
 // Phase 1 of the fused inference attention and the block-sparse attention:
-// input validation, dispatch, schedule tables and workspace sizing.  Pure
-// host code; the only HIP call is the optional pinned allocation of the
-// schedule copy.
+// input validation, dispatch, schedule tables and workspace sizing.  Host
+// code; its only HIP calls allocate and fill the plan's device copy of the
+// schedule tables (skipped when no device is visible).
 //
 // Validation follows the parameter descriptions and constraints of pages
 // "torch_npu.npu_fused_infer_attention_score_v2", "torch_npu.npu_prompt_flash_
@@ -172,11 +172,7 @@ void finish_tables(fia_plan* p)
 {
     p->tables_bytes = align_up(p->host_tables.size(), 256);
     p->host_tables.resize(p->tables_bytes);
-    if (p->tables_bytes) {
-        p->pinned_tables = alloc_pinned(p->tables_bytes);
-        if (p->pinned_tables)
-            std::memcpy(p->pinned_tables, p->host_tables.data(), p->tables_bytes);
-    }
+    if (p->tables_bytes) p->dev_tables = upload_tables(p->host_tables.data(), p->tables_bytes);
 }
 
 }  // namespace
@@ -226,9 +222,7 @@ const char* fia_status_string(fia_status s)
 void fia_plan_destroy(fia_plan* plan)
 {
     if (!plan) return;
-    // the last run's schedule copy may still read the pinned buffer
-    if (plan->copy_done) wait_and_release(plan->copy_done);
-    if (plan->pinned_tables) free_pinned(plan->pinned_tables);
+    if (plan->dev_tables) free_tables(plan->dev_tables);
     delete plan;
 }
 
@@ -502,7 +496,7 @@ fia_status fia_get_workspace_size(const fia_tensor* query, const fia_tensor* key
         p->off_batch = 0;
         put(p->host_tables, 0, db);
         finish_tables(p.get());
-        p->off_part_o = p->tables_bytes;
+        p->off_part_o = 0;
         p->off_part_lse = align_up(p->off_part_o + (uint64_t)items * Gc * Dv * 4, 256);
         p->workspace_bytes = align_up(p->off_part_lse + (uint64_t)items * Gc * 4, 256);
         *workspace_size = p->workspace_bytes;
@@ -586,7 +580,7 @@ fia_status fia_get_workspace_size(const fia_tensor* query, const fia_tensor* key
     p->off_tiles = align_up(end, 256);
     put(p->host_tables, p->off_tiles, tiles);
     finish_tables(p.get());
-    p->workspace_bytes = p->tables_bytes;
+    p->workspace_bytes = 0;                  // prefill needs no scratch
     *workspace_size = p->workspace_bytes;
     *plan_out = p.release();
     return FIA_OK;
@@ -783,7 +777,7 @@ fia_status bsa_get_workspace_size(const fia_tensor* query, const fia_tensor* key
     p->off_tiles = align_up(end, 256);
     put(p->host_tables, p->off_tiles, tiles);
     finish_tables(p.get());
-    p->off_cnt = p->tables_bytes;
+    p->off_cnt = 0;
     p->off_idx = align_up(p->off_cnt + (uint64_t)p->n_rows * 4, 256);
     p->workspace_bytes = align_up(p->off_idx + (uint64_t)p->n_rows * nkb * 4, 256);
     *workspace_size = p->workspace_bytes;
@@ -809,23 +803,24 @@ static fia_status run_common(void* ws, uint64_t ws_size, fia_plan* p, void* stre
     if (bsa != (p->kind == KIND_BSA) && p->kind != KIND_EMPTY) return FIA_ERR_PARAM;
     if (p->kind == KIND_EMPTY) return FIA_OK;
     if (ws_size < p->workspace_bytes || (!ws && p->workspace_bytes)) return FIA_ERR_WORKSPACE;
-    unsigned char* w = (unsigned char*)ws;
-    const void* src = p->pinned_tables ? p->pinned_tables : (const void*)p->host_tables.data();
-    if (p->tables_bytes) {
-        if (copy_tables(w, src, p->tables_bytes, stream)) return FIA_ERR_HIP;
-        if (p->pinned_tables && record_copy_done(&p->copy_done, stream)) return FIA_ERR_HIP;
+    if (p->tables_bytes && !p->dev_tables) {
+        // phase 1 ran where no device was visible; upload now
+        p->dev_tables = upload_tables(p->host_tables.data(), p->tables_bytes);
+        if (!p->dev_tables) return FIA_ERR_HIP;
     }
+    unsigned char* w = (unsigned char*)ws;
+    const unsigned char* tb = (const unsigned char*)p->dev_tables;
     int rc = 0;
     if (p->kind == KIND_DECODE) {
         DecodeArgs d = p->dec;
-        d.batch = (const DecBatch*)(w + p->off_batch);
+        d.batch = (const DecBatch*)(tb + p->off_batch);
         d.part_o = (float*)(w + p->off_part_o);
         d.part_lse = (float*)(w + p->off_part_lse);
         rc = launch_decode(*p, d, stream);
     } else {
         AttnArgs a = p->attn;
-        a.batch = (const BatchInfo*)(w + p->off_batch);
-        a.tiles = (const Tile*)(w + p->off_tiles);
+        a.batch = (const BatchInfo*)(tb + p->off_batch);
+        a.tiles = (const Tile*)(tb + p->off_tiles);
         if (p->kind == KIND_BSA) {
             a.bsa_cnt = (const int32_t*)(w + p->off_cnt);
             a.bsa_idx = (const int32_t*)(w + p->off_idx);

@@ -1,0 +1,251 @@
+#!/usr/bin/env python3
+"""Benchmark of the MI355X fused inference attention forward.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2] [--secondary c1,c3,c4,c5]
+
+One step is one fia_run (phase 2) of the headline workload: the GQA causal
+prefill, bf16, B=4, Q_N=32, KV_N=8, max S=4096, D=128, BSND, per-batch
+lengths uniform in [1024, 4096] (seeded).  Inputs are resident in HBM before
+the timed region; the plan (phase 1, host validation + schedule upload) is
+built once and its host time is reported separately.  `value` is
+algorithmic TFLOP/s: 2 * (D_qk + D_v) flops per allowed (query, key) pair,
+pairs counted exactly from the lengths and the mask mode (masked pairs and
+skipped tiles are not counted).
+
+The other workloads (dense causal fp16 prefill, paged GQA decode, varlen TND
+prefill, block-sparse prefill) are timed the same way and reported under
+"secondary"; the decode line is in GB/s of algorithmic bytes (every KV byte of
+every kv head once, plus q, out, lse and the block-table entries read).
+
+The JSON line carries the roofline of the headline kernel (achieved from HIP
+events on the stream the kernel runs on) and the fp64 CPU oracle timed on a
+bounded sample of the same workload on this host.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+sys.path.insert(0, os.path.join(ROOT, "tests"))
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16/fp16 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+
+
+def allowed_pairs_fia(case) -> int:
+    """Exact number of allowed (i, j) pairs summed over batches and query
+    heads (counts only, from lengths and the mask mode)."""
+    import numpy as np
+    B = case.B
+    lq = case.lq if case.lq is not None else np.full(B, case.Sq)
+    lkv = case.lkv if case.lkv is not None else np.full(B, case.Skv)
+    total = 0
+    for b in range(B):
+        Lq, Lkv = int(lq[b]), int(lkv[b])
+        if case.decode:
+            total += Lkv
+            continue
+        i = np.arange(Lq, dtype=np.int64)
+        d = Lkv - Lq
+        if case.sparse_mode == 3:
+            hi = np.minimum(i + d, Lkv - 1)
+            lo = np.zeros_like(i)
+        elif case.sparse_mode == 2:
+            hi = np.minimum(i, Lkv - 1)
+            lo = np.zeros_like(i)
+        elif case.sparse_mode == 0 and case.atten_mask is None:
+            hi = np.full_like(i, Lkv - 1)
+            lo = np.zeros_like(i)
+        else:
+            raise ValueError("pair count implemented for modes 0 (no mask), 2, 3")
+        total += int(np.clip(hi - lo + 1, 0, None).sum())
+    return total * case.QN
+
+
+def allowed_pairs_bsa(case) -> int:
+    import numpy as np
+    m = case.block_mask.detach().cpu().numpy() != 0
+    B, N, nqb, nkb = m.shape
+    lq = case.lq if case.lq is not None else np.full(B, case.Sq)
+    lkv = case.lkv if case.lkv is not None else np.full(B, case.Skv)
+    total = 0
+    for b in range(B):
+        rows = np.clip(np.minimum((np.arange(nqb) + 1) * case.X, lq[b]) - np.arange(nqb) * case.X, 0, None)
+        cols = np.clip(np.minimum((np.arange(nkb) + 1) * case.Y, lkv[b]) - np.arange(nkb) * case.Y, 0, None)
+        total += int(np.einsum("hqk,q,k->", m[b].astype(np.int64), rows, cols))
+    return total
+
+
+def decode_bytes(case) -> int:
+    import numpy as np
+    L = case.lkv.astype(np.int64)
+    kv = int(L.sum()) * case.KVN * (case.Dqk + case.Dv) * 2
+    qo = case.B * case.QN * (case.Dqk + case.Dv) * 2
+    lse = case.B * case.QN * 4 if case.return_lse else 0
+    bt = 4 * int(((L + case.block_size - 1) // case.block_size).sum()) if case.block_table is not None else 0
+    return kv + qo + lse + bt
+
+
+def time_plan(plan, steps: int, warmup: int):
+    """Warm up, then time `steps` runs: wall clock between synchronizations
+    and HIP events on the stream the kernels are launched on."""
+    import torch
+    for _ in range(warmup):
+        plan.run()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(steps):
+        plan.run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / steps
+    ev = e0.elapsed_time(e1) / 1e3 / steps
+    return wall, ev
+
+
+def build_plan(name, case):
+    from fia_gpu import bsa_plan, fia_plan, to_dev
+    to_dev(case)
+    t0 = time.perf_counter()
+    plan = bsa_plan(case) if name == "c5" else fia_plan(case)
+    t1 = time.perf_counter()
+    return plan, (t1 - t0) * 1e6
+
+
+def measure(name, steps, warmup):
+    import torch
+    import workloads as W
+    case = W.WORKLOADS[name](device="cuda")
+    torch.cuda.synchronize()
+    plan, phase1_us = build_plan(name, case)
+    wall, ev = time_plan(plan, steps, warmup)
+    res = {"workload": case.name, "steps": steps, "ms_per_step": wall * 1e3,
+           "kernel_ms": ev * 1e3, "phase1_us": round(phase1_us, 1)}
+    if name == "c3":
+        nbytes = decode_bytes(case)
+        res.update(value=nbytes / wall / 1e9, unit="GB/s", algorithmic_bytes=nbytes,
+                   roofline={"bound": "hbm", "achieved": nbytes / ev / 1e9, "peak": PEAK_HBM_GBS,
+                             "unit": "GB/s", "frac": nbytes / ev / 1e9 / PEAK_HBM_GBS})
+    else:
+        if name == "c5":
+            pairs = allowed_pairs_bsa(case)
+            flops = 2 * (case.D + case.D) * pairs
+        else:
+            pairs = allowed_pairs_fia(case)
+            flops = 2 * (case.Dqk + case.Dv) * pairs
+        res.update(value=flops / wall / 1e12, unit="TFLOP/s", algorithmic_flops=flops,
+                   roofline={"bound": "mfma", "achieved": flops / ev / 1e12,
+                             "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                             "frac": flops / ev / 1e12 / PEAK_BF16_TFLOPS})
+    plan.close()
+    del case
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(name="c2", target_s=15.0):
+    """The fp64 oracle as it is, on a seeded sample of query rows of the
+    headline workload, on this host's cores."""
+    import numpy as np
+    import oracle
+    import workloads as W
+    from fia_gpu import sample_rows
+    case = W.WORKLOADS[name](device="cpu")
+    lq = case.lq
+    rng = np.random.default_rng(99)
+
+    def rows_of(n):
+        out = []
+        for _ in range(n):
+            b = int(rng.integers(case.B))
+            out.append((b, int(rng.integers(case.QN)), int(rng.integers(int(lq[b])))))
+        return out
+
+    def flops_of(rows):
+        # causal, Lq = Lkv: row i sees i + 1 keys
+        return sum(2 * (case.Dqk + case.Dv) * (i + 1) for _, _, i in rows)
+
+    pilot = rows_of(64)
+    t0 = time.perf_counter()
+    oracle.attention(case, rows=pilot)
+    dt = time.perf_counter() - t0
+    n = int(min(200000, max(64, 64 * target_s / max(dt, 1e-3))))
+    rows = rows_of(n)
+    t0 = time.perf_counter()
+    oracle.attention(case, rows=rows)
+    dt = time.perf_counter() - t0
+    fl = flops_of(rows)
+    return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle", "seconds": round(dt, 2),
+            "sample": f"{n} seeded random (batch, head, row) query rows of {case.name}, "
+                      f"fp64, OpenMP over rows"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="c2")
+    ap.add_argument("--secondary", default="c1,c3,c4,c5",
+                    help="comma list of other workloads to time ('' for none)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build runs on a single MI355X "
+              f"(asked for --gpus {args.gpus}); run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from attention_fia_fwd_amd import _abi
+    if not os.path.exists(_abi.LIB_PATH):
+        from attention_fia_fwd_amd.build import build
+        build()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    props = torch.cuda.get_device_properties(0)
+
+    head = measure(args.workload, args.steps, args.warmup)
+    secondary = {}
+    for name in [s for s in args.secondary.split(",") if s and s != args.workload]:
+        secondary[name] = measure(name, max(5, args.steps // 2), max(2, args.warmup // 2))
+        print(f"# {name}: {json.dumps(secondary[name])}", file=sys.stderr, flush=True)
+
+    cpu = None if args.no_cpu_baseline else cpu_baseline(args.workload if args.workload in ("c2",) else "c2")
+    is_decode = args.workload == "c3"
+    line = {
+        "metric": "prefill TFLOP/s (% bf16 MFMA peak); paged decode KV GB/s (% HBM peak)",
+        "value": head["value"],
+        "unit": head["unit"],
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16" if args.workload == "c1" else "bf16",
+        "data": "synthetic (seeded N(0,1) inputs of the workload's shapes and length mix)",
+        "config": {"workload": head["workload"], "kernel_ms": head["kernel_ms"],
+                   "phase1_us": head["phase1_us"],
+                   "device": getattr(props, "gcnArchName", props.name),
+                   "compute_units": props.multi_processor_count},
+        "roofline": dict(head["roofline"], traffic=None),
+        "cpu_baseline": cpu,
+        "secondary": secondary,
+    }
+    if is_decode:
+        line["config"]["note"] = "decode workload"
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

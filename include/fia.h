@@ -27,11 +27,17 @@
  *   - Length arrays (actual_seq_*) are HOST pointers, copied in phase 1.
  *   - The plan keeps the tensor pointers: the tensors must stay allocated
  *     until the stream work of the last *_run on that plan has completed.
- *   - Phase 1 never touches the GPU.  Phase 2 enqueues work on `stream`
- *     (a hipStream_t; NULL = the default stream), allocates nothing and does
- *     not synchronize.  It copies the plan's schedule tables into the head
- *     of the workspace, so the workspace must not be shared by two runs in
- *     flight at the same time.
+ *   - Phase 1 launches no kernel.  It uploads the plan's schedule tables
+ *     (per-batch offsets and the tile / split order, tens of bytes per tile)
+ *     into device memory the plan owns, on the current device, with a
+ *     synchronous copy; fia_plan_destroy frees them.  Where no device is
+ *     visible, phase 1 still validates and sizes, and the upload happens at
+ *     the first run.
+ *   - Phase 2 only enqueues kernels on `stream` (a hipStream_t; NULL = the
+ *     default stream): it allocates nothing, copies nothing and does not
+ *     synchronize.  The workspace holds scratch of one run (decode partial
+ *     results, the compacted block-sparse schedule), so two runs in flight
+ *     at the same time must not share a workspace.
  *   - Results are deterministic: no atomics, fixed reduction order; two runs
  *     of one plan give bitwise identical outputs ("aclnnFusedInferAttention
  *     ScoreV5", constraints: deterministic computation).
