@@ -114,39 +114,85 @@ __device__ __forceinline__ int vpos32(int t)
     return (((t >> 2) & 3) << 3) | (((t >> 4) & 1) << 2) | (t & 3);
 }
 
-// Whether key j may be attended by query row i (sparse_mode list of the v2
-// parameter description; delta = Lkv - Lq).  Rows >= qend and keys >= lkv are
-// never allowed.
-__device__ __forceinline__ bool allowed(const AttnArgs& a, int mode, int64_t i, int64_t j,
-                                        int64_t delta, const uint8_t* mrow)
-{
-    switch (mode) {
-    case 0:
-        if (!mrow) return true;
-        return mrow[j] == 0 && (j - i >= -a.pre) && (j - i <= a.next);
-    case 1: return mrow[j] == 0;
-    case 2: return j <= i;
-    case 3: return j <= i + delta;
-    case 4: return (j - i - delta >= -a.pre) && (j - i - delta <= a.next);
-    default: return false;
-    }
-}
-
 // ---------------------------------------------------------------------------
 // Prefill / block-sparse attention.
+//
+// Workgroup: 4 waves, 128 query rows of one head; wave w owns rows
+// q0 + 32w .. q0 + 32w + 31.  Per 64-token kv tile:
+//   S^T (64 x 32 per wave) = K Q^T   two 32x32 MFMA tiles, Q in registers,
+//                                    K read from LDS (row-major, padded rows)
+//   online softmax on the S^T accumulators: lane (row, half) holds 32 of the
+//   row's 64 scores; the two halves exchange max and sum once.
+//   O^T (D_v x 32) += V^T P^T         P straight from the S^T registers as the
+//                                    B operand; V read from a row-major LDS
+//                                    tile with the gfx950 transpose read.
+// The kv index set of the B operand slots (from the S^T accumulator layout)
+// and of the A operand slots (from the transposed V reads) is the same, so
+// the contraction pairs each P value with its V row.
 // ---------------------------------------------------------------------------
+typedef short s16x4 __attribute__((__vector_size__(4 * sizeof(short))));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// Transposed LDS read (ds_read_b64_tr_b16): within each group of 16 lanes,
+// lane j supplies row j/4, columns 4(j%4)..+3 of a 4 x 16 block; lane i
+// receives column i of the 4 rows.
+__device__ __forceinline__ uint2 lds_read_tr16(const uint16_t* p)
+{
+    s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+    return __builtin_bit_cast(uint2, v);
+}
+
+// Value of x in the lane 32 positions away (the other half of the wave).
+__device__ __forceinline__ float other_half_max(float x)
+{
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float other_half_sum(float x)
+{
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Rows whose running max grows by less than 2^kLazy (in exp2 units) keep
+// their old max: p stays below 2^kLazy and no O rescale is needed.
+constexpr float kLazy = 8.f;
+// Smallest scale used in exp2(s * c - m * c): keeps masked (-inf) scores at
+// exactly 0 when the scale is 0, while every finite score gives exp2(0) = 1.
+constexpr float kMinScale = 1e-30f;
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// 16 bytes per lane from a buffer resource straight into LDS: lane i of the
+// wave writes lds_wave + 16 i.  Offsets past the resource's range read 0.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, uint16_t* lds_wave, uint32_t voff)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)lds_wave, 16, voff, 0, 0, 0);
+}
+
+// Buffer resource over rows [row0, lkv) of a row-strided tensor (rows of
+// `rowlen` elements every `stride` elements); 0 valid bytes when none.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const uint16_t* base, int64_t row0,
+                                                            int64_t lkv, int64_t stride, int rowlen)
+{
+    const int64_t n = lkv - row0;
+    const int64_t bytes = n > 0 ? ((n - 1) * stride + rowlen) * 2 : 0;
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(base + row0 * stride), (short)0,
+                                             (int)min(bytes, (int64_t)0x7fffffff), 0x00020000);
+}
+
 template <int DT, int DQK, int DV, bool BSA>
 __global__ __launch_bounds__(256, 2) void attn_fwd(AttnArgs a)
 {
     constexpr int BN = kBlockN;            // 64 kv tokens per tile
-    constexpr int KP = DQK + 8;            // K tile row pitch (elements)
-    constexpr int VP = BN + 8;             // transposed V tile row pitch
-    constexpr int KT = BN * KP;
-    constexpr int STAGE = KT + DV * VP;
+    constexpr int KCH = DQK / 8;           // 16-byte chunks per K row
+    constexpr int VCH = DV / 8;            // 16-byte chunks per V row
+    constexpr int KT = BN * DQK;           // K tile elements (rows not padded)
+    constexpr int STAGE = KT + BN * DV;
     constexpr int NQ = DQK / 16;           // k-steps of S^T = K Q^T
     constexpr int NO = DV / 32;            // 32-row d tiles of O^T
-    constexpr int NKS = DQK / 32;          // 16-byte K chunks staged per thread
-    constexpr int NVU = 2 * DV;            // V staging units (4 rows x 8 d)
+    constexpr int NKI = BN * KCH / 256;    // K load instructions per wave per tile
+    constexpr int NVI = BN * VCH / 256;    // V load instructions per wave per tile
     using O = Ops<DT>;
 
     extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
@@ -164,8 +210,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd(AttnArgs a)
     const int Lq = bi.lq, Lkv = bi.lkv;
     const int g = h / a.G;
     const int qend = min(q1, Lq);
-    const int64_t delta = (int64_t)Lkv - Lq;
+    const int delta = Lkv - Lq;
     const int mode = a.mode;
+    const int pre = (int)a.pre, next = (int)a.next;
 
     const uint16_t* qp = (const uint16_t*)a.q + bi.q_row0 * a.q_rowmul + (int64_t)h * a.q_sH;
     const uint16_t* kp = (const uint16_t*)a.k + bi.kv_row0 * a.k_rowmul + (int64_t)g * a.k_sH;
@@ -176,12 +223,20 @@ __global__ __launch_bounds__(256, 2) void attn_fwd(AttnArgs a)
     const int row = wr0 + l32;             // this lane's query row
     const int wend = min(wr0 + 32, qend);  // rows < wend are computed
 
+    // A negative scale is moved onto Q (exact sign flip) so that c > 0.
+    const float c = fmaxf(fabsf(a.scale_log2), kMinScale);
+    const uint32_t qflip = a.scale_log2 < 0.f ? 0x80008000u : 0u;
+
     // Q as the B operand of S^T = K Q^T: lane (row, hh) holds d = 16s + 8hh.
     uint4 qf[NQ];
     if (row < qend) {
         const uint16_t* src = qp + (int64_t)row * a.q_sS + 8 * hh;
 #pragma unroll
-        for (int s = 0; s < NQ; ++s) qf[s] = *(const uint4*)(src + 16 * s);
+        for (int s = 0; s < NQ; ++s) {
+            uint4 v = *(const uint4*)(src + 16 * s);
+            v.x ^= qflip; v.y ^= qflip; v.z ^= qflip; v.w ^= qflip;
+            qf[s] = v;
+        }
     } else {
 #pragma unroll
         for (int s = 0; s < NQ; ++s) qf[s] = make_uint4(0, 0, 0, 0);
@@ -189,7 +244,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd(AttnArgs a)
 
     // kv tiles of this workgroup
     int ntiles = 0;
-    int64_t kv_lo = 0;
+    int kv_lo = 0;
     const int32_t* blist = nullptr;
     int per = 1;
     if (BSA) {
@@ -199,73 +254,65 @@ __global__ __launch_bounds__(256, 2) void attn_fwd(AttnArgs a)
         ntiles = qend > q0 ? a.bsa_cnt[rowi] * per : 0;
         blist = a.bsa_idx + rowi * a.nkb;
     } else if (qend > q0 && Lkv > 0) {
-        const int64_t last = qend - 1;
-        int64_t lo = 0, hi = Lkv;
+        const int last = qend - 1;
+        int lo = 0, hi = Lkv;
         if (mode == 0 && mbase) {
-            lo = max((int64_t)0, (int64_t)q0 - a.pre);
-            hi = min((int64_t)Lkv, last + a.next + 1);
+            lo = max(0, q0 - pre);
+            hi = min(Lkv, last + next + 1);
         } else if (mode == 2) {
-            hi = min((int64_t)Lkv, last + 1);
+            hi = min(Lkv, last + 1);
         } else if (mode == 3) {
-            hi = min((int64_t)Lkv, last + delta + 1);
+            hi = min(Lkv, last + delta + 1);
         } else if (mode == 4) {
-            lo = max((int64_t)0, (int64_t)q0 + delta - a.pre);
-            hi = min((int64_t)Lkv, last + delta + a.next + 1);
+            lo = max(0, q0 + delta - pre);
+            hi = min(Lkv, last + delta + next + 1);
         }
         if (hi > lo) {
             kv_lo = lo / BN * BN;
-            ntiles = (int)((hi - kv_lo + BN - 1) / BN);
+            ntiles = (hi - kv_lo + BN - 1) / BN;
         }
     }
-    auto tile_c0 = [&](int it) -> int64_t {
-        if (BSA) return (int64_t)blist[it / per] * a.by + (int64_t)BN * (it % per);
-        return kv_lo + (int64_t)BN * it;
+    auto tile_c0 = [&](int it) -> int {
+        if (BSA) return blist[it / per] * a.by + BN * (it % per);
+        return kv_lo + BN * it;
     };
 
-    // staging registers
-    uint4 kst[NKS];
-    uint4 vst[4];
-    const bool vunit = tid < NVU;
-    const int kv4 = tid & 15, vdc = tid >> 4;
-
-    auto load_tile = [&](int64_t c0) {
-#pragma unroll
-        for (int u = 0; u < NKS; ++u) {
-            const int ci = tid + 256 * u;
-            const int r = ci / (DQK / 8), cc = ci % (DQK / 8);
-            const int64_t j = c0 + r;
-            kst[u] = j < Lkv ? *(const uint4*)(kp + j * a.k_sS + 8 * cc) : make_uint4(0, 0, 0, 0);
-        }
-        if (vunit) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int64_t j = c0 + 4 * kv4 + r;
-                vst[r] = j < Lkv ? *(const uint4*)(vp + j * a.v_sS + 8 * vdc) : make_uint4(0, 0, 0, 0);
-            }
-        }
-    };
-    auto store_tile = [&](int buf) {
+    // Direct-to-LDS loads.  Tiles are row-major without padding; 16-byte
+    // chunk c of K row r sits at chunk c ^ (r & 7), of V row r at
+    // c ^ 2 (r & 3), which spreads the MFMA operand reads over all banks.
+    // Instruction u of wave w fills LDS slots 64 (4u + w) + lane.
+    auto load_tile = [&](int c0, int buf) {
         uint16_t* ks = smem + buf * STAGE;
         uint16_t* vs = ks + KT;
+        const __amdgpu_buffer_rsrc_t kr = rows_rsrc(kp, c0, Lkv, a.k_sS, DQK);
+        const __amdgpu_buffer_rsrc_t vr = rows_rsrc(vp, c0, Lkv, a.v_sS, DV);
 #pragma unroll
-        for (int u = 0; u < NKS; ++u) {
-            const int ci = tid + 256 * u;
-            const int r = ci / (DQK / 8), cc = ci % (DQK / 8);
-            *(uint4*)(ks + r * KP + 8 * cc) = kst[u];
+        for (int u = 0; u < NKI; ++u) {
+            const int blk = 4 * u + w;
+            const int sl = 64 * blk + lane;
+            const int r = sl / KCH, pc = sl % KCH;
+            const int cc = pc ^ (r & 7);
+            dma16(kr, ks + blk * 512, (uint32_t)(r * a.k_sS + 8 * cc) * 2u);
         }
-        if (vunit) {
-            const int pos = vpos16(4 * kv4);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const uint32_t d0 = dw(vst[0], e >> 1), d1 = dw(vst[1], e >> 1);
-                const uint32_t d2 = dw(vst[2], e >> 1), d3 = dw(vst[3], e >> 1);
-                uint2 pr;
-                pr.x = (e & 1) ? sel_hi(d0, d1) : sel_lo(d0, d1);
-                pr.y = (e & 1) ? sel_hi(d2, d3) : sel_lo(d2, d3);
-                *(uint2*)(vs + (8 * vdc + e) * VP + pos) = pr;
-            }
+        for (int u = 0; u < NVI; ++u) {
+            const int blk = 4 * u + w;
+            const int sl = 64 * blk + lane;
+            const int r = sl / VCH, pc = sl % VCH;
+            const int cc = pc ^ (2 * (r & 3));
+            dma16(vr, vs + blk * 512, (uint32_t)(r * a.v_sS + 8 * cc) * 2u);
         }
     };
+
+    // per-lane LDS offsets of the MFMA operand reads
+    const int krow0 = l32, krow1 = 32 + l32;
+    // V transposed reads: group gi = lane/16 covers d 16 (gi & 1) of a 32-row
+    // d tile and kv rows 4 hh + (i >> 2) (+8 for the second read), i = lane & 15
+    const int vi = lane & 15;
+    const int vrow = 4 * hh + (vi >> 2);
+    const int vswz = 2 * (vi >> 2);        // = 2 * (vrow & 3)
+    const int vcol_lo = 2 * ((lane >> 4) & 1) + ((vi & 3) >> 1);
+    const int vsub = 4 * (vi & 1);
 
     f32x16 acc[NO];
 #pragma unroll
@@ -273,107 +320,143 @@ __global__ __launch_bounds__(256, 2) void attn_fwd(AttnArgs a)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[o][r] = 0.f;
     float m = -INFINITY, l = 0.f;
+    const float lazy_raw = kLazy / c;
 
-    if (ntiles > 0) load_tile(tile_c0(0));
+    if (ntiles > 0) load_tile(tile_c0(0), 0);
     for (int it = 0; it < ntiles; ++it) {
         const int buf = it & 1;
-        store_tile(buf);
-        __syncthreads();
-        const int64_t c0 = tile_c0(it);
-        if (it + 1 < ntiles) load_tile(tile_c0(it + 1));
+        __builtin_amdgcn_s_waitcnt(0);     // this wave's loads of tile `it` landed
+        __syncthreads();                   // everyone's did; buffer buf^1 is free
+        const int c0 = tile_c0(it);
+        if (it + 1 < ntiles) load_tile(tile_c0(it + 1), buf ^ 1);
 
         // Which part of this tile the wave's rows may see.
         bool skip = wend <= wr0 || c0 >= Lkv;
         bool full = !skip && (c0 + BN <= Lkv) && (wend - wr0 == 32);
         if (!BSA && !skip) {
-            const int64_t r0 = wr0, r1 = wend - 1, cl = c0 + BN - 1;
+            const int r0 = wr0, r1 = wend - 1, cl = c0 + BN - 1;
             switch (mode) {
             case 0:
                 if (mbase) {
                     full = false;
-                    skip = cl < r0 - a.pre || c0 > r1 + a.next;
+                    skip = cl < r0 - pre || c0 > r1 + next;
                 }
                 break;
             case 1: full = false; break;
             case 2: skip = c0 > r1; full = full && cl <= r0; break;
             case 3: skip = c0 > r1 + delta; full = full && cl <= r0 + delta; break;
             case 4:
-                skip = cl < r0 + delta - a.pre || c0 > r1 + delta + a.next;
-                full = full && c0 >= r1 + delta - a.pre && cl <= r0 + delta + a.next;
+                skip = cl < r0 + delta - pre || c0 > r1 + delta + next;
+                full = full && c0 >= r1 + delta - pre && cl <= r0 + delta + next;
                 break;
             default: break;
             }
         }
-        if (!skip) {
-            const uint16_t* ks = smem + buf * STAGE;
-            const uint16_t* vs = ks + KT;
-            f32x16 s0, s1;
+        if (skip) continue;
+
+        const uint16_t* ks = smem + buf * STAGE;
+        const uint16_t* vs = ks + KT;
+        f32x16 s0, s1;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) s0[r] = s1[r] = 0.f;
+        for (int r = 0; r < 16; ++r) s0[r] = s1[r] = 0.f;
 #pragma unroll
-            for (int s = 0; s < NQ; ++s) {
-                const uint4 ka0 = *(const uint4*)(ks + l32 * KP + 16 * s + 8 * hh);
-                const uint4 ka1 = *(const uint4*)(ks + (32 + l32) * KP + 16 * s + 8 * hh);
-                s0 = O::mma32(ka0, qf[s], s0);
-                s1 = O::mma32(ka1, qf[s], s1);
-            }
-            float x[32];
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                x[r] = s0[r] * a.scale_log2;
-                x[16 + r] = s1[r] * a.scale_log2;
-            }
-            if (!full) {
-                const uint8_t* mrow = mbase ? mbase + (int64_t)row * a.mask_rstride : nullptr;
-#pragma unroll
-                for (int r = 0; r < 32; ++r) {
-                    const int rr = r & 15;
-                    const int64_t j = c0 + 32 * (r >> 4) + 8 * (rr >> 2) + 4 * hh + (rr & 3);
-                    bool ok = row < qend && j < Lkv;
-                    if (!BSA && ok) ok = allowed(a, mode, row, j, delta, mrow);
-                    if (!ok) x[r] = -INFINITY;
+        for (int s = 0; s < NQ; ++s) {
+            const int ch = 2 * s + hh;
+            const uint4 ka0 = *(const uint4*)(ks + krow0 * DQK + 8 * (ch ^ (krow0 & 7)));
+            const uint4 ka1 = *(const uint4*)(ks + krow1 * DQK + 8 * (ch ^ (krow1 & 7)));
+            s0 = O::mma32(ka0, qf[s], s0);
+            s1 = O::mma32(ka1, qf[s], s1);
+        }
+
+        // element mask (boundary tiles only): accumulator r holds kv index
+        // c0 + 4 hh + kofs(r), kofs(r) = 32 (r/16) + 8 ((r%16)/4) + r%4; the
+        // row's allowed keys are [jlo, jhi] relative to c0 + 4 hh, plus the
+        // explicit mask in modes 0/1.
+        if (!full) {
+            const int base = c0 + 4 * hh;
+            int jlo = -base, jhi = Lkv - 1 - base;
+            if (row >= qend) jhi = -1;
+            if (!BSA) {
+                if (mode == 2) jhi = min(jhi, row - base);
+                else if (mode == 3) jhi = min(jhi, row + delta - base);
+                else if (mode == 4) {
+                    jlo = max(jlo, row + delta - pre - base);
+                    jhi = min(jhi, row + delta + next - base);
+                } else if (mode == 0 && mbase) {
+                    jlo = max(jlo, row - pre - base);
+                    jhi = min(jhi, row + next - base);
                 }
             }
-            float mt = x[0];
+            const uint8_t* mrow =
+                (!BSA && mbase && row < qend) ? mbase + (int64_t)row * a.mask_rstride + base : nullptr;
 #pragma unroll
-            for (int r = 1; r < 32; ++r) mt = fmaxf(mt, x[r]);
-            mt = fmaxf(mt, __shfl_xor(mt, 32));
-            const float mn = fmaxf(m, mt);
-            const float mu = mn == -INFINITY ? 0.f : mn;
-            const float alpha = fast_exp2(m - mu);
-            float ps = 0.f;
-#pragma unroll
-            for (int r = 0; r < 32; ++r) {
-                x[r] = fast_exp2(x[r] - mu);
-                ps += x[r];
+            for (int r = 0; r < 16; ++r) {
+                const int k0 = 8 * (r >> 2) + (r & 3), k1 = 32 + k0;
+                bool ok0 = k0 >= jlo && k0 <= jhi, ok1 = k1 >= jlo && k1 <= jhi;
+                if (mrow) {
+                    ok0 = ok0 && mrow[k0] == 0;
+                    ok1 = ok1 && mrow[k1] == 0;
+                }
+                s0[r] = ok0 ? s0[r] : -INFINITY;
+                s1[r] = ok1 ? s1[r] : -INFINITY;
             }
-            l = l * alpha + ps;
+        }
+
+        // row max over the tile (raw score units; c > 0)
+        float mt = fmaxf(s0[0], s1[0]);
+#pragma unroll
+        for (int r = 1; r < 16; ++r) mt = fmaxf(mt, fmaxf(s0[r], s1[r]));
+        mt = other_half_max(mt);
+        const float mn = fmaxf(m, mt);
+        const bool grow = (m == -INFINITY) ? (mn > -INFINITY) : (mn > m + lazy_raw);
+        if (__ballot(grow)) {
+            // adopt the new max in every row of the wave; rescale O and l
+            float alpha = 1.f;
+            if (m == -INFINITY) alpha = 0.f;
+            else if (mn != -INFINITY) alpha = fast_exp2((m - mn) * c);
             m = mn;
+            l *= alpha;
 #pragma unroll
             for (int o = 0; o < NO; ++o)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) acc[o][r] *= alpha;
-            uint4 pb[4];
+        }
+        const float mc = (m == -INFINITY) ? 0.f : m * c;
+        float ps = 0.f;
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                pb[k].x = O::pack2(x[8 * k + 0], x[8 * k + 1]);
-                pb[k].y = O::pack2(x[8 * k + 2], x[8 * k + 3]);
-                pb[k].z = O::pack2(x[8 * k + 4], x[8 * k + 5]);
-                pb[k].w = O::pack2(x[8 * k + 6], x[8 * k + 7]);
+        for (int r = 0; r < 16; ++r) {
+            s0[r] = fast_exp2(__builtin_fmaf(s0[r], c, -mc));
+            s1[r] = fast_exp2(__builtin_fmaf(s1[r], c, -mc));
+            ps += s0[r] + s1[r];
+        }
+        l += ps;
+
+        // P^T as the B operand: k-step k holds accumulators 8k..8k+7 of the
+        // 32 (s0 then s1); the matching V rows come from two transposed reads.
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const f32x16& src = (k < 2) ? s0 : s1;
+            const int b8 = 8 * (k & 1);
+            uint4 pb;
+            pb.x = O::pack2(src[b8 + 0], src[b8 + 1]);
+            pb.y = O::pack2(src[b8 + 2], src[b8 + 3]);
+            pb.z = O::pack2(src[b8 + 4], src[b8 + 5]);
+            pb.w = O::pack2(src[b8 + 6], src[b8 + 7]);
+            const uint16_t* vk = vs + (16 * k + vrow) * DV + vsub;
+#pragma unroll
+            for (int o = 0; o < NO; ++o) {
+                const int pc = (4 * o + vcol_lo) ^ vswz;
+                const uint2 lo = lds_read_tr16(vk + 8 * pc);
+                const uint2 hi = lds_read_tr16(vk + 8 * DV + 8 * pc);
+                const uint4 va = make_uint4(lo.x, lo.y, hi.x, hi.y);
+                acc[o] = O::mma32(va, pb, acc[o]);
             }
-#pragma unroll
-            for (int o = 0; o < NO; ++o)
-#pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    const uint4 va = *(const uint4*)(vs + (32 * o + l32) * VP + 16 * k + 8 * hh);
-                    acc[o] = O::mma32(va, pb[k], acc[o]);
-                }
         }
     }
 
     // epilogue: rows < q1 are written; rows in [qend, q1) and rows with no
     // allowed key get out = 0 and lse = +inf.
-    const float lt = l + __shfl_xor(l, 32);
+    const float lt = other_half_sum(l);
     if (row < q1) {
         const bool valid = row < qend && lt > 0.f;
         const float inv = valid ? 1.f / lt : 0.f;
@@ -391,7 +474,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd(AttnArgs a)
         if (a.return_lse && hh == 0) {
             float* lp = a.lse + bi.q_row0 * a.lse_rowmul + (int64_t)h * a.lse_sH +
                         (int64_t)row * a.lse_sS;
-            *lp = valid ? (m + __log2f(lt)) * kLn2 : INFINITY;
+            *lp = valid ? (m * c + __log2f(lt)) * kLn2 : INFINITY;
         }
     }
 }
@@ -651,7 +734,7 @@ __global__ __launch_bounds__(256) void bsa_compact(const uint8_t* mask, const Ba
 template <int DT, int DQK, int DV, bool BSA>
 int launch_attn(const fia_plan& p, const AttnArgs& a, hipStream_t stream)
 {
-    constexpr int STAGE = kBlockN * (DQK + 8) + DV * (kBlockN + 8);
+    constexpr int STAGE = kBlockN * DQK + kBlockN * DV;
     const size_t lds = 2 * STAGE * sizeof(uint16_t);
     static bool configured = false;
     if (!configured) {

@@ -353,8 +353,9 @@ fia_status fia_get_workspace_size(const fia_tensor* query, const fia_tensor* key
             return st;
     }
     p->B = B;
-    for (int64_t b = 0; b < B; ++b)
-        if (lq[(size_t)b] > INT32_MAX || lkv[(size_t)b] > INT32_MAX) return FIA_ERR_UNSUPPORTED;
+    // sequence axes up to 2^29 rows (the pages' limit is 20M); kernels index
+    // rows in int32
+    if (gq.S >= ((int64_t)1 << 29) || Skv >= ((int64_t)1 << 29)) return FIA_ERR_UNSUPPORTED;
 
     int64_t max_blocks = 0;
     if (paged) {
@@ -519,9 +520,13 @@ fia_status fia_get_workspace_size(const fia_tensor* query, const fia_tensor* key
     a.has_mask = mask != nullptr;
     a.mode = mode;
     // Modes 1, 2 and 3 ignore pre/next; mode 0 without a mask ignores them
-    // (sparse_mode parameter description).
+    // (sparse_mode parameter description).  With S < 2^29 a band bound past
+    // +-2^30 is the same as an infinite one, so the kernel works in int32.
+    const int64_t band_lim = (int64_t)1 << 30;
     a.pre = (mode == 4 || (mode == 0 && mask)) ? prm->pre_tokens : kIntMax;
     a.next = (mode == 4 || (mode == 0 && mask)) ? prm->next_tokens : kIntMax;
+    a.pre = std::max(-band_lim, std::min(band_lim, a.pre));
+    a.next = std::max(-band_lim, std::min(band_lim, a.next));
     a.QN = (int32_t)QN;
     a.KVN = (int32_t)KVN;
     a.G = (int32_t)(QN / KVN);
