@@ -185,13 +185,14 @@ template <int DT, int DQK, int DV, bool BSA>
 __global__ __launch_bounds__(256, 2) void attn_fwd(AttnArgs a)
 {
     constexpr int BN = kBlockN;            // 64 kv tokens per tile
-    constexpr int KCH = DQK / 8;           // 16-byte chunks per K row
     constexpr int VCH = DV / 8;            // 16-byte chunks per V row
+    constexpr int VSW = VCH >= 16 ? 4 : 2; // V chunk swizzle step
+    constexpr bool KROWS = DQK == 128;     // K layout: swizzled rows or panels
     constexpr int KT = BN * DQK;           // K tile elements (rows not padded)
     constexpr int STAGE = KT + BN * DV;
     constexpr int NQ = DQK / 16;           // k-steps of S^T = K Q^T
     constexpr int NO = DV / 32;            // 32-row d tiles of O^T
-    constexpr int NKI = BN * KCH / 256;    // K load instructions per wave per tile
+    constexpr int NKI = BN * DQK / 8 / 256; // K load instructions per wave per tile
     constexpr int NVI = BN * VCH / 256;    // V load instructions per wave per tile
     using O = Ops<DT>;
 
@@ -277,10 +278,15 @@ __global__ __launch_bounds__(256, 2) void attn_fwd(AttnArgs a)
         return kv_lo + BN * it;
     };
 
-    // Direct-to-LDS loads.  Tiles are row-major without padding; 16-byte
-    // chunk c of K row r sits at chunk c ^ (r & 7), of V row r at
-    // c ^ 2 (r & 3), which spreads the MFMA operand reads over all banks.
-    // Instruction u of wave w fills LDS slots 64 (4u + w) + lane.
+    // Direct-to-LDS loads; instruction u of wave w fills 16-byte slots
+    // 64 (4u + w) + lane of the tile.  LDS layouts (64 banks of 4 bytes):
+    //   K, D_qk = 128: row-major 256-byte rows; chunk c of row r sits at
+    //      c ^ (r & 15).  Other D_qk: column panels of 64 rows x 64 d
+    //      (128-byte rows); chunk c of row r sits at c ^ ((r >> 1) & 7).
+    //      Either way each 16-row group of the MFMA operand reads hits 16
+    //      distinct 16-byte bank groups.
+    //   V: row-major rows of DV; chunk c of row r sits at c ^ VSW (r & 3): the
+    //      4-row groups of the transposed reads hit distinct bank groups.
     auto load_tile = [&](int c0, int buf) {
         uint16_t* ks = smem + buf * STAGE;
         uint16_t* vs = ks + KT;
@@ -290,27 +296,36 @@ __global__ __launch_bounds__(256, 2) void attn_fwd(AttnArgs a)
         for (int u = 0; u < NKI; ++u) {
             const int blk = 4 * u + w;
             const int sl = 64 * blk + lane;
-            const int r = sl / KCH, pc = sl % KCH;
-            const int cc = pc ^ (r & 7);
-            dma16(kr, ks + blk * 512, (uint32_t)(r * a.k_sS + 8 * cc) * 2u);
+            int r, col;
+            if (KROWS) {
+                r = sl >> 4;
+                col = 8 * ((sl & 15) ^ (r & 15));
+            } else {
+                const int pnl = sl >> 9;
+                r = (sl >> 3) & 63;
+                col = 64 * pnl + 8 * ((sl & 7) ^ ((r >> 1) & 7));
+            }
+            dma16(kr, ks + blk * 512, (uint32_t)(r * a.k_sS + col) * 2u);
         }
 #pragma unroll
         for (int u = 0; u < NVI; ++u) {
             const int blk = 4 * u + w;
             const int sl = 64 * blk + lane;
             const int r = sl / VCH, pc = sl % VCH;
-            const int cc = pc ^ (2 * (r & 3));
+            const int cc = pc ^ (VSW * (r & 3));
             dma16(vr, vs + blk * 512, (uint32_t)(r * a.v_sS + 8 * cc) * 2u);
         }
     };
 
     // per-lane LDS offsets of the MFMA operand reads
     const int krow0 = l32, krow1 = 32 + l32;
+    const int kx0 = KROWS ? (krow0 & 15) : ((krow0 >> 1) & 7);
+    const int kx1 = KROWS ? (krow1 & 15) : ((krow1 >> 1) & 7);
     // V transposed reads: group gi = lane/16 covers d 16 (gi & 1) of a 32-row
     // d tile and kv rows 4 hh + (i >> 2) (+8 for the second read), i = lane & 15
     const int vi = lane & 15;
     const int vrow = 4 * hh + (vi >> 2);
-    const int vswz = 2 * (vi >> 2);        // = 2 * (vrow & 3)
+    const int vswz = VSW * (vi >> 2);      // = VSW * (vrow & 3)
     const int vcol_lo = 2 * ((lane >> 4) & 1) + ((vi & 3) >> 1);
     const int vsub = 4 * (vi & 1);
 
@@ -361,9 +376,17 @@ __global__ __launch_bounds__(256, 2) void attn_fwd(AttnArgs a)
         for (int r = 0; r < 16; ++r) s0[r] = s1[r] = 0.f;
 #pragma unroll
         for (int s = 0; s < NQ; ++s) {
-            const int ch = 2 * s + hh;
-            const uint4 ka0 = *(const uint4*)(ks + krow0 * DQK + 8 * (ch ^ (krow0 & 7)));
-            const uint4 ka1 = *(const uint4*)(ks + krow1 * DQK + 8 * (ch ^ (krow1 & 7)));
+            uint4 ka0, ka1;
+            if (KROWS) {
+                const int ch = 2 * s + hh;
+                ka0 = *(const uint4*)(ks + krow0 * DQK + 8 * (ch ^ kx0));
+                ka1 = *(const uint4*)(ks + krow1 * DQK + 8 * (ch ^ kx1));
+            } else {
+                const int ch = 2 * (s & 3) + hh;
+                const uint16_t* pn = ks + (s >> 2) * (BN * 64);
+                ka0 = *(const uint4*)(pn + krow0 * 64 + 8 * (ch ^ kx0));
+                ka1 = *(const uint4*)(pn + krow1 * 64 + 8 * (ch ^ kx1));
+            }
             s0 = O::mma32(ka0, qf[s], s0);
             s1 = O::mma32(ka1, qf[s], s1);
         }

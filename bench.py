@@ -96,8 +96,14 @@ def time_plan(plan, steps: int, warmup: int):
     """Warm up, then time `steps` runs: wall clock between synchronizations
     and HIP events on the stream the kernels are launched on."""
     import torch
-    for _ in range(warmup):
+    # warm-up: at least `warmup` runs and at least 0.5 s, so clocks settle
+    t_end = time.perf_counter() + 0.5
+    n = 0
+    while n < warmup or time.perf_counter() < t_end:
         plan.run()
+        n += 1
+        if n % 8 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -199,6 +205,9 @@ def main():
     ap.add_argument("--secondary", default="c1,c3,c4,c5",
                     help="comma list of other workloads to time ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run 3 plain device copies of MIB MiB (scales the "
+                         "FETCH_SIZE / WRITE_SIZE counters to bytes) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this build runs on a single MI355X "
@@ -206,6 +215,15 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.calibrate_copy:
+        n = args.calibrate_copy << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": n}))
+        return
     from attention_fia_fwd_amd import _abi
     if not os.path.exists(_abi.LIB_PATH):
         from attention_fia_fwd_amd.build import build
