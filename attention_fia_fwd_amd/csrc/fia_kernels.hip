@@ -83,36 +83,7 @@ struct Ops<FIA_F16> {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-__device__ __forceinline__ uint32_t sel_lo(uint32_t a, uint32_t b)
-{
-    // {a.lo16, b.lo16}
-    return __builtin_amdgcn_perm(b, a, 0x05040100u);
-}
-__device__ __forceinline__ uint32_t sel_hi(uint32_t a, uint32_t b)
-{
-    // {a.hi16, b.hi16}
-    return __builtin_amdgcn_perm(b, a, 0x07060302u);
-}
 
-__device__ __forceinline__ uint32_t dw(const uint4& v, int i)
-{
-    return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w));
-}
-
-// Position of kv token t inside a transposed V tile row.  Within each group
-// of 16 tokens, bits 2 and 3 of the index are swapped, so that the 8 tokens
-// one MFMA lane needs for P V are contiguous (16-byte LDS read).
-__device__ __forceinline__ int vpos16(int t)
-{
-    return (t & ~15) | (((t >> 2) & 1) << 3) | (((t >> 3) & 1) << 2) | (t & 3);
-}
-
-// Position of token t (0..31) in a decode V tile row: tokens 16a + 4c + r
-// go to 8c + 4a + r.
-__device__ __forceinline__ int vpos32(int t)
-{
-    return (((t >> 2) & 3) << 3) | (((t >> 4) & 1) << 2) | (t & 3);
-}
 
 // ---------------------------------------------------------------------------
 // Prefill / block-sparse attention.
@@ -504,17 +475,49 @@ __global__ __launch_bounds__(256, 2) void attn_fwd(AttnArgs a)
 
 // ---------------------------------------------------------------------------
 // Decode: split-KV attention over (optionally paged) K/V.
+//
+// One wave per work item (batch b, kv head, chunk of <= 16 query heads of
+// its GQA group, kv split).  Per step of 32 tokens (two 16-token sub-tiles;
+// a sub-tile never crosses a page because block_size % 16 == 0):
+//   S^T (32 tokens x 16 heads) = K Q^T on v_mfma_f32_16x16x32: K comes
+//       straight from HBM into the A operand (each lane one token row, four
+//       16-byte chunks), the query heads are the 16 B-operand columns, so a
+//       K/V byte is read once for the whole GQA group;
+//   V rows stream direct-to-LDS and feed O^T += V^T P^T through transposed
+//       LDS reads; P stays in registers.
+// Page / offset of each sub-tile are tracked as wave-uniform scalars, so the
+// per-lane address work is one multiply-add per sub-tile.  The next step's
+// K registers and V rows are in flight while the current step computes.
 // ---------------------------------------------------------------------------
+__device__ __forceinline__ float quad_max(float x)
+{
+    // max over lanes l, l^16, l^32, l^48 (the four quarters of the wave)
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    return other_half_max(x);
+}
+__device__ __forceinline__ float quad_sum(float x)
+{
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    return other_half_sum(x);
+}
+
+// waitcnt immediates (gfx9 encoding): vmcnt(n) alone, lgkmcnt(0) alone
+#define FIA_VMCNT(n) (((n) & 15) | (((n) >> 4) << 14) | 0x70 | 0xF00)
+#define FIA_LGKMCNT0 0xC07F
+
 template <int DT, int D>
 __global__ __launch_bounds__(64) void decode_split(DecodeArgs a)
 {
     constexpr int ST = kDecodeStep;       // 32 tokens per step
-    constexpr int VP = ST + 8;            // transposed V row pitch (elements)
     constexpr int NK = D / 32;            // k-steps of S^T = K Q^T
     constexpr int NO = D / 16;            // 16-row d tiles of O^T
-    constexpr int NVU = D / 64;           // V staging units per lane (4 tokens x 8 d)
+    constexpr int VCH = D / 8;            // 16-byte chunks per V row
+    constexpr int RPI = 64 / VCH;         // V rows per DMA instruction
+    constexpr int NVI = 16 / RPI;         // DMA instructions per sub-tile
     using O = Ops<DT>;
-    __shared__ __attribute__((aligned(16))) uint16_t vt[2][D * VP];
+    __shared__ __attribute__((aligned(16))) uint16_t vbuf[2][ST * D];
 
     const int lane = threadIdx.x;
     const int n = lane & 15, qd = lane >> 4;
@@ -537,99 +540,118 @@ __global__ __launch_bounds__(64) void decode_split(DecodeArgs a)
     const int t1 = min(t0 + a.chunk, db.lkv);
     const int nh = min(kDecodeHeads, a.G - kDecodeHeads * hc);
     const int hq = kvh * a.G + kDecodeHeads * hc + n;
+    const float c = fmaxf(fabsf(a.scale_log2), kMinScale);
+    const uint32_t qflip = a.scale_log2 < 0.f ? 0x80008000u : 0u;
 
     // Q^T as the B operand: column n = head hq, d = 32s + 8qd.
     uint4 qf[NK];
     if (n < nh) {
         const uint16_t* src = (const uint16_t*)a.q + ((int64_t)b * a.QN + hq) * D + 8 * qd;
 #pragma unroll
-        for (int s = 0; s < NK; ++s) qf[s] = *(const uint4*)(src + 32 * s);
+        for (int s = 0; s < NK; ++s) {
+            uint4 v = *(const uint4*)(src + 32 * s);
+            v.x ^= qflip; v.y ^= qflip; v.z ^= qflip; v.w ^= qflip;
+            qf[s] = v;
+        }
     } else {
 #pragma unroll
         for (int s = 0; s < NK; ++s) qf[s] = make_uint4(0, 0, 0, 0);
     }
 
+    // Sub-tile addressing: the page (block) and the token offset inside it.
+    const int bs = a.paged ? a.block_size : 0x40000000;
+    const int32_t* bt = a.paged ? a.block_table + (int64_t)b * a.bt_stride : nullptr;
+    const int64_t tokstride = a.paged ? a.p_tok : a.c_tok;
     const uint16_t* kbase = (const uint16_t*)a.k;
     const uint16_t* vbase = (const uint16_t*)a.v;
-    const int32_t* bt = a.paged ? a.block_table + (int64_t)b * a.bt_stride : nullptr;
-    auto tok_off = [&](int tk) -> int64_t {
-        if (a.paged) {
-            const int64_t blk = bt[tk / a.block_size];
-            return blk * a.p_blk + (int64_t)kvh * a.p_head + (int64_t)(tk % a.block_size) * a.p_tok;
-        }
-        return db.kv_row0 * a.c_rowmul + (int64_t)kvh * a.c_head + (int64_t)tk * a.c_tok;
+    const int64_t hoff = a.paged ? (int64_t)kvh * a.p_head
+                                 : db.kv_row0 * a.c_rowmul + (int64_t)kvh * a.c_head;
+    auto sub_rsrc = [&](const uint16_t* base, int pg, int off, int tb) {
+        // rows [off, off + nvalid) of page pg; rows past t1 read as zero
+        const int nvalid = min(16, t1 - tb);
+        // a sub-tile past the end reads nothing, not even its table entry
+        const int64_t pbase = (a.paged && nvalid > 0) ? (int64_t)bt[pg] * a.p_blk : 0;
+        const int64_t bytes = nvalid > 0 ? ((int64_t)(nvalid - 1) * tokstride + D) * 2 : 0;
+        return __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(base + pbase + hoff + (int64_t)off * tokstride), (short)0,
+            (int)min(bytes, (int64_t)0x7fffffff), 0x00020000);
     };
 
-    uint4 kf[2][NK];
-    uint4 vst[NVU][4];
-    auto load_step = [&](int tt0) {
+    // K rows into registers: lane (token n, quarter qd) reads d = 32s + 8qd.
+    const uint32_t k_voff = (uint32_t)((n * tokstride + 8 * qd) * 2);
+    // V rows via DMA: instruction u of sub-tile c fills rows 16c + RPI u + lane / VCH.
+    const int vr_in = lane / VCH, vpc = lane % VCH;
+    auto vswz = [](int r) { return VCH >= 16 ? 2 * (r & 7) : 2 * ((r >> 1) & 3); };
+
+    auto issue = [&](int tt0, int pg0, int off0, int pg1, int off1, uint4 (&kf)[2][NK], int buf) {
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
-            const int tk = tt0 + 16 * c + n;
-            if (tk < t1) {
-                const uint16_t* src = kbase + tok_off(tk) + 8 * qd;
+        for (int cc = 0; cc < 2; ++cc) {
+            const int pg = cc ? pg1 : pg0, off = cc ? off1 : off0, tb = tt0 + 16 * cc;
+            const __amdgpu_buffer_rsrc_t kr = sub_rsrc(kbase, pg, off, tb);
 #pragma unroll
-                for (int s = 0; s < NK; ++s) kf[c][s] = *(const uint4*)(src + 32 * s);
-            } else {
+            for (int s = 0; s < NK; ++s)
+                kf[cc][s] = __builtin_bit_cast(
+                    uint4, __builtin_amdgcn_raw_buffer_load_b128(kr, k_voff + 64 * s, 0, 0));
+            const __amdgpu_buffer_rsrc_t vr = sub_rsrc(vbase, pg, off, tb);
 #pragma unroll
-                for (int s = 0; s < NK; ++s) kf[c][s] = make_uint4(0, 0, 0, 0);
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < NVU; ++u) {
-            const int unit = lane + 64 * u;
-            const int tok4 = unit & 7, dc = unit >> 3;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int tk = tt0 + 4 * tok4 + r;
-                vst[u][r] = tk < t1 ? *(const uint4*)(vbase + tok_off(tk) + 8 * dc)
-                                    : make_uint4(0, 0, 0, 0);
-            }
-        }
-    };
-    auto store_v = [&](int buf) {
-#pragma unroll
-        for (int u = 0; u < NVU; ++u) {
-            const int unit = lane + 64 * u;
-            const int tok4 = unit & 7, dc = unit >> 3;
-            const int pos = vpos32(4 * tok4);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const uint32_t d0 = dw(vst[u][0], e >> 1), d1 = dw(vst[u][1], e >> 1);
-                const uint32_t d2 = dw(vst[u][2], e >> 1), d3 = dw(vst[u][3], e >> 1);
-                uint2 pr;
-                pr.x = (e & 1) ? sel_hi(d0, d1) : sel_lo(d0, d1);
-                pr.y = (e & 1) ? sel_hi(d2, d3) : sel_lo(d2, d3);
-                *(uint2*)(&vt[buf][(8 * dc + e) * VP + pos]) = pr;
+            for (int u = 0; u < NVI; ++u) {
+                const int r = RPI * u + vr_in;                 // row inside the sub-tile
+                const int R = 16 * cc + r;                     // row inside the step
+                const int chunk = vpc ^ vswz(R);
+                dma16(vr, &vbuf[buf][(16 * cc + RPI * u) * D], (uint32_t)((r * tokstride + 8 * chunk) * 2));
             }
         }
     };
+
+    // V^T A operand: lane (d = 16 dt + (lane & 15), quarter qd) needs tokens
+    // 4 qd + 0..3 and 16 + 4 qd + 0..3; each group of 16 lanes reads its 4-row
+    // block with one transposed read (row 4 qd + vi / 4, columns 4 (vi % 4)).
+    const int vi = lane & 15;
+    const int trow = 4 * qd + (vi >> 2);
+    const int tsw = vswz(trow);                          // same for trow + 16
+    const int tcol_lo = (vi & 3) >> 1, tsub = 4 * (vi & 1);
 
     f32x4 acc[NO];
 #pragma unroll
     for (int o = 0; o < NO; ++o) acc[o] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m = -INFINITY, l = 0.f;
+    const float lazy_raw = kLazy / c;
 
     const int nsteps = (t1 - t0 + ST - 1) / ST;
-    if (nsteps > 0) load_step(t0);
-    for (int st = 0; st < nsteps; ++st) {
-        const int buf = st & 1;
+    int pg = t0 / bs, off = t0 % bs;
+    auto advance16 = [&](int& p, int& o) {
+        o += 16;
+        if (o >= bs) { o -= bs; ++p; }
+    };
+
+    uint4 kfa[2][NK], kfb[2][NK];
+    auto step = [&](int st, uint4 (&kcur)[2][NK], uint4 (&knext)[2][NK]) {
         const int tt0 = t0 + ST * st;
-        store_v(buf);
+        // pg/off point at the first sub-tile of step st + 1 here
+        if (st + 1 < nsteps) {
+            int pg1 = pg, off1 = off;
+            advance16(pg1, off1);
+            __builtin_amdgcn_s_waitcnt(FIA_LGKMCNT0);   // reads of the other V buffer done
+            issue(tt0 + ST, pg, off, pg1, off1, knext, (st + 1) & 1);
+            pg = pg1; off = off1;
+            advance16(pg, off);
+            __builtin_amdgcn_s_waitcnt(FIA_VMCNT(2 * (NK + NVI)));   // step st landed
+        } else {
+            __builtin_amdgcn_s_waitcnt(FIA_VMCNT(0));
+        }
+        __syncthreads();
+
         f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < NK; ++s) {
-            s0 = O::mma16(kf[0][s], qf[s], s0);
-            s1 = O::mma16(kf[1][s], qf[s], s1);
+            s0 = O::mma16(kcur[0][s], qf[s], s0);
+            s1 = O::mma16(kcur[1][s], qf[s], s1);
         }
-        __syncthreads();
-        if (st + 1 < nsteps) load_step(tt0 + ST);
-
         float x[8];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            x[i] = s0[i] * a.scale_log2;
-            x[4 + i] = s1[i] * a.scale_log2;
+            x[i] = s0[i];
+            x[4 + i] = s1[i];
         }
         if (tt0 + ST > t1) {
 #pragma unroll
@@ -641,35 +663,55 @@ __global__ __launch_bounds__(64) void decode_split(DecodeArgs a)
         float mt = x[0];
 #pragma unroll
         for (int r = 1; r < 8; ++r) mt = fmaxf(mt, x[r]);
-        mt = fmaxf(mt, __shfl_xor(mt, 16));
-        mt = fmaxf(mt, __shfl_xor(mt, 32));
+        mt = quad_max(mt);
         const float mn = fmaxf(m, mt);
-        const float mu = mn == -INFINITY ? 0.f : mn;
-        const float alpha = fast_exp2(m - mu);
+        const bool grow = (m == -INFINITY) ? (mn > -INFINITY) : (mn > m + lazy_raw);
+        if (__ballot(grow)) {
+            float alpha = 1.f;
+            if (m == -INFINITY) alpha = 0.f;
+            else if (mn != -INFINITY) alpha = fast_exp2((m - mn) * c);
+            m = mn;
+            l *= alpha;
+#pragma unroll
+            for (int o = 0; o < NO; ++o) acc[o] *= alpha;
+        }
+        const float mc = (m == -INFINITY) ? 0.f : m * c;
         float ps = 0.f;
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
-            x[r] = fast_exp2(x[r] - mu);
+            x[r] = fast_exp2(__builtin_fmaf(x[r], c, -mc));
             ps += x[r];
         }
-        l = l * alpha + ps;
-        m = mn;
+        l += ps;
         uint4 pb;
         pb.x = O::pack2(x[0], x[1]);
         pb.y = O::pack2(x[2], x[3]);
         pb.z = O::pack2(x[4], x[5]);
         pb.w = O::pack2(x[6], x[7]);
+        const uint16_t* vb = vbuf[st & 1];
 #pragma unroll
         for (int o = 0; o < NO; ++o) {
-            acc[o] *= alpha;
-            const uint4 va = *(const uint4*)(&vt[buf][(16 * o + n) * VP + 8 * qd]);
-            acc[o] = O::mma16(va, pb, acc[o]);
+            const int pc = (2 * o + tcol_lo) ^ tsw;
+            const uint2 lo = lds_read_tr16(vb + trow * D + 8 * pc + tsub);
+            const uint2 hi = lds_read_tr16(vb + (trow + 16) * D + 8 * pc + tsub);
+            acc[o] = O::mma16(make_uint4(lo.x, lo.y, hi.x, hi.y), pb, acc[o]);
         }
+    };
+
+    if (nsteps > 0) {
+        int pg1 = pg, off1 = off;
+        advance16(pg1, off1);
+        issue(t0, pg, off, pg1, off1, kfa, 0);
+        pg = pg1; off = off1;
+        advance16(pg, off);
+    }
+    for (int st = 0; st < nsteps; st += 2) {
+        step(st, kfa, kfb);
+        if (st + 1 < nsteps) step(st + 1, kfb, kfa);
     }
 
     // partial: normalised O and natural-log LSE of this split
-    float lt = l + __shfl_xor(l, 16);
-    lt += __shfl_xor(lt, 32);
+    const float lt = quad_sum(l);
     if (n < nh) {
         const float inv = lt > 0.f ? 1.f / lt : 0.f;
         float* po = a.part_o + ((int64_t)item * a.Gc + n) * D;
@@ -679,7 +721,7 @@ __global__ __launch_bounds__(64) void decode_split(DecodeArgs a)
             *(f32x4*)(po + 16 * o + 4 * qd) = v;
         }
         if (qd == 0)
-            a.part_lse[(int64_t)item * a.Gc + n] = lt > 0.f ? (m + __log2f(lt)) * kLn2 : -INFINITY;
+            a.part_lse[(int64_t)item * a.Gc + n] = lt > 0.f ? (m * c + __log2f(lt)) * kLn2 : -INFINITY;
     }
 }
 
