@@ -21,8 +21,10 @@ constexpr int kBlockN = 64;
 constexpr int kDecodeStep = 32;
 // Query heads one decode wave serves (a GQA group is cut into chunks of this).
 constexpr int kDecodeHeads = 16;
-// Compute units of one MI355X, used only to size the decode split plan.
+// Compute units of one MI355X and decode waves resident per CU, used only to
+// size the decode schedule.
 constexpr int kNumCUs = 256;
+constexpr int kDecodeWavesPerCU = 8;
 
 // Per-batch addressing, 24 bytes.  row0 is the first row of batch b on the
 // tensor's row axis: b * S for BNSD/BSND, the cumulative start for TND.
@@ -67,12 +69,21 @@ struct AttnArgs {
     int32_t n_tiles;
 };
 
-// Decode: one wave per work item (batch b, kv head, head chunk, kv split).
-struct DecBatch {
+// Decode schedule.  A segment is (batch b, kv head, chunk of <= 16 query
+// heads of its GQA group) over kv tokens [0, Lkv_b).  The token streams of
+// all segments are concatenated and cut into equal per-wave quotas; a piece
+// is the part of one segment that one wave processes.
+struct DecSeg {
     int64_t kv_row0;     // contiguous KV: first row of batch b
+    int32_t b;
     int32_t lkv;
-    int32_t item0;       // first work item of batch b
-    int32_t nsplit;      // kv splits of batch b
+    int32_t first;       // first piece of this segment
+    int32_t count;       // pieces of this segment (0 when lkv == 0)
+};
+
+struct DecPiece {
+    int32_t seg;         // (b * KV_N + kv head) * nhc + head chunk
+    int32_t t0, t1;      // kv tokens [t0, t1), t0 % 16 == 0
     int32_t pad;
 };
 
@@ -90,12 +101,13 @@ struct DecodeArgs {
     int64_t p_blk, p_head, p_tok;
     // contiguous strides (elements): head, token, and row0 multiplier
     int64_t c_head, c_tok, c_rowmul;
-    const DecBatch* batch;         // workspace
-    float* part_o;                 // [n_items, Gc, Dv]
-    float* part_lse;               // [n_items, Gc]
+    const DecSeg* segs;            // plan tables
+    const DecPiece* pieces;
+    const int32_t* wave_first;     // [n_waves + 1]: pieces of wave w
+    float* part_o;                 // [n_pieces, Gc, Dv]
+    float* part_lse;               // [n_pieces, Gc]
     int32_t B, QN, KVN, G, Gc, nhc;
-    int32_t chunk;                 // kv tokens per split
-    int32_t n_items;
+    int32_t n_waves, n_pieces;
     float scale_log2;
     int32_t return_lse;
 };
@@ -116,13 +128,14 @@ struct fia_plan {
     uint64_t workspace_bytes = 0;
 
     // byte offsets inside dev_tables
-    uint64_t off_batch = 0, off_tiles = 0;
+    uint64_t off_batch = 0, off_tiles = 0, off_pieces = 0, off_waves = 0;
     // byte offsets inside the caller's workspace
     uint64_t off_part_o = 0, off_part_lse = 0;
     uint64_t off_cnt = 0, off_idx = 0;
 
     int64_t n_tiles = 0;     // prefill / block-sparse workgroups
-    int64_t n_items = 0;     // decode waves
+    int64_t n_waves = 0;     // decode waves
+    int64_t n_pieces = 0;    // decode pieces (partial results)
     int64_t n_rows = 0;      // block-sparse compaction rows (B * N1 * nqb)
 
     fia::AttnArgs attn{};

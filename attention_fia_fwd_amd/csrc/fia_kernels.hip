@@ -5,11 +5,12 @@
 //                   tokens staged through LDS (double buffered); S^T = K Q^T
 //                   and O^T = V^T P^T on v_mfma_f32_32x32x16_{bf16,f16}; fp32
 //                   online softmax in registers; optional LSE.
-//   decode_split    decode: one wave per (batch, kv head, head chunk, kv
-//                   split); the GQA heads sharing a kv head are the 16
-//                   columns of v_mfma_f32_16x16x32, so every K/V byte is read
-//                   once; pages are gathered through the block table.
-//   decode_combine  merges the splits of one (batch, head) by their LSE.
+//   decode_split    decode: one wave per resident slot, each with an equal
+//                   share of all (batch, kv head, head chunk) token streams;
+//                   the GQA heads sharing a kv head are the 16 columns of
+//                   v_mfma_f32_16x16x32, so every K/V byte is read once;
+//                   pages are gathered through the block table.
+//   decode_combine  merges the pieces of one (batch, head) by their LSE.
 //   bsa_compact     compacts the block-sparse mask into ascending kv-block
 //                   lists per (batch, head, q block).
 //
@@ -476,8 +477,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd(AttnArgs a)
 // ---------------------------------------------------------------------------
 // Decode: split-KV attention over (optionally paged) K/V.
 //
-// One wave per work item (batch b, kv head, chunk of <= 16 query heads of
-// its GQA group, kv split).  Per step of 32 tokens (two 16-token sub-tiles;
+// One wave per resident slot; it walks its pieces, each a token range of one
+// segment (batch b, kv head, chunk of <= 16 query heads of its GQA group),
+// and writes one partial result per piece.  Per step of 32 tokens (two 16-token sub-tiles;
 // a sub-tile never crosses a page because block_size % 16 == 0):
 //   S^T (32 tokens x 16 heads) = K Q^T on v_mfma_f32_16x16x32: K comes
 //       straight from HBM into the A operand (each lane one token row, four
@@ -521,207 +523,202 @@ __global__ __launch_bounds__(64) void decode_split(DecodeArgs a)
 
     const int lane = threadIdx.x;
     const int n = lane & 15, qd = lane >> 4;
-    const int item = blockIdx.x;
+    const int wv = blockIdx.x;
+    const int p_end = a.wave_first[wv + 1];
+    for (int item = a.wave_first[wv]; item < p_end; ++item) {
+        const DecPiece pc_ = a.pieces[item];
+        const DecSeg db = a.segs[pc_.seg];
+        const int b = db.b;
+        const int hc = pc_.seg % a.nhc;
+        const int kvh = (pc_.seg / a.nhc) % a.KVN;
+        const int t0 = pc_.t0;
+        const int t1 = pc_.t1;
+        const int nh = min(kDecodeHeads, a.G - kDecodeHeads * hc);
+        const int hq = kvh * a.G + kDecodeHeads * hc + n;
+        const float c = fmaxf(fabsf(a.scale_log2), kMinScale);
+        const uint32_t qflip = a.scale_log2 < 0.f ? 0x80008000u : 0u;
 
-    // batch of this item: last b with item0 <= item
-    int lo = 0, hi = a.B - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (a.batch[mid].item0 <= item) lo = mid; else hi = mid - 1;
-    }
-    const int b = lo;
-    const DecBatch db = a.batch[b];
-    const int rel = item - db.item0;
-    const int split = rel % db.nsplit;
-    const int rest = rel / db.nsplit;
-    const int hc = rest % a.nhc;
-    const int kvh = rest / a.nhc;
-    const int t0 = split * a.chunk;
-    const int t1 = min(t0 + a.chunk, db.lkv);
-    const int nh = min(kDecodeHeads, a.G - kDecodeHeads * hc);
-    const int hq = kvh * a.G + kDecodeHeads * hc + n;
-    const float c = fmaxf(fabsf(a.scale_log2), kMinScale);
-    const uint32_t qflip = a.scale_log2 < 0.f ? 0x80008000u : 0u;
-
-    // Q^T as the B operand: column n = head hq, d = 32s + 8qd.
-    uint4 qf[NK];
-    if (n < nh) {
-        const uint16_t* src = (const uint16_t*)a.q + ((int64_t)b * a.QN + hq) * D + 8 * qd;
-#pragma unroll
-        for (int s = 0; s < NK; ++s) {
-            uint4 v = *(const uint4*)(src + 32 * s);
-            v.x ^= qflip; v.y ^= qflip; v.z ^= qflip; v.w ^= qflip;
-            qf[s] = v;
-        }
-    } else {
-#pragma unroll
-        for (int s = 0; s < NK; ++s) qf[s] = make_uint4(0, 0, 0, 0);
-    }
-
-    // Sub-tile addressing: the page (block) and the token offset inside it.
-    const int bs = a.paged ? a.block_size : 0x40000000;
-    const int32_t* bt = a.paged ? a.block_table + (int64_t)b * a.bt_stride : nullptr;
-    const int64_t tokstride = a.paged ? a.p_tok : a.c_tok;
-    const uint16_t* kbase = (const uint16_t*)a.k;
-    const uint16_t* vbase = (const uint16_t*)a.v;
-    const int64_t hoff = a.paged ? (int64_t)kvh * a.p_head
-                                 : db.kv_row0 * a.c_rowmul + (int64_t)kvh * a.c_head;
-    auto sub_rsrc = [&](const uint16_t* base, int pg, int off, int tb) {
-        // rows [off, off + nvalid) of page pg; rows past t1 read as zero
-        const int nvalid = min(16, t1 - tb);
-        // a sub-tile past the end reads nothing, not even its table entry
-        const int64_t pbase = (a.paged && nvalid > 0) ? (int64_t)bt[pg] * a.p_blk : 0;
-        const int64_t bytes = nvalid > 0 ? ((int64_t)(nvalid - 1) * tokstride + D) * 2 : 0;
-        return __builtin_amdgcn_make_buffer_rsrc(
-            (void*)(base + pbase + hoff + (int64_t)off * tokstride), (short)0,
-            (int)min(bytes, (int64_t)0x7fffffff), 0x00020000);
-    };
-
-    // K rows into registers: lane (token n, quarter qd) reads d = 32s + 8qd.
-    const uint32_t k_voff = (uint32_t)((n * tokstride + 8 * qd) * 2);
-    // V rows via DMA: instruction u of sub-tile c fills rows 16c + RPI u + lane / VCH.
-    const int vr_in = lane / VCH, vpc = lane % VCH;
-    auto vswz = [](int r) { return VCH >= 16 ? 2 * (r & 7) : 2 * ((r >> 1) & 3); };
-
-    auto issue = [&](int tt0, int pg0, int off0, int pg1, int off1, uint4 (&kf)[2][NK], int buf) {
-#pragma unroll
-        for (int cc = 0; cc < 2; ++cc) {
-            const int pg = cc ? pg1 : pg0, off = cc ? off1 : off0, tb = tt0 + 16 * cc;
-            const __amdgpu_buffer_rsrc_t kr = sub_rsrc(kbase, pg, off, tb);
-#pragma unroll
-            for (int s = 0; s < NK; ++s)
-                kf[cc][s] = __builtin_bit_cast(
-                    uint4, __builtin_amdgcn_raw_buffer_load_b128(kr, k_voff + 64 * s, 0, 0));
-            const __amdgpu_buffer_rsrc_t vr = sub_rsrc(vbase, pg, off, tb);
-#pragma unroll
-            for (int u = 0; u < NVI; ++u) {
-                const int r = RPI * u + vr_in;                 // row inside the sub-tile
-                const int R = 16 * cc + r;                     // row inside the step
-                const int chunk = vpc ^ vswz(R);
-                dma16(vr, &vbuf[buf][(16 * cc + RPI * u) * D], (uint32_t)((r * tokstride + 8 * chunk) * 2));
+        // Q^T as the B operand: column n = head hq, d = 32s + 8qd.
+        uint4 qf[NK];
+        if (n < nh) {
+            const uint16_t* src = (const uint16_t*)a.q + ((int64_t)b * a.QN + hq) * D + 8 * qd;
+    #pragma unroll
+            for (int s = 0; s < NK; ++s) {
+                uint4 v = *(const uint4*)(src + 32 * s);
+                v.x ^= qflip; v.y ^= qflip; v.z ^= qflip; v.w ^= qflip;
+                qf[s] = v;
             }
+        } else {
+    #pragma unroll
+            for (int s = 0; s < NK; ++s) qf[s] = make_uint4(0, 0, 0, 0);
         }
-    };
 
-    // V^T A operand: lane (d = 16 dt + (lane & 15), quarter qd) needs tokens
-    // 4 qd + 0..3 and 16 + 4 qd + 0..3; each group of 16 lanes reads its 4-row
-    // block with one transposed read (row 4 qd + vi / 4, columns 4 (vi % 4)).
-    const int vi = lane & 15;
-    const int trow = 4 * qd + (vi >> 2);
-    const int tsw = vswz(trow);                          // same for trow + 16
-    const int tcol_lo = (vi & 3) >> 1, tsub = 4 * (vi & 1);
+        // Sub-tile addressing: the page (block) and the token offset inside it.
+        const int bs = a.paged ? a.block_size : 0x40000000;
+        const int32_t* bt = a.paged ? a.block_table + (int64_t)b * a.bt_stride : nullptr;
+        const int64_t tokstride = a.paged ? a.p_tok : a.c_tok;
+        const uint16_t* kbase = (const uint16_t*)a.k;
+        const uint16_t* vbase = (const uint16_t*)a.v;
+        const int64_t hoff = a.paged ? (int64_t)kvh * a.p_head
+                                     : db.kv_row0 * a.c_rowmul + (int64_t)kvh * a.c_head;
+        auto sub_rsrc = [&](const uint16_t* base, int pg, int off, int tb) {
+            // rows [off, off + nvalid) of page pg; rows past t1 read as zero
+            const int nvalid = min(16, t1 - tb);
+            // a sub-tile past the end reads nothing, not even its table entry
+            const int64_t pbase = (a.paged && nvalid > 0) ? (int64_t)bt[pg] * a.p_blk : 0;
+            const int64_t bytes = nvalid > 0 ? ((int64_t)(nvalid - 1) * tokstride + D) * 2 : 0;
+            return __builtin_amdgcn_make_buffer_rsrc(
+                (void*)(base + pbase + hoff + (int64_t)off * tokstride), (short)0,
+                (int)min(bytes, (int64_t)0x7fffffff), 0x00020000);
+        };
 
-    f32x4 acc[NO];
-#pragma unroll
-    for (int o = 0; o < NO; ++o) acc[o] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m = -INFINITY, l = 0.f;
-    const float lazy_raw = kLazy / c;
+        // K rows into registers: lane (token n, quarter qd) reads d = 32s + 8qd.
+        const uint32_t k_voff = (uint32_t)((n * tokstride + 8 * qd) * 2);
+        // V rows via DMA: instruction u of sub-tile c fills rows 16c + RPI u + lane / VCH.
+        const int vr_in = lane / VCH, vpc = lane % VCH;
+        auto vswz = [](int r) { return VCH >= 16 ? 2 * (r & 7) : 2 * ((r >> 1) & 3); };
 
-    const int nsteps = (t1 - t0 + ST - 1) / ST;
-    int pg = t0 / bs, off = t0 % bs;
-    auto advance16 = [&](int& p, int& o) {
-        o += 16;
-        if (o >= bs) { o -= bs; ++p; }
-    };
+        auto issue = [&](int tt0, int pg0, int off0, int pg1, int off1, uint4 (&kf)[2][NK], int buf) {
+    #pragma unroll
+            for (int cc = 0; cc < 2; ++cc) {
+                const int pg = cc ? pg1 : pg0, off = cc ? off1 : off0, tb = tt0 + 16 * cc;
+                const __amdgpu_buffer_rsrc_t kr = sub_rsrc(kbase, pg, off, tb);
+    #pragma unroll
+                for (int s = 0; s < NK; ++s)
+                    kf[cc][s] = __builtin_bit_cast(
+                        uint4, __builtin_amdgcn_raw_buffer_load_b128(kr, k_voff + 64 * s, 0, 0));
+                const __amdgpu_buffer_rsrc_t vr = sub_rsrc(vbase, pg, off, tb);
+    #pragma unroll
+                for (int u = 0; u < NVI; ++u) {
+                    const int r = RPI * u + vr_in;                 // row inside the sub-tile
+                    const int R = 16 * cc + r;                     // row inside the step
+                    const int chunk = vpc ^ vswz(R);
+                    dma16(vr, &vbuf[buf][(16 * cc + RPI * u) * D], (uint32_t)((r * tokstride + 8 * chunk) * 2));
+                }
+            }
+        };
 
-    uint4 kfa[2][NK], kfb[2][NK];
-    auto step = [&](int st, uint4 (&kcur)[2][NK], uint4 (&knext)[2][NK]) {
-        const int tt0 = t0 + ST * st;
-        // pg/off point at the first sub-tile of step st + 1 here
-        if (st + 1 < nsteps) {
+        // V^T A operand: lane (d = 16 dt + (lane & 15), quarter qd) needs tokens
+        // 4 qd + 0..3 and 16 + 4 qd + 0..3; each group of 16 lanes reads its 4-row
+        // block with one transposed read (row 4 qd + vi / 4, columns 4 (vi % 4)).
+        const int vi = lane & 15;
+        const int trow = 4 * qd + (vi >> 2);
+        const int tsw = vswz(trow);                          // same for trow + 16
+        const int tcol_lo = (vi & 3) >> 1, tsub = 4 * (vi & 1);
+
+        f32x4 acc[NO];
+    #pragma unroll
+        for (int o = 0; o < NO; ++o) acc[o] = f32x4{0.f, 0.f, 0.f, 0.f};
+        float m = -INFINITY, l = 0.f;
+        const float lazy_raw = kLazy / c;
+
+        const int nsteps = (t1 - t0 + ST - 1) / ST;
+        int pg = t0 / bs, off = t0 % bs;
+        auto advance16 = [&](int& p, int& o) {
+            o += 16;
+            if (o >= bs) { o -= bs; ++p; }
+        };
+
+        uint4 kfa[2][NK], kfb[2][NK];
+        auto step = [&](int st, uint4 (&kcur)[2][NK], uint4 (&knext)[2][NK]) {
+            const int tt0 = t0 + ST * st;
+            // pg/off point at the first sub-tile of step st + 1 here
+            if (st + 1 < nsteps) {
+                int pg1 = pg, off1 = off;
+                advance16(pg1, off1);
+                __builtin_amdgcn_s_waitcnt(FIA_LGKMCNT0);   // reads of the other V buffer done
+                issue(tt0 + ST, pg, off, pg1, off1, knext, (st + 1) & 1);
+                pg = pg1; off = off1;
+                advance16(pg, off);
+                __builtin_amdgcn_s_waitcnt(FIA_VMCNT(2 * (NK + NVI)));   // step st landed
+            } else {
+                __builtin_amdgcn_s_waitcnt(FIA_VMCNT(0));
+            }
+            __syncthreads();
+
+            f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+    #pragma unroll
+            for (int s = 0; s < NK; ++s) {
+                s0 = O::mma16(kcur[0][s], qf[s], s0);
+                s1 = O::mma16(kcur[1][s], qf[s], s1);
+            }
+            float x[8];
+    #pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                x[i] = s0[i];
+                x[4 + i] = s1[i];
+            }
+            if (tt0 + ST > t1) {
+    #pragma unroll
+                for (int r = 0; r < 8; ++r) {
+                    const int tk = tt0 + 16 * (r >> 2) + 4 * qd + (r & 3);
+                    if (tk >= t1) x[r] = -INFINITY;
+                }
+            }
+            float mt = x[0];
+    #pragma unroll
+            for (int r = 1; r < 8; ++r) mt = fmaxf(mt, x[r]);
+            mt = quad_max(mt);
+            const float mn = fmaxf(m, mt);
+            const bool grow = (m == -INFINITY) ? (mn > -INFINITY) : (mn > m + lazy_raw);
+            if (__ballot(grow)) {
+                float alpha = 1.f;
+                if (m == -INFINITY) alpha = 0.f;
+                else if (mn != -INFINITY) alpha = fast_exp2((m - mn) * c);
+                m = mn;
+                l *= alpha;
+    #pragma unroll
+                for (int o = 0; o < NO; ++o) acc[o] *= alpha;
+            }
+            const float mc = (m == -INFINITY) ? 0.f : m * c;
+            float ps = 0.f;
+    #pragma unroll
+            for (int r = 0; r < 8; ++r) {
+                x[r] = fast_exp2(__builtin_fmaf(x[r], c, -mc));
+                ps += x[r];
+            }
+            l += ps;
+            uint4 pb;
+            pb.x = O::pack2(x[0], x[1]);
+            pb.y = O::pack2(x[2], x[3]);
+            pb.z = O::pack2(x[4], x[5]);
+            pb.w = O::pack2(x[6], x[7]);
+            const uint16_t* vb = vbuf[st & 1];
+    #pragma unroll
+            for (int o = 0; o < NO; ++o) {
+                const int pc = (2 * o + tcol_lo) ^ tsw;
+                const uint2 lo = lds_read_tr16(vb + trow * D + 8 * pc + tsub);
+                const uint2 hi = lds_read_tr16(vb + (trow + 16) * D + 8 * pc + tsub);
+                acc[o] = O::mma16(make_uint4(lo.x, lo.y, hi.x, hi.y), pb, acc[o]);
+            }
+        };
+
+        if (nsteps > 0) {
             int pg1 = pg, off1 = off;
             advance16(pg1, off1);
-            __builtin_amdgcn_s_waitcnt(FIA_LGKMCNT0);   // reads of the other V buffer done
-            issue(tt0 + ST, pg, off, pg1, off1, knext, (st + 1) & 1);
+            issue(t0, pg, off, pg1, off1, kfa, 0);
             pg = pg1; off = off1;
             advance16(pg, off);
-            __builtin_amdgcn_s_waitcnt(FIA_VMCNT(2 * (NK + NVI)));   // step st landed
-        } else {
-            __builtin_amdgcn_s_waitcnt(FIA_VMCNT(0));
         }
-        __syncthreads();
+        for (int st = 0; st < nsteps; st += 2) {
+            step(st, kfa, kfb);
+            if (st + 1 < nsteps) step(st + 1, kfb, kfa);
+        }
 
-        f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < NK; ++s) {
-            s0 = O::mma16(kcur[0][s], qf[s], s0);
-            s1 = O::mma16(kcur[1][s], qf[s], s1);
-        }
-        float x[8];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            x[i] = s0[i];
-            x[4 + i] = s1[i];
-        }
-        if (tt0 + ST > t1) {
-#pragma unroll
-            for (int r = 0; r < 8; ++r) {
-                const int tk = tt0 + 16 * (r >> 2) + 4 * qd + (r & 3);
-                if (tk >= t1) x[r] = -INFINITY;
+        // partial: normalised O and natural-log LSE of this split
+        const float lt = quad_sum(l);
+        if (n < nh) {
+            const float inv = lt > 0.f ? 1.f / lt : 0.f;
+            float* po = a.part_o + ((int64_t)item * a.Gc + n) * D;
+    #pragma unroll
+            for (int o = 0; o < NO; ++o) {
+                f32x4 v = acc[o] * inv;
+                *(f32x4*)(po + 16 * o + 4 * qd) = v;
             }
+            if (qd == 0)
+                a.part_lse[(int64_t)item * a.Gc + n] = lt > 0.f ? (m * c + __log2f(lt)) * kLn2 : -INFINITY;
         }
-        float mt = x[0];
-#pragma unroll
-        for (int r = 1; r < 8; ++r) mt = fmaxf(mt, x[r]);
-        mt = quad_max(mt);
-        const float mn = fmaxf(m, mt);
-        const bool grow = (m == -INFINITY) ? (mn > -INFINITY) : (mn > m + lazy_raw);
-        if (__ballot(grow)) {
-            float alpha = 1.f;
-            if (m == -INFINITY) alpha = 0.f;
-            else if (mn != -INFINITY) alpha = fast_exp2((m - mn) * c);
-            m = mn;
-            l *= alpha;
-#pragma unroll
-            for (int o = 0; o < NO; ++o) acc[o] *= alpha;
-        }
-        const float mc = (m == -INFINITY) ? 0.f : m * c;
-        float ps = 0.f;
-#pragma unroll
-        for (int r = 0; r < 8; ++r) {
-            x[r] = fast_exp2(__builtin_fmaf(x[r], c, -mc));
-            ps += x[r];
-        }
-        l += ps;
-        uint4 pb;
-        pb.x = O::pack2(x[0], x[1]);
-        pb.y = O::pack2(x[2], x[3]);
-        pb.z = O::pack2(x[4], x[5]);
-        pb.w = O::pack2(x[6], x[7]);
-        const uint16_t* vb = vbuf[st & 1];
-#pragma unroll
-        for (int o = 0; o < NO; ++o) {
-            const int pc = (2 * o + tcol_lo) ^ tsw;
-            const uint2 lo = lds_read_tr16(vb + trow * D + 8 * pc + tsub);
-            const uint2 hi = lds_read_tr16(vb + (trow + 16) * D + 8 * pc + tsub);
-            acc[o] = O::mma16(make_uint4(lo.x, lo.y, hi.x, hi.y), pb, acc[o]);
-        }
-    };
-
-    if (nsteps > 0) {
-        int pg1 = pg, off1 = off;
-        advance16(pg1, off1);
-        issue(t0, pg, off, pg1, off1, kfa, 0);
-        pg = pg1; off = off1;
-        advance16(pg, off);
-    }
-    for (int st = 0; st < nsteps; st += 2) {
-        step(st, kfa, kfb);
-        if (st + 1 < nsteps) step(st + 1, kfb, kfa);
-    }
-
-    // partial: normalised O and natural-log LSE of this split
-    const float lt = quad_sum(l);
-    if (n < nh) {
-        const float inv = lt > 0.f ? 1.f / lt : 0.f;
-        float* po = a.part_o + ((int64_t)item * a.Gc + n) * D;
-#pragma unroll
-        for (int o = 0; o < NO; ++o) {
-            f32x4 v = acc[o] * inv;
-            *(f32x4*)(po + 16 * o + 4 * qd) = v;
-        }
-        if (qd == 0)
-            a.part_lse[(int64_t)item * a.Gc + n] = lt > 0.f ? (m * c + __log2f(lt)) * kLn2 : -INFINITY;
+        __syncthreads();     // the LDS buffers are reused by the next piece
     }
 }
 
@@ -734,9 +731,9 @@ __global__ __launch_bounds__(64) void decode_combine(DecodeArgs a)
     const int b = bh / a.QN, h = bh % a.QN;
     const int kvh = h / a.G, r = h % a.G;
     const int hc = r / kDecodeHeads, n = r % kDecodeHeads;
-    const DecBatch db = a.batch[b];
-    const int ns = db.nsplit;
-    const int64_t slot0 = db.item0 + (int64_t)(kvh * a.nhc + hc) * ns;
+    const DecSeg sg = a.segs[((int64_t)b * a.KVN + kvh) * a.nhc + hc];
+    const int ns = sg.count;
+    const int64_t slot0 = sg.first;
     const int lane = threadIdx.x;
     uint16_t* op = (uint16_t*)a.o + ((int64_t)b * a.QN + h) * D;
 
@@ -818,8 +815,8 @@ int launch_attn(const fia_plan& p, const AttnArgs& a, hipStream_t stream)
 template <int DT, int D>
 int launch_dec(const fia_plan& p, const DecodeArgs& a, hipStream_t stream)
 {
-    if (p.n_items > 0)
-        hipLaunchKernelGGL((decode_split<DT, D>), dim3((unsigned)p.n_items), dim3(64), 0, stream, a);
+    if (p.n_waves > 0)
+        hipLaunchKernelGGL((decode_split<DT, D>), dim3((unsigned)p.n_waves), dim3(64), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return (int)e;
     hipLaunchKernelGGL((decode_combine<DT, D>), dim3((unsigned)(p.B * p.QN)), dim3(64), 0, stream, a);

@@ -463,43 +463,67 @@ fia_status fia_get_workspace_size(const fia_tensor* query, const fia_tensor* key
         const int64_t G = QN / KVN;
         const int64_t Gc = std::min<int64_t>(G, kDecodeHeads);
         const int64_t nhc = (G + kDecodeHeads - 1) / kDecodeHeads;
-        // Split plan: kv tokens per wave item, a multiple of the decode step,
-        // sized so the grid holds several waves per wave slot of the chip.
-        int64_t tok_heads = 0;
-        for (int64_t b = 0; b < B; ++b) tok_heads += lkv[(size_t)b] * KVN * nhc;
-        const int64_t target_items = (int64_t)kNumCUs * 8 * 4;
-        int64_t chunk = tok_heads / std::max<int64_t>(1, target_items);
-        chunk = (chunk + 255) / 256 * 256;
-        chunk = std::max<int64_t>(256, std::min<int64_t>(chunk, 4096));
-        std::vector<DecBatch> db((size_t)B);
-        int64_t items = 0;
-        for (int64_t b = 0; b < B; ++b) {
-            const int64_t L = lkv[(size_t)b];
-            const int64_t ns = (L + chunk - 1) / chunk;
-            db[(size_t)b].kv_row0 = paged ? 0 : b * Skv;
-            db[(size_t)b].lkv = (int32_t)L;
-            db[(size_t)b].item0 = (int32_t)items;
-            db[(size_t)b].nsplit = (int32_t)ns;
-            db[(size_t)b].pad = 0;
-            items += KVN * nhc * ns;
-        }
-        if (items > INT32_MAX / 2) return FIA_ERR_UNSUPPORTED;
+        // Balanced schedule: one wave per resident slot, each with an equal
+        // quota of the concatenated token stream (a multiple of 16 tokens, so
+        // a 16-token sub-tile never crosses a page).
+        const int64_t nseg = B * KVN * nhc;
+        int64_t total = 0;
+        for (int64_t b = 0; b < B; ++b) total += lkv[(size_t)b] * KVN * nhc;
+        const int64_t steps = (total + kDecodeStep - 1) / kDecodeStep;
+        const int64_t W = std::min<int64_t>((int64_t)kNumCUs * kDecodeWavesPerCU, steps);
+        int64_t quota = W > 0 ? (total + W - 1) / W : 0;
+        quota = (quota + kDecodeStep - 1) / kDecodeStep * kDecodeStep;
+        std::vector<DecSeg> segs((size_t)nseg);
+        std::vector<DecPiece> pieces;
+        std::vector<int32_t> wave_first;
+        wave_first.push_back(0);
+        int64_t remaining = quota;
+        for (int64_t b = 0; b < B; ++b)
+            for (int64_t g = 0; g < KVN * nhc; ++g) {
+                const int64_t si = b * KVN * nhc + g;
+                const int64_t L = lkv[(size_t)b];
+                DecSeg& sg = segs[(size_t)si];
+                sg.kv_row0 = paged ? 0 : b * Skv;
+                sg.b = (int32_t)b;
+                sg.lkv = (int32_t)L;
+                sg.first = (int32_t)pieces.size();
+                for (int64_t t = 0; t < L;) {
+                    if (remaining < 16) {                  // next wave
+                        wave_first.push_back((int32_t)pieces.size());
+                        remaining = quota;
+                    }
+                    const int64_t take = std::min(L - t, remaining / 16 * 16);
+                    pieces.push_back(DecPiece{(int32_t)si, (int32_t)t, (int32_t)(t + take), 0});
+                    t += take;
+                    remaining -= take;
+                    remaining = remaining / 16 * 16;       // keep pieces 16-aligned
+                }
+                sg.count = (int32_t)pieces.size() - sg.first;
+            }
+        if (!pieces.empty()) wave_first.push_back((int32_t)pieces.size());
+        if (pieces.size() > (size_t)INT32_MAX / 2) return FIA_ERR_UNSUPPORTED;
         d.B = (int32_t)B;
         d.QN = (int32_t)QN;
         d.KVN = (int32_t)KVN;
         d.G = (int32_t)G;
         d.Gc = (int32_t)Gc;
         d.nhc = (int32_t)nhc;
-        d.chunk = (int32_t)chunk;
-        d.n_items = (int32_t)items;
+        d.n_waves = (int32_t)(wave_first.size() - 1);
+        d.n_pieces = (int32_t)pieces.size();
         d.scale_log2 = (float)scale_log2;
-        p->n_items = items;
+        p->n_waves = d.n_waves;
+        p->n_pieces = d.n_pieces;
         p->off_batch = 0;
-        put(p->host_tables, 0, db);
+        uint64_t end = put(p->host_tables, 0, segs);
+        p->off_pieces = align_up(end, 256);
+        end = put(p->host_tables, p->off_pieces, pieces);
+        p->off_waves = align_up(end, 256);
+        put(p->host_tables, p->off_waves, wave_first);
         finish_tables(p.get());
+        const uint64_t np = std::max<uint64_t>(1, pieces.size());
         p->off_part_o = 0;
-        p->off_part_lse = align_up(p->off_part_o + (uint64_t)items * Gc * Dv * 4, 256);
-        p->workspace_bytes = align_up(p->off_part_lse + (uint64_t)items * Gc * 4, 256);
+        p->off_part_lse = align_up(p->off_part_o + np * Gc * Dv * 4, 256);
+        p->workspace_bytes = align_up(p->off_part_lse + np * Gc * 4, 256);
         *workspace_size = p->workspace_bytes;
         *plan_out = p.release();
         return FIA_OK;
@@ -818,7 +842,9 @@ static fia_status run_common(void* ws, uint64_t ws_size, fia_plan* p, void* stre
     int rc = 0;
     if (p->kind == KIND_DECODE) {
         DecodeArgs d = p->dec;
-        d.batch = (const DecBatch*)(tb + p->off_batch);
+        d.segs = (const DecSeg*)(tb + p->off_batch);
+        d.pieces = (const DecPiece*)(tb + p->off_pieces);
+        d.wave_first = (const int32_t*)(tb + p->off_waves);
         d.part_o = (float*)(w + p->off_part_o);
         d.part_lse = (float*)(w + p->off_part_lse);
         rc = launch_decode(*p, d, stream);
