@@ -92,6 +92,22 @@ def decode_bytes(case) -> int:
     return kv + qo + lse + bt
 
 
+def measured_traffic(name):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when it was taken on a different kernel source."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "hbm_traffic_counters.txt")
+    src = os.path.join(ROOT, "attention_fia_fwd_amd", "csrc", "fia_kernels.hip")
+    if not os.path.exists(path):
+        return None
+    kv = dict(l.strip().split("=", 1) for l in open(path) if "=" in l and not l.startswith("#"))
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    if kv.get("kernel_source_sha256_prefix") != sha or f"{name}_fetch_kib" not in kv:
+        return None
+    return int(float(kv[f"{name}_fetch_kib"]) * 1024 * float(kv["fetch_scale"]) +
+               float(kv[f"{name}_write_kib"]) * 1024 * float(kv["write_scale"]))
+
+
 def time_plan(plan, steps: int, warmup: int):
     """Warm up, then time `steps` runs: wall clock between synchronizations
     and HIP events on the stream the kernels are launched on."""
@@ -152,6 +168,7 @@ def measure(name, steps, warmup):
                    roofline={"bound": "mfma", "achieved": flops / ev / 1e12,
                              "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                              "frac": flops / ev / 1e12 / PEAK_BF16_TFLOPS})
+    res["roofline"]["traffic"] = measured_traffic(name)
     plan.close()
     del case
     torch.cuda.empty_cache()
@@ -164,7 +181,6 @@ def cpu_baseline(name="c2", target_s=15.0):
     import numpy as np
     import oracle
     import workloads as W
-    from fia_gpu import sample_rows
     case = W.WORKLOADS[name](device="cpu")
     lq = case.lq
     rng = np.random.default_rng(99)
@@ -180,11 +196,11 @@ def cpu_baseline(name="c2", target_s=15.0):
         # causal, Lq = Lkv: row i sees i + 1 keys
         return sum(2 * (case.Dqk + case.Dv) * (i + 1) for _, _, i in rows)
 
-    pilot = rows_of(64)
+    pilot = rows_of(2048)
     t0 = time.perf_counter()
     oracle.attention(case, rows=pilot)
     dt = time.perf_counter() - t0
-    n = int(min(200000, max(64, 64 * target_s / max(dt, 1e-3))))
+    n = int(min(5_000_000, max(2048, 2048 * target_s / max(dt, 1e-3))))
     rows = rows_of(n)
     t0 = time.perf_counter()
     oracle.attention(case, rows=rows)
@@ -256,7 +272,7 @@ def main():
                    "phase1_us": head["phase1_us"],
                    "device": getattr(props, "gcnArchName", props.name),
                    "compute_units": props.multi_processor_count},
-        "roofline": dict(head["roofline"], traffic=None),
+        "roofline": head["roofline"],
         "cpu_baseline": cpu,
         "secondary": secondary,
     }
