@@ -134,23 +134,54 @@ constexpr float kLazy = 8.f;
 constexpr float kMinScale = 1e-30f;
 
 typedef __attribute__((address_space(3))) void lds_void;
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Buffer resource (V#) over `bytes` bytes at `base`: stride 0, raw 32-bit
+// dword format; offsets at or past `bytes` read as zero.
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, int64_t bytes)
+{
+    const uint64_t addr = (uint64_t)(uintptr_t)base;
+    // the values are wave-uniform; readfirstlane places them in SGPRs
+    i32x4 r;
+    r.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)addr);
+    r.y = __builtin_amdgcn_readfirstlane((int)((uint32_t)(addr >> 32) & 0xffffu));
+    r.z = __builtin_amdgcn_readfirstlane((int)min(max(bytes, (int64_t)0), (int64_t)0x7fffffff));
+    r.w = 0x00020000;
+    return r;
+}
 
 // 16 bytes per lane from a buffer resource straight into LDS: lane i of the
-// wave writes lds_wave + 16 i.  Offsets past the resource's range read 0.
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, uint16_t* lds_wave, uint32_t voff)
+// wave writes lds_wave + 16 i.  Issued as inline assembly on purpose: the
+// compiler cannot prove that LDS reads of the other pipeline buffer do not
+// alias these writes and would otherwise wait for the prefetch to finish
+// before every read.  The kernels order the data themselves: vmcnt wait +
+// barrier before a buffer is read, and no prefetch into a buffer before its
+// last reads are complete.
+__device__ __forceinline__ void dma16(i32x4 rs, const uint16_t* lds_wave, uint32_t voff)
+{
+    const uint32_t m0v = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)lds_wave);
+    // m0 is reserved by the compiler: save and restore it around the load
+    uint32_t keep;
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
+                 "buffer_load_dwordx4 %2, %3, 0 offen lds\n\ts_mov_b32 m0, %0"
+                 : "=&s"(keep) : "s"(m0v), "v"(voff), "s"(rs) : "memory");
+}
+
+// The same load through the compiler-visible intrinsic (the compiler then
+// orders the LDS reads after it conservatively).
+__device__ __forceinline__ void dma16_tracked(__amdgpu_buffer_rsrc_t rs, uint16_t* lds_wave, uint32_t voff)
 {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)lds_wave, 16, voff, 0, 0, 0);
 }
 
 // Buffer resource over rows [row0, lkv) of a row-strided tensor (rows of
 // `rowlen` elements every `stride` elements); 0 valid bytes when none.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const uint16_t* base, int64_t row0,
-                                                            int64_t lkv, int64_t stride, int rowlen)
+__device__ __forceinline__ i32x4 rows_rsrc(const uint16_t* base, int64_t row0, int64_t lkv,
+                                           int64_t stride, int rowlen)
 {
     const int64_t n = lkv - row0;
     const int64_t bytes = n > 0 ? ((n - 1) * stride + rowlen) * 2 : 0;
-    return __builtin_amdgcn_make_buffer_rsrc((void*)(base + row0 * stride), (short)0,
-                                             (int)min(bytes, (int64_t)0x7fffffff), 0x00020000);
+    return make_rsrc(base + row0 * stride, bytes);
 }
 
 template <int DT, int DQK, int DV, bool BSA>
@@ -262,8 +293,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd(AttnArgs a)
     auto load_tile = [&](int c0, int buf) {
         uint16_t* ks = smem + buf * STAGE;
         uint16_t* vs = ks + KT;
-        const __amdgpu_buffer_rsrc_t kr = rows_rsrc(kp, c0, Lkv, a.k_sS, DQK);
-        const __amdgpu_buffer_rsrc_t vr = rows_rsrc(vp, c0, Lkv, a.v_sS, DV);
+        const i32x4 kr = rows_rsrc(kp, c0, Lkv, a.k_sS, DQK);
+        const i32x4 vr = rows_rsrc(vp, c0, Lkv, a.v_sS, DV);
 #pragma unroll
         for (int u = 0; u < NKI; ++u) {
             const int blk = 4 * u + w;
@@ -519,7 +550,8 @@ __global__ __launch_bounds__(64) void decode_split(DecodeArgs a)
     constexpr int RPI = 64 / VCH;         // V rows per DMA instruction
     constexpr int NVI = 16 / RPI;         // DMA instructions per sub-tile
     using O = Ops<DT>;
-    __shared__ __attribute__((aligned(16))) uint16_t vbuf[2][ST * D];
+    __shared__ __attribute__((aligned(16))) uint16_t vbuf0[ST * D];
+    __shared__ __attribute__((aligned(16))) uint16_t vbuf1[ST * D];
 
     const int lane = threadIdx.x;
     const int n = lane & 15, qd = lane >> 4;
@@ -542,14 +574,14 @@ __global__ __launch_bounds__(64) void decode_split(DecodeArgs a)
         uint4 qf[NK];
         if (n < nh) {
             const uint16_t* src = (const uint16_t*)a.q + ((int64_t)b * a.QN + hq) * D + 8 * qd;
-    #pragma unroll
+#pragma unroll
             for (int s = 0; s < NK; ++s) {
                 uint4 v = *(const uint4*)(src + 32 * s);
                 v.x ^= qflip; v.y ^= qflip; v.z ^= qflip; v.w ^= qflip;
                 qf[s] = v;
             }
         } else {
-    #pragma unroll
+#pragma unroll
             for (int s = 0; s < NK; ++s) qf[s] = make_uint4(0, 0, 0, 0);
         }
 
@@ -561,15 +593,25 @@ __global__ __launch_bounds__(64) void decode_split(DecodeArgs a)
         const uint16_t* vbase = (const uint16_t*)a.v;
         const int64_t hoff = a.paged ? (int64_t)kvh * a.p_head
                                      : db.kv_row0 * a.c_rowmul + (int64_t)kvh * a.c_head;
+        // The piece's block-table entries (at most 64 pages; the planner caps
+        // piece lengths): lane i holds the id of page pg_first + i, so a
+        // sub-tile's page id comes from v_readlane without a memory access.
+        const int pg_first = t0 / bs;
+        const int pg_last = t1 > t0 ? (t1 - 1) / bs : pg_first;
+        const int my_page = (a.paged && pg_first + lane <= pg_last) ? bt[pg_first + lane] : 0;
+        // settle the table load here: a wait for it inside the step loop
+        // would also drain the prefetch in flight
+        __builtin_amdgcn_s_waitcnt(FIA_VMCNT(0));
         auto sub_rsrc = [&](const uint16_t* base, int pg, int off, int tb) {
             // rows [off, off + nvalid) of page pg; rows past t1 read as zero
             const int nvalid = min(16, t1 - tb);
             // a sub-tile past the end reads nothing, not even its table entry
-            const int64_t pbase = (a.paged && nvalid > 0) ? (int64_t)bt[pg] * a.p_blk : 0;
+            const int64_t pbase =
+                (a.paged && nvalid > 0) ? (int64_t)__builtin_amdgcn_readlane(my_page, pg - pg_first) * a.p_blk : 0;
             const int64_t bytes = nvalid > 0 ? ((int64_t)(nvalid - 1) * tokstride + D) * 2 : 0;
-            return __builtin_amdgcn_make_buffer_rsrc(
-                (void*)(base + pbase + hoff + (int64_t)off * tokstride), (short)0,
-                (int)min(bytes, (int64_t)0x7fffffff), 0x00020000);
+            return __builtin_amdgcn_make_buffer_rsrc((void*)(base + pbase + hoff + (int64_t)off * tokstride),
+                                                         (short)0, (int)min(bytes, (int64_t)0x7fffffff),
+                                                         0x00020000);
         };
 
         // K rows into registers: lane (token n, quarter qd) reads d = 32s + 8qd.
@@ -578,22 +620,22 @@ __global__ __launch_bounds__(64) void decode_split(DecodeArgs a)
         const int vr_in = lane / VCH, vpc = lane % VCH;
         auto vswz = [](int r) { return VCH >= 16 ? 2 * (r & 7) : 2 * ((r >> 1) & 3); };
 
-        auto issue = [&](int tt0, int pg0, int off0, int pg1, int off1, uint4 (&kf)[2][NK], int buf) {
-    #pragma unroll
+        auto issue = [&](int tt0, int pg0, int off0, int pg1, int off1, uint4 (&kf)[2][NK], uint16_t* vb) {
+#pragma unroll
             for (int cc = 0; cc < 2; ++cc) {
                 const int pg = cc ? pg1 : pg0, off = cc ? off1 : off0, tb = tt0 + 16 * cc;
                 const __amdgpu_buffer_rsrc_t kr = sub_rsrc(kbase, pg, off, tb);
-    #pragma unroll
+#pragma unroll
                 for (int s = 0; s < NK; ++s)
                     kf[cc][s] = __builtin_bit_cast(
                         uint4, __builtin_amdgcn_raw_buffer_load_b128(kr, k_voff + 64 * s, 0, 0));
                 const __amdgpu_buffer_rsrc_t vr = sub_rsrc(vbase, pg, off, tb);
-    #pragma unroll
+#pragma unroll
                 for (int u = 0; u < NVI; ++u) {
                     const int r = RPI * u + vr_in;                 // row inside the sub-tile
                     const int R = 16 * cc + r;                     // row inside the step
                     const int chunk = vpc ^ vswz(R);
-                    dma16(vr, &vbuf[buf][(16 * cc + RPI * u) * D], (uint32_t)((r * tokstride + 8 * chunk) * 2));
+                    dma16_tracked(vr, vb + (16 * cc + RPI * u) * D, (uint32_t)((r * tokstride + 8 * chunk) * 2));
                 }
             }
         };
@@ -607,7 +649,7 @@ __global__ __launch_bounds__(64) void decode_split(DecodeArgs a)
         const int tcol_lo = (vi & 3) >> 1, tsub = 4 * (vi & 1);
 
         f32x4 acc[NO];
-    #pragma unroll
+#pragma unroll
         for (int o = 0; o < NO; ++o) acc[o] = f32x4{0.f, 0.f, 0.f, 0.f};
         float m = -INFINITY, l = 0.f;
         const float lazy_raw = kLazy / c;
@@ -620,14 +662,14 @@ __global__ __launch_bounds__(64) void decode_split(DecodeArgs a)
         };
 
         uint4 kfa[2][NK], kfb[2][NK];
-        auto step = [&](int st, uint4 (&kcur)[2][NK], uint4 (&knext)[2][NK]) {
+        auto step = [&](int st, uint4 (&kcur)[2][NK], uint4 (&knext)[2][NK], uint16_t* vcur, uint16_t* vnext) {
             const int tt0 = t0 + ST * st;
             // pg/off point at the first sub-tile of step st + 1 here
             if (st + 1 < nsteps) {
                 int pg1 = pg, off1 = off;
                 advance16(pg1, off1);
                 __builtin_amdgcn_s_waitcnt(FIA_LGKMCNT0);   // reads of the other V buffer done
-                issue(tt0 + ST, pg, off, pg1, off1, knext, (st + 1) & 1);
+                issue(tt0 + ST, pg, off, pg1, off1, knext, vnext);
                 pg = pg1; off = off1;
                 advance16(pg, off);
                 __builtin_amdgcn_s_waitcnt(FIA_VMCNT(2 * (NK + NVI)));   // step st landed
@@ -637,26 +679,26 @@ __global__ __launch_bounds__(64) void decode_split(DecodeArgs a)
             __syncthreads();
 
             f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-    #pragma unroll
+#pragma unroll
             for (int s = 0; s < NK; ++s) {
                 s0 = O::mma16(kcur[0][s], qf[s], s0);
                 s1 = O::mma16(kcur[1][s], qf[s], s1);
             }
             float x[8];
-    #pragma unroll
+#pragma unroll
             for (int i = 0; i < 4; ++i) {
                 x[i] = s0[i];
                 x[4 + i] = s1[i];
             }
             if (tt0 + ST > t1) {
-    #pragma unroll
+#pragma unroll
                 for (int r = 0; r < 8; ++r) {
                     const int tk = tt0 + 16 * (r >> 2) + 4 * qd + (r & 3);
                     if (tk >= t1) x[r] = -INFINITY;
                 }
             }
             float mt = x[0];
-    #pragma unroll
+#pragma unroll
             for (int r = 1; r < 8; ++r) mt = fmaxf(mt, x[r]);
             mt = quad_max(mt);
             const float mn = fmaxf(m, mt);
@@ -667,12 +709,12 @@ __global__ __launch_bounds__(64) void decode_split(DecodeArgs a)
                 else if (mn != -INFINITY) alpha = fast_exp2((m - mn) * c);
                 m = mn;
                 l *= alpha;
-    #pragma unroll
+#pragma unroll
                 for (int o = 0; o < NO; ++o) acc[o] *= alpha;
             }
             const float mc = (m == -INFINITY) ? 0.f : m * c;
             float ps = 0.f;
-    #pragma unroll
+#pragma unroll
             for (int r = 0; r < 8; ++r) {
                 x[r] = fast_exp2(__builtin_fmaf(x[r], c, -mc));
                 ps += x[r];
@@ -683,8 +725,8 @@ __global__ __launch_bounds__(64) void decode_split(DecodeArgs a)
             pb.y = O::pack2(x[2], x[3]);
             pb.z = O::pack2(x[4], x[5]);
             pb.w = O::pack2(x[6], x[7]);
-            const uint16_t* vb = vbuf[st & 1];
-    #pragma unroll
+            const uint16_t* vb = vcur;
+#pragma unroll
             for (int o = 0; o < NO; ++o) {
                 const int pc = (2 * o + tcol_lo) ^ tsw;
                 const uint2 lo = lds_read_tr16(vb + trow * D + 8 * pc + tsub);
@@ -696,13 +738,13 @@ __global__ __launch_bounds__(64) void decode_split(DecodeArgs a)
         if (nsteps > 0) {
             int pg1 = pg, off1 = off;
             advance16(pg1, off1);
-            issue(t0, pg, off, pg1, off1, kfa, 0);
+            issue(t0, pg, off, pg1, off1, kfa, vbuf0);
             pg = pg1; off = off1;
             advance16(pg, off);
         }
         for (int st = 0; st < nsteps; st += 2) {
-            step(st, kfa, kfb);
-            if (st + 1 < nsteps) step(st + 1, kfb, kfa);
+            step(st, kfa, kfb, vbuf0, vbuf1);
+            if (st + 1 < nsteps) step(st + 1, kfb, kfa, vbuf1, vbuf0);
         }
 
         // partial: normalised O and natural-log LSE of this split
@@ -710,7 +752,7 @@ __global__ __launch_bounds__(64) void decode_split(DecodeArgs a)
         if (n < nh) {
             const float inv = lt > 0.f ? 1.f / lt : 0.f;
             float* po = a.part_o + ((int64_t)item * a.Gc + n) * D;
-    #pragma unroll
+#pragma unroll
             for (int o = 0; o < NO; ++o) {
                 f32x4 v = acc[o] * inv;
                 *(f32x4*)(po + 16 * o + 4 * qd) = v;

@@ -473,6 +473,9 @@ fia_status fia_get_workspace_size(const fia_tensor* query, const fia_tensor* key
         const int64_t W = std::min<int64_t>((int64_t)kNumCUs * kDecodeWavesPerCU, steps);
         int64_t quota = W > 0 ? (total + W - 1) / W : 0;
         quota = (quota + kDecodeStep - 1) / kDecodeStep * kDecodeStep;
+        // a piece touches at most 64 pages (one block-table entry per lane)
+        const int64_t piece_cap = paged ? std::max<int64_t>(16, 63 * prm->block_size / 16 * 16)
+                                        : ((int64_t)1 << 40);
         std::vector<DecSeg> segs((size_t)nseg);
         std::vector<DecPiece> pieces;
         std::vector<int32_t> wave_first;
@@ -492,7 +495,7 @@ fia_status fia_get_workspace_size(const fia_tensor* query, const fia_tensor* key
                         wave_first.push_back((int32_t)pieces.size());
                         remaining = quota;
                     }
-                    const int64_t take = std::min(L - t, remaining / 16 * 16);
+                    const int64_t take = std::min(std::min(L - t, remaining / 16 * 16), piece_cap);
                     pieces.push_back(DecPiece{(int32_t)si, (int32_t)t, (int32_t)(t + take), 0});
                     t += take;
                     remaining -= take;
