@@ -13,10 +13,13 @@ namespace fia {
 enum Kind : int32_t { KIND_EMPTY = 0, KIND_PREFILL = 1, KIND_DECODE = 2, KIND_BSA = 3 };
 enum Layout : int32_t { LAYOUT_BNSD = 0, LAYOUT_BSND = 1, LAYOUT_TND = 2 };
 
-// Rows of the attention tiles (query rows per workgroup) and kv tokens per
-// inner step of the prefill / block-sparse kernel.
-constexpr int kBlockM = 128;
+// Query rows per workgroup of the prefill and block-sparse kernels (4 waves
+// of 32 rows) and kv tokens per inner step.
+constexpr int kBlockMDense = 128;
+constexpr int kBlockMSparse = 128;
 constexpr int kBlockN = 64;
+// XCDs of one MI355X: workgroup i of a launch runs on XCD i % kNumXcds.
+constexpr int kNumXcds = 8;
 // Tokens per inner step of the decode kernel; a decode split is a multiple.
 constexpr int kDecodeStep = 32;
 // Query heads one decode wave serves (a GQA group is cut into chunks of this).

@@ -24,6 +24,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <type_traits>
 
 #include "fia_internal.h"
 
@@ -133,6 +134,10 @@ constexpr float kLazy = 8.f;
 // exactly 0 when the scale is 0, while every finite score gives exp2(0) = 1.
 constexpr float kMinScale = 1e-30f;
 
+// waitcnt immediates (gfx9 encoding): vmcnt(n) alone, lgkmcnt(0) alone
+#define FIA_VMCNT(n) (((n) & 15) | (((n) >> 4) << 14) | 0x70 | 0xF00)
+#define FIA_LGKMCNT0 0xC07F
+
 typedef __attribute__((address_space(3))) void lds_void;
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
@@ -151,20 +156,34 @@ __device__ __forceinline__ i32x4 make_rsrc(const void* base, int64_t bytes)
 }
 
 // 16 bytes per lane from a buffer resource straight into LDS: lane i of the
-// wave writes lds_wave + 16 i.  Issued as inline assembly on purpose: the
+// wave writes LDS byte address lds_wave + 16 i.  Issued as inline assembly on purpose: the
 // compiler cannot prove that LDS reads of the other pipeline buffer do not
 // alias these writes and would otherwise wait for the prefetch to finish
 // before every read.  The kernels order the data themselves: vmcnt wait +
 // barrier before a buffer is read, and no prefetch into a buffer before its
 // last reads are complete.
-__device__ __forceinline__ void dma16(i32x4 rs, const uint16_t* lds_wave, uint32_t voff)
+__device__ __forceinline__ void dma16(i32x4 rs, uint32_t lds_wave, uint32_t voff)
 {
-    const uint32_t m0v = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)lds_wave);
+    const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_wave);
     // m0 is reserved by the compiler: save and restore it around the load
     uint32_t keep;
     asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
                  "buffer_load_dwordx4 %2, %3, 0 offen lds\n\ts_mov_b32 m0, %0"
                  : "=&s"(keep) : "s"(m0v), "v"(voff), "s"(rs) : "memory");
+}
+
+// The same resource moved `d` bytes further (fewer valid bytes, never < 0);
+// offsets past the valid range still read as zero.
+__device__ __forceinline__ i32x4 rsrc_advance(i32x4 r, uint32_t d)
+{
+    const uint64_t addr = ((uint64_t)(uint32_t)r.x | ((uint64_t)((uint32_t)r.y & 0xffffu) << 32)) + d;
+    // wave-uniform values: readfirstlane keeps them in SGPRs
+    i32x4 o;
+    o.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)addr);
+    o.y = __builtin_amdgcn_readfirstlane((int)((uint32_t)(addr >> 32) & 0xffffu));
+    o.z = __builtin_amdgcn_readfirstlane((int)((uint32_t)r.z > d ? (uint32_t)r.z - d : 0u));
+    o.w = r.w;
+    return o;
 }
 
 // The same load through the compiler-visible intrinsic (the compiler then
@@ -184,9 +203,35 @@ __device__ __forceinline__ i32x4 rows_rsrc(const uint16_t* base, int64_t row0, i
     return make_rsrc(base + row0 * stride, bytes);
 }
 
-template <int DT, int DQK, int DV, bool BSA>
+// Kinds of the prefill kernel: masks from lengths and sparse_mode bands only;
+// plus an explicit byte mask (sparse_mode 0/1); block-sparse tile lists.
+enum { kDense = 0, kMasked = 1, kSparse = 2 };
+
+// Running max over values that may be -inf (no NaN quieting needed).
+__device__ __forceinline__ float vmax(float x, float y) { return __builtin_elementwise_maximum(x, y); }
+
+// ---------------------------------------------------------------------------
+// Prefill / block-sparse attention.
+//
+// Workgroup: 4 waves, 128 query rows of one head (a block-sparse tile never
+// straddles two q blocks); wave w owns rows q0 + 32w .. q0 + 32w + 31.  Per
+// 64-token kv tile (the q block's list for block-sparse):
+//   S^T (64 x 32 per wave) = K Q^T   two 32x32 MFMA tiles, Q in registers,
+//                                    K read from LDS
+//   online softmax on the S^T accumulators: lane (row, half) holds 32 of the
+//   row's 64 scores; the two halves exchange max and sum once.
+//   O^T (D_v x 32) += V^T P^T         P straight from the S^T registers as the
+//                                    B operand; V read from a row-major LDS
+//                                    tile with the gfx950 transpose read.
+// The kv index set of the B operand slots (from the S^T accumulator layout)
+// and of the A operand slots (from the transposed V reads) is the same, so
+// the contraction pairs each P value with its V row.  K and V tiles are
+// double buffered; the next tile's loads go out at the top of an iteration.
+// ---------------------------------------------------------------------------
+template <int DT, int DQK, int DV, int KIND>
 __global__ __launch_bounds__(256, 2) void attn_fwd(AttnArgs a)
 {
+    constexpr bool BSA = KIND == kSparse;
     constexpr int BN = kBlockN;            // 64 kv tokens per tile
     constexpr int VCH = DV / 8;            // 16-byte chunks per V row
     constexpr int VSW = VCH >= 16 ? 4 : 2; // V chunk swizzle step
@@ -200,9 +245,10 @@ __global__ __launch_bounds__(256, 2) void attn_fwd(AttnArgs a)
     using O = Ops<DT>;
 
     extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
+    const uint32_t smem_lds = (uint32_t)(uintptr_t)(lds_void*)smem;
 
     const int tid = threadIdx.x;
-    const int w = tid >> 6;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
     const int lane = tid & 63;
     const int l32 = lane & 31;
     const int hh = lane >> 5;
@@ -221,7 +267,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd(AttnArgs a)
     const uint16_t* qp = (const uint16_t*)a.q + bi.q_row0 * a.q_rowmul + (int64_t)h * a.q_sH;
     const uint16_t* kp = (const uint16_t*)a.k + bi.kv_row0 * a.k_rowmul + (int64_t)g * a.k_sH;
     const uint16_t* vp = (const uint16_t*)a.v + bi.kv_row0 * a.v_rowmul + (int64_t)g * a.v_sH;
-    const uint8_t* mbase = a.has_mask ? a.mask + (int64_t)t.b * a.mask_bstride : nullptr;
+    // the explicit mask exists only in the kMasked instantiation
+    const uint8_t* mbase = KIND == kMasked ? a.mask + (int64_t)t.b * a.mask_bstride : nullptr;
 
     const int wr0 = q0 + 32 * w;           // first row of this wave
     const int row = wr0 + l32;             // this lane's query row
@@ -291,8 +338,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd(AttnArgs a)
     //   V: row-major rows of DV; chunk c of row r sits at c ^ VSW (r & 3): the
     //      4-row groups of the transposed reads hit distinct bank groups.
     auto load_tile = [&](int c0, int buf) {
-        uint16_t* ks = smem + buf * STAGE;
-        uint16_t* vs = ks + KT;
+        const uint32_t ks = smem_lds + 2u * (uint32_t)(buf * STAGE);
+        const uint32_t vs = ks + 2u * KT;
         const i32x4 kr = rows_rsrc(kp, c0, Lkv, a.k_sS, DQK);
         const i32x4 vr = rows_rsrc(vp, c0, Lkv, a.v_sS, DV);
 #pragma unroll
@@ -308,7 +355,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd(AttnArgs a)
                 r = (sl >> 3) & 63;
                 col = 64 * pnl + 8 * ((sl & 7) ^ ((r >> 1) & 7));
             }
-            dma16(kr, ks + blk * 512, (uint32_t)(r * a.k_sS + col) * 2u);
+            dma16(kr, ks + 1024u * blk, (uint32_t)(r * a.k_sS + col) * 2u);
         }
 #pragma unroll
         for (int u = 0; u < NVI; ++u) {
@@ -316,7 +363,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd(AttnArgs a)
             const int sl = 64 * blk + lane;
             const int r = sl / VCH, pc = sl % VCH;
             const int cc = pc ^ (VSW * (r & 3));
-            dma16(vr, vs + blk * 512, (uint32_t)(r * a.v_sS + 8 * cc) * 2u);
+            dma16(vr, vs + 1024u * blk, (uint32_t)(r * a.v_sS + 8 * cc) * 2u);
         }
     };
 
@@ -429,9 +476,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd(AttnArgs a)
         }
 
         // row max over the tile (raw score units; c > 0)
-        float mt = fmaxf(s0[0], s1[0]);
+        float mt = vmax(s0[0], s1[0]);
 #pragma unroll
-        for (int r = 1; r < 16; ++r) mt = fmaxf(mt, fmaxf(s0[r], s1[r]));
+        for (int r = 1; r < 16; ++r) mt = vmax(mt, vmax(s0[r], s1[r]));
         mt = other_half_max(mt);
         const float mn = fmaxf(m, mt);
         const bool grow = (m == -INFINITY) ? (mn > -INFINITY) : (mn > m + lazy_raw);
@@ -536,9 +583,6 @@ __device__ __forceinline__ float quad_sum(float x)
     return other_half_sum(x);
 }
 
-// waitcnt immediates (gfx9 encoding): vmcnt(n) alone, lgkmcnt(0) alone
-#define FIA_VMCNT(n) (((n) & 15) | (((n) >> 4) << 14) | 0x70 | 0xF00)
-#define FIA_LGKMCNT0 0xC07F
 
 template <int DT, int D>
 __global__ __launch_bounds__(64) void decode_split(DecodeArgs a)
@@ -835,22 +879,25 @@ __global__ __launch_bounds__(256) void bsa_compact(const uint8_t* mask, const Ba
     if (lane == 0) cnt[row] = base;
 }
 
-template <int DT, int DQK, int DV, bool BSA>
-int launch_attn(const fia_plan& p, const AttnArgs& a, hipStream_t stream)
+template <typename K>
+void raise_lds_limit(K kernel, size_t lds, bool& configured)
 {
-    constexpr int STAGE = kBlockN * DQK + kBlockN * DV;
-    const size_t lds = 2 * STAGE * sizeof(uint16_t);
-    static bool configured = false;
     if (!configured) {
         // raise the dynamic LDS limit past the 64 KB default (gfx950: 160 KB)
-        (void)hipFuncSetAttribute((const void*)attn_fwd<DT, DQK, DV, BSA>,
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        (void)hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         (void)hipGetLastError();
         configured = true;
     }
+}
+
+template <int DT, int DQK, int DV, int KIND>
+int launch_attn(const fia_plan& p, const AttnArgs& a, hipStream_t stream)
+{
+    const size_t lds = 2 * (size_t)kBlockN * (DQK + DV) * sizeof(uint16_t);
+    static bool configured = false;
+    raise_lds_limit(attn_fwd<DT, DQK, DV, KIND>, lds, configured);
     if (p.n_tiles == 0) return 0;
-    hipLaunchKernelGGL((attn_fwd<DT, DQK, DV, BSA>), dim3((unsigned)p.n_tiles), dim3(256), lds,
-                       stream, a);
+    hipLaunchKernelGGL((attn_fwd<DT, DQK, DV, KIND>), dim3((unsigned)p.n_tiles), dim3(256), lds, stream, a);
     return (int)hipGetLastError();
 }
 
@@ -867,16 +914,22 @@ int launch_dec(const fia_plan& p, const DecodeArgs& a, hipStream_t stream)
 
 }  // namespace
 
+template <int DT, int DQK, int DV>
+int launch_prefill_kind(const fia_plan& p, const AttnArgs& a, hipStream_t s)
+{
+    return a.has_mask ? launch_attn<DT, DQK, DV, kMasked>(p, a, s) : launch_attn<DT, DQK, DV, kDense>(p, a, s);
+}
+
 int launch_prefill(const fia_plan& p, const AttnArgs& a, void* stream)
 {
     hipStream_t s = (hipStream_t)stream;
     const bool bf = p.dtype == FIA_BF16;
     if (p.Dqk == 64 && p.Dv == 64)
-        return bf ? launch_attn<FIA_BF16, 64, 64, false>(p, a, s) : launch_attn<FIA_F16, 64, 64, false>(p, a, s);
+        return bf ? launch_prefill_kind<FIA_BF16, 64, 64>(p, a, s) : launch_prefill_kind<FIA_F16, 64, 64>(p, a, s);
     if (p.Dqk == 128 && p.Dv == 128)
-        return bf ? launch_attn<FIA_BF16, 128, 128, false>(p, a, s) : launch_attn<FIA_F16, 128, 128, false>(p, a, s);
+        return bf ? launch_prefill_kind<FIA_BF16, 128, 128>(p, a, s) : launch_prefill_kind<FIA_F16, 128, 128>(p, a, s);
     if (p.Dqk == 192 && p.Dv == 128)
-        return bf ? launch_attn<FIA_BF16, 192, 128, false>(p, a, s) : launch_attn<FIA_F16, 192, 128, false>(p, a, s);
+        return bf ? launch_prefill_kind<FIA_BF16, 192, 128>(p, a, s) : launch_prefill_kind<FIA_F16, 192, 128>(p, a, s);
     return (int)hipErrorInvalidValue;
 }
 
@@ -892,9 +945,9 @@ int launch_bsa(const fia_plan& p, const AttnArgs& a, void* stream)
     }
     const bool bf = p.dtype == FIA_BF16;
     if (p.Dqk == 64)
-        return bf ? launch_attn<FIA_BF16, 64, 64, true>(p, a, s) : launch_attn<FIA_F16, 64, 64, true>(p, a, s);
+        return bf ? launch_attn<FIA_BF16, 64, 64, kSparse>(p, a, s) : launch_attn<FIA_F16, 64, 64, kSparse>(p, a, s);
     if (p.Dqk == 128)
-        return bf ? launch_attn<FIA_BF16, 128, 128, true>(p, a, s) : launch_attn<FIA_F16, 128, 128, true>(p, a, s);
+        return bf ? launch_attn<FIA_BF16, 128, 128, kSparse>(p, a, s) : launch_attn<FIA_F16, 128, 128, kSparse>(p, a, s);
     return (int)hipErrorInvalidValue;
 }
 

@@ -159,6 +159,32 @@ int64_t kv_tiles_of(int32_t mode, bool has_mask, int64_t pre, int64_t next, int6
     return (hi - start + kBlockN - 1) / kBlockN;
 }
 
+// Launch order for n tiles given in priority order: position i runs on XCD
+// i % kNumXcds, so position i takes the first remaining tile that prefers
+// that XCD; when none is left, the first remaining tile of any XCD.
+template <class Get, class Pref>
+std::vector<Tile> xcd_order(size_t n, Get get, Pref pref)
+{
+    std::vector<std::vector<size_t>> q((size_t)kNumXcds);
+    for (size_t i = 0; i < n; ++i) q[(size_t)pref(i)].push_back(i);
+    std::vector<size_t> head((size_t)kNumXcds, 0);
+    std::vector<Tile> out;
+    out.reserve(n);
+    for (size_t pos = 0; pos < n; ++pos) {
+        size_t x = pos % (size_t)kNumXcds;
+        if (head[x] == q[x].size()) {
+            size_t best = n;
+            for (size_t y = 0; y < (size_t)kNumXcds; ++y)
+                if (head[y] < q[y].size() && q[y][head[y]] < best) {
+                    best = q[y][head[y]];
+                    x = y;
+                }
+        }
+        out.push_back(get(q[x][head[x]++]));
+    }
+    return out;
+}
+
 template <class T>
 uint64_t put(std::vector<unsigned char>& buf, uint64_t off, const std::vector<T>& v)
 {
@@ -587,13 +613,14 @@ fia_status fia_get_workspace_size(const fia_tensor* query, const fia_tensor* key
         bi[(size_t)b].lkv = (int32_t)lkv[(size_t)b];
     }
     // Tiles of 128 query rows per (batch, head); padded layouts also cover
-    // the padding rows (written as zeros).  Longest-first order.
+    // the padding rows (written as zeros).  Longest-first order, with the
+    // tiles of one kv head kept on one XCD so that they share its L2.
     struct W { int64_t work; Tile t; };
     std::vector<W> tl;
     for (int64_t b = 0; b < B; ++b) {
         const int64_t rows = layout == LAYOUT_TND ? lq[(size_t)b] : gq.S;
-        for (int64_t q0 = 0; q0 < rows; q0 += kBlockM) {
-            const int64_t q1 = std::min<int64_t>(q0 + kBlockM, rows);
+        for (int64_t q0 = 0; q0 < rows; q0 += kBlockMDense) {
+            const int64_t q1 = std::min<int64_t>(q0 + kBlockMDense, rows);
             const int64_t w = kv_tiles_of(mode, mask != nullptr, a.pre, a.next, lq[(size_t)b],
                                           lkv[(size_t)b], q0, q1);
             for (int64_t h = 0; h < QN; ++h)
@@ -601,9 +628,8 @@ fia_status fia_get_workspace_size(const fia_tensor* query, const fia_tensor* key
         }
     }
     std::stable_sort(tl.begin(), tl.end(), [](const W& x, const W& y) { return x.work > y.work; });
-    std::vector<Tile> tiles;
-    tiles.reserve(tl.size());
-    for (auto& w : tl) tiles.push_back(w.t);
+    std::vector<Tile> tiles = xcd_order(tl.size(), [&](size_t i) { return tl[i].t; },
+                                        [&](size_t i) { return (int)((tl[i].t.h / (QN / KVN)) % kNumXcds); });
     if (tiles.size() > (size_t)INT32_MAX) return FIA_ERR_UNSUPPORTED;
     p->n_tiles = (int64_t)tiles.size();
     a.n_tiles = (int32_t)tiles.size();
@@ -794,8 +820,8 @@ fia_status bsa_get_workspace_size(const fia_tensor* query, const fia_tensor* key
         const int64_t rows = layout == LAYOUT_TND ? lq[(size_t)b] : gq.S;
         for (int64_t qb = 0; qb * X < rows; ++qb) {
             const int64_t bend = std::min<int64_t>((qb + 1) * X, rows);
-            for (int64_t q0 = qb * X; q0 < bend; q0 += kBlockM) {
-                const int64_t q1 = std::min<int64_t>(q0 + kBlockM, bend);
+            for (int64_t q0 = qb * X; q0 < bend; q0 += kBlockMSparse) {
+                const int64_t q1 = std::min<int64_t>(q0 + kBlockMSparse, bend);
                 for (int64_t h = 0; h < N1; ++h)
                     tiles.push_back(Tile{(int32_t)b, (int32_t)h, (int32_t)q0, (int32_t)q1});
             }
