@@ -13,9 +13,9 @@ namespace fia {
 enum Kind : int32_t { KIND_EMPTY = 0, KIND_PREFILL = 1, KIND_DECODE = 2, KIND_BSA = 3 };
 enum Layout : int32_t { LAYOUT_BNSD = 0, LAYOUT_BSND = 1, LAYOUT_TND = 2 };
 
-// Query rows per workgroup of the prefill and block-sparse kernels (4 waves
-// of 32 rows) and kv tokens per inner step.
-constexpr int kBlockMDense = 128;
+// Waves of a prefill workgroup (each 32 query rows of one head), query rows
+// per block-sparse workgroup (4 waves), and kv tokens per inner step.
+constexpr int kDenseWaves = 4;
 constexpr int kBlockMSparse = 128;
 constexpr int kBlockN = 64;
 // XCDs of one MI355X: workgroup i of a launch runs on XCD i % kNumXcds.
@@ -70,6 +70,7 @@ struct AttnArgs {
     int64_t pre, next;
     int32_t return_lse;
     int32_t n_tiles;
+    int32_t hg;                    // heads per dense workgroup (a divisor of G)
 };
 
 // Decode schedule.  A segment is (batch b, kv head, chunk of <= 16 query

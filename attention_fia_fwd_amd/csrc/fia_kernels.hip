@@ -228,8 +228,8 @@ __device__ __forceinline__ float vmax(float x, float y) { return __builtin_eleme
 // the contraction pairs each P value with its V row.  K and V tiles are
 // double buffered; the next tile's loads go out at the top of an iteration.
 // ---------------------------------------------------------------------------
-template <int DT, int DQK, int DV, int KIND>
-__global__ __launch_bounds__(256, 2) void attn_fwd(AttnArgs a)
+template <int DT, int DQK, int DV, int KIND, int NW, int NS>
+__global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd(AttnArgs a)
 {
     constexpr bool BSA = KIND == kSparse;
     constexpr int BN = kBlockN;            // 64 kv tokens per tile
@@ -240,8 +240,10 @@ __global__ __launch_bounds__(256, 2) void attn_fwd(AttnArgs a)
     constexpr int STAGE = KT + BN * DV;
     constexpr int NQ = DQK / 16;           // k-steps of S^T = K Q^T
     constexpr int NO = DV / 32;            // 32-row d tiles of O^T
-    constexpr int NKI = BN * DQK / 8 / 256; // K load instructions per wave per tile
-    constexpr int NVI = BN * VCH / 256;    // V load instructions per wave per tile
+    constexpr int NKI = BN * DQK / 8 / (64 * NW); // K load instructions per wave per tile
+    constexpr int NVI = BN * VCH / (64 * NW);     // V load instructions per wave per tile
+    static_assert(NKI * 64 * NW * 8 == BN * DQK && NVI * 64 * NW == BN * VCH, "tile split");
+    static_assert(NS >= 2 && NS <= 4, "stages");
     using O = Ops<DT>;
 
     extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
@@ -253,9 +255,13 @@ __global__ __launch_bounds__(256, 2) void attn_fwd(AttnArgs a)
     const int l32 = lane & 31;
     const int hh = lane >> 5;
 
+    // A workgroup covers hg heads of one GQA group (t.h ..) and 32 NW / hg
+    // rows (t.q0 .. t.q1); wave w takes head t.h + w % hg, rows
+    // t.q0 + 32 (w / hg) + (0..31).
+    const int hg = BSA ? 1 : a.hg;
     const Tile t = a.tiles[blockIdx.x];
     const BatchInfo bi = a.batch[t.b];
-    const int h = t.h;
+    const int h = t.h + w % hg;
     const int q0 = t.q0, q1 = t.q1;
     const int Lq = bi.lq, Lkv = bi.lkv;
     const int g = h / a.G;
@@ -270,7 +276,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd(AttnArgs a)
     // the explicit mask exists only in the kMasked instantiation
     const uint8_t* mbase = KIND == kMasked ? a.mask + (int64_t)t.b * a.mask_bstride : nullptr;
 
-    const int wr0 = q0 + 32 * w;           // first row of this wave
+    const int wr0 = q0 + 32 * (w / hg);    // first row of this wave
     const int row = wr0 + l32;             // this lane's query row
     const int wend = min(wr0 + 32, qend);  // rows < wend are computed
 
@@ -337,34 +343,36 @@ __global__ __launch_bounds__(256, 2) void attn_fwd(AttnArgs a)
     //      distinct 16-byte bank groups.
     //   V: row-major rows of DV; chunk c of row r sits at c ^ VSW (r & 3): the
     //      4-row groups of the transposed reads hit distinct bank groups.
+    // Instruction u of wave w fills slots 64 u' + lane, u' = NW u + w; the
+    // lane offsets do not depend on the tile (computed once).
+    auto k_off = [&](int up, int ln) -> int {   // element offset of K slot 64 u' + ln
+        const int sl = 64 * up + ln;
+        if (KROWS) {
+            const int r = sl >> 4;
+            return r * a.k_sS + 8 * ((sl & 15) ^ (r & 15));
+        }
+        const int r = (sl >> 3) & 63;
+        return r * a.k_sS + 64 * (sl >> 9) + 8 * ((sl & 7) ^ ((r >> 1) & 7));
+    };
+    auto v_off = [&](int up, int ln) -> int {   // element offset of V slot 64 u' + ln
+        const int sl = 64 * up + ln;
+        const int r = sl / VCH;
+        return r * a.v_sS + 8 * ((sl % VCH) ^ (VSW * (r & 3)));
+    };
+    uint32_t koff[NKI], voff[NVI];
+#pragma unroll
+    for (int u = 0; u < NKI; ++u) koff[u] = (uint32_t)k_off(NW * u + w, lane) * 2u;
+#pragma unroll
+    for (int u = 0; u < NVI; ++u) voff[u] = (uint32_t)v_off(NW * u + w, lane) * 2u;
     auto load_tile = [&](int c0, int buf) {
         const uint32_t ks = smem_lds + 2u * (uint32_t)(buf * STAGE);
         const uint32_t vs = ks + 2u * KT;
         const i32x4 kr = rows_rsrc(kp, c0, Lkv, a.k_sS, DQK);
         const i32x4 vr = rows_rsrc(vp, c0, Lkv, a.v_sS, DV);
 #pragma unroll
-        for (int u = 0; u < NKI; ++u) {
-            const int blk = 4 * u + w;
-            const int sl = 64 * blk + lane;
-            int r, col;
-            if (KROWS) {
-                r = sl >> 4;
-                col = 8 * ((sl & 15) ^ (r & 15));
-            } else {
-                const int pnl = sl >> 9;
-                r = (sl >> 3) & 63;
-                col = 64 * pnl + 8 * ((sl & 7) ^ ((r >> 1) & 7));
-            }
-            dma16(kr, ks + 1024u * blk, (uint32_t)(r * a.k_sS + col) * 2u);
-        }
+        for (int u = 0; u < NKI; ++u) dma16(kr, ks + 1024u * (NW * u + w), koff[u]);
 #pragma unroll
-        for (int u = 0; u < NVI; ++u) {
-            const int blk = 4 * u + w;
-            const int sl = 64 * blk + lane;
-            const int r = sl / VCH, pc = sl % VCH;
-            const int cc = pc ^ (VSW * (r & 3));
-            dma16(vr, vs + 1024u * blk, (uint32_t)(r * a.v_sS + 8 * cc) * 2u);
-        }
+        for (int u = 0; u < NVI; ++u) dma16(vr, vs + 1024u * (NW * u + w), voff[u]);
     };
 
     // per-lane LDS offsets of the MFMA operand reads
@@ -387,13 +395,22 @@ __global__ __launch_bounds__(256, 2) void attn_fwd(AttnArgs a)
     float m = -INFINITY, l = 0.f;
     const float lazy_raw = kLazy / c;
 
-    if (ntiles > 0) load_tile(tile_c0(0), 0);
+    // NS stages: tiles it + 1 .. it + NS - 2 stay in flight while tile it is
+    // computed; tile it + NS - 1 goes into the stage of tile it - 1.
+    constexpr int PER = NKI + NVI;         // load instructions per wave and tile
+#pragma unroll
+    for (int j = 0; j < NS - 1; ++j)
+        if (j < ntiles) load_tile(tile_c0(j), j);
     for (int it = 0; it < ntiles; ++it) {
-        const int buf = it & 1;
-        __builtin_amdgcn_s_waitcnt(0);     // this wave's loads of tile `it` landed
-        __syncthreads();                   // everyone's did; buffer buf^1 is free
+        const int buf = it % NS;
+        // this wave's loads of tile `it` landed: later tiles may be pending
+        const int later = min(NS - 2, ntiles - 1 - it);
+        if (NS >= 4 && later >= 2) __builtin_amdgcn_s_waitcnt(FIA_VMCNT(2 * PER));
+        else if (NS >= 3 && later >= 1) __builtin_amdgcn_s_waitcnt(FIA_VMCNT(PER));
+        else __builtin_amdgcn_s_waitcnt(FIA_VMCNT(0));
+        __syncthreads();                   // everyone's did; stage of tile it - 1 is free
         const int c0 = tile_c0(it);
-        if (it + 1 < ntiles) load_tile(tile_c0(it + 1), buf ^ 1);
+        if (it + NS - 1 < ntiles) load_tile(tile_c0(it + NS - 1), (it + NS - 1) % NS);
 
         // Which part of this tile the wave's rows may see.
         bool skip = wend <= wr0 || c0 >= Lkv;
@@ -893,11 +910,16 @@ void raise_lds_limit(K kernel, size_t lds, bool& configured)
 template <int DT, int DQK, int DV, int KIND>
 int launch_attn(const fia_plan& p, const AttnArgs& a, hipStream_t stream)
 {
-    const size_t lds = 2 * (size_t)kBlockN * (DQK + DV) * sizeof(uint16_t);
+    // 4 waves, two workgroups per CU, K/V double buffered (measured faster
+    // than 8-wave workgroups with deeper LDS pipelines)
+    constexpr int NW = kDenseWaves;
+    constexpr int NS = 2;
+    const size_t lds = (size_t)NS * kBlockN * (DQK + DV) * sizeof(uint16_t);
     static bool configured = false;
-    raise_lds_limit(attn_fwd<DT, DQK, DV, KIND>, lds, configured);
+    raise_lds_limit(attn_fwd<DT, DQK, DV, KIND, NW, NS>, lds, configured);
     if (p.n_tiles == 0) return 0;
-    hipLaunchKernelGGL((attn_fwd<DT, DQK, DV, KIND>), dim3((unsigned)p.n_tiles), dim3(256), lds, stream, a);
+    hipLaunchKernelGGL((attn_fwd<DT, DQK, DV, KIND, NW, NS>), dim3((unsigned)p.n_tiles), dim3(NW * 64), lds,
+                       stream, a);
     return (int)hipGetLastError();
 }
 

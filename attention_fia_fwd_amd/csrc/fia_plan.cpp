@@ -612,18 +612,25 @@ fia_status fia_get_workspace_size(const fia_tensor* query, const fia_tensor* key
         bi[(size_t)b].lq = (int32_t)lq[(size_t)b];
         bi[(size_t)b].lkv = (int32_t)lkv[(size_t)b];
     }
-    // Tiles of 128 query rows per (batch, head); padded layouts also cover
-    // the padding rows (written as zeros).  Longest-first order, with the
-    // tiles of one kv head kept on one XCD so that they share its L2.
+    // A workgroup covers hg heads of one GQA group (hg the largest power of
+    // two dividing G, at most kDenseWaves) and 32 kDenseWaves / hg query
+    // rows: the heads share every K/V tile.  Padded layouts also cover the
+    // padding rows (written as zeros).  Longest-first order, with the tiles
+    // of one kv head kept on one XCD so that they share its L2.
+    const int64_t G = QN / KVN;
+    int64_t hg = 1;
+    while (hg < kDenseWaves && G % (2 * hg) == 0) hg *= 2;
+    a.hg = (int32_t)hg;
+    const int64_t rows_per = 32 * kDenseWaves / hg;
     struct W { int64_t work; Tile t; };
     std::vector<W> tl;
     for (int64_t b = 0; b < B; ++b) {
         const int64_t rows = layout == LAYOUT_TND ? lq[(size_t)b] : gq.S;
-        for (int64_t q0 = 0; q0 < rows; q0 += kBlockMDense) {
-            const int64_t q1 = std::min<int64_t>(q0 + kBlockMDense, rows);
+        for (int64_t q0 = 0; q0 < rows; q0 += rows_per) {
+            const int64_t q1 = std::min<int64_t>(q0 + rows_per, rows);
             const int64_t w = kv_tiles_of(mode, mask != nullptr, a.pre, a.next, lq[(size_t)b],
                                           lkv[(size_t)b], q0, q1);
-            for (int64_t h = 0; h < QN; ++h)
+            for (int64_t h = 0; h < QN; h += hg)
                 tl.push_back({w, Tile{(int32_t)b, (int32_t)h, (int32_t)q0, (int32_t)q1}});
         }
     }
@@ -780,6 +787,7 @@ fia_status bsa_get_workspace_size(const fia_tensor* query, const fia_tensor* key
     a.QN = (int32_t)N1;
     a.KVN = (int32_t)N2;
     a.G = (int32_t)(N1 / N2);
+    a.hg = 1;
     a.scale_log2 = (float)(prm->scale_value * kLog2e);
     a.nqb = (int32_t)nqb;
     a.nkb = (int32_t)nkb;
