@@ -59,6 +59,26 @@ def test_prefill_head_dims_and_gqa(D):
     check_fia(case)
 
 
+@pytest.mark.parametrize("QN,KVN", [(24, 8), (12, 2), (16, 2), (32, 2)])
+@pytest.mark.parametrize("mode", [3, 4])
+def test_prefill_gqa_head_groups(QN, KVN, mode):
+    # G = 3, 6, 8, 16: workgroups pack 1, 2, 4, 4 heads of a GQA group with
+    # 128, 64, 32, 32 rows each; lengths cut through those row blocks
+    case = W.make_fia(f"prefill_g{QN // KVN}_m{mode}", layout="BSND", dtype=torch.bfloat16, B=2,
+                      QN=QN, KVN=KVN, Sq=290, Skv=310, Dqk=128, sparse_mode=mode, pre_tokens=100,
+                      next_tokens=20, lq=[290, 97], lkv=[310, 131], mask_kind="template",
+                      seed=130 + QN + mode)
+    check_fia(case)
+
+
+def test_prefill_gqa_explicit_mask():
+    # the masked instantiation with 4 heads per workgroup
+    case = W.make_fia("prefill_g8_mask", layout="BNSD", dtype=torch.float16, B=2, QN=16, KVN=2,
+                      Sq=150, Skv=170, Dqk=64, sparse_mode=0, pre_tokens=60, next_tokens=10,
+                      lq=[150, 77], lkv=[170, 90], mask_kind="random", seed=141)
+    check_fia(case)
+
+
 def test_prefill_tnd_192_128():
     L = [200, 1, 64, 129, 511]
     case = W.make_fia("prefill_tnd_192", layout="TND", dtype=torch.bfloat16, B=5, QN=4, KVN=4,
