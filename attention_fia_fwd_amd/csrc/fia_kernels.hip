@@ -441,21 +441,32 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd(AttnArgs a)
         f32x16 s0, s1;
 #pragma unroll
         for (int r = 0; r < 16; ++r) s0[r] = s1[r] = 0.f;
-#pragma unroll
-        for (int s = 0; s < NQ; ++s) {
-            uint4 ka0, ka1;
+        // The K operands are read two k-steps ahead of the MFMAs that use
+        // them; the scheduling barriers keep the compiler from moving each
+        // read back next to its MFMA, which would expose the LDS latency at
+        // every k-step.
+        constexpr int KPD = NQ < 2 ? NQ : 2;
+        uint4 ka0[NQ], ka1[NQ];
+        auto read_k = [&](int s) {
             if (KROWS) {
                 const int ch = 2 * s + hh;
-                ka0 = *(const uint4*)(ks + krow0 * DQK + 8 * (ch ^ kx0));
-                ka1 = *(const uint4*)(ks + krow1 * DQK + 8 * (ch ^ kx1));
+                ka0[s] = *(const uint4*)(ks + krow0 * DQK + 8 * (ch ^ kx0));
+                ka1[s] = *(const uint4*)(ks + krow1 * DQK + 8 * (ch ^ kx1));
             } else {
                 const int ch = 2 * (s & 3) + hh;
                 const uint16_t* pn = ks + (s >> 2) * (BN * 64);
-                ka0 = *(const uint4*)(pn + krow0 * 64 + 8 * (ch ^ kx0));
-                ka1 = *(const uint4*)(pn + krow1 * 64 + 8 * (ch ^ kx1));
+                ka0[s] = *(const uint4*)(pn + krow0 * 64 + 8 * (ch ^ kx0));
+                ka1[s] = *(const uint4*)(pn + krow1 * 64 + 8 * (ch ^ kx1));
             }
-            s0 = O::mma32(ka0, qf[s], s0);
-            s1 = O::mma32(ka1, qf[s], s1);
+        };
+#pragma unroll
+        for (int s = 0; s < KPD; ++s) read_k(s);
+#pragma unroll
+        for (int s = 0; s < NQ; ++s) {
+            if (s + KPD < NQ) read_k(s + KPD);
+            s0 = O::mma32(ka0[s], qf[s], s0);
+            s1 = O::mma32(ka1[s], qf[s], s1);
+            __builtin_amdgcn_sched_barrier(0);
         }
 
         // element mask (boundary tiles only): accumulator r holds kv index
