@@ -401,6 +401,38 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd(AttnArgs a)
 #pragma unroll
     for (int j = 0; j < NS - 1; ++j)
         if (j < ntiles) load_tile(tile_c0(j), j);
+    // Allowed keys of row r form the band r + lo_off <= j <= r + hi_off
+    // (besides j < Lkv and the explicit mask), with +-2^30 for an open side;
+    // fixed per wave, so each tile is classified with a few comparisons.
+    int lo_off = -(1 << 30), hi_off = 1 << 30;
+    bool allow_full = true;                // false: every tile takes the element mask
+    if (!BSA) {
+        int64_t lo = lo_off, hi = hi_off;
+        switch (mode) {
+        case 0:
+            if (mbase) { lo = -(int64_t)pre; hi = next; allow_full = false; }
+            break;
+        case 1: allow_full = false; break;
+        case 2: hi = 0; break;
+        case 3: hi = delta; break;
+        case 4: lo = (int64_t)delta - pre; hi = (int64_t)delta + next; break;
+        default: break;
+        }
+        lo_off = (int)max<int64_t>(-(1 << 30), min<int64_t>(1 << 30, lo));
+        hi_off = (int)max<int64_t>(-(1 << 30), min<int64_t>(1 << 30, hi));
+    }
+    // The same conditions as thresholds on the tile start c0 (last key
+    // cl = c0 + BN - 1) for the wave's rows [wr0, wend - 1]:
+    //   skip <=> c0 < tlo_skip (cl < wr0 + lo_off)  or  c0 > thi_skip
+    //            (c0 > wend - 1 + hi_off, or c0 >= Lkv), or no rows;
+    //   full <=> tlo_full <= c0 <= thi_full (c0 >= wend - 1 + lo_off,
+    //            cl <= wr0 + hi_off, c0 + BN <= Lkv, 32 rows, no mask).
+    auto clamp32 = [](int64_t x) -> int { return (int)max<int64_t>(INT32_MIN, min<int64_t>(INT32_MAX, x)); };
+    const int tlo_skip = wend <= wr0 ? INT32_MAX : clamp32((int64_t)wr0 + lo_off - BN + 1);
+    const int thi_skip = clamp32(min<int64_t>(Lkv - 1, (int64_t)wend - 1 + hi_off));
+    const int tlo_full = allow_full && wend - wr0 == 32 ? clamp32((int64_t)wend - 1 + lo_off) : INT32_MAX;
+    const int thi_full = clamp32(min<int64_t>((int64_t)Lkv - BN, (int64_t)wr0 + hi_off - BN + 1));
+
     for (int it = 0; it < ntiles; ++it) {
         const int buf = it % NS;
         // this wave's loads of tile `it` landed: later tiles may be pending
@@ -412,28 +444,10 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd(AttnArgs a)
         const int c0 = tile_c0(it);
         if (it + NS - 1 < ntiles) load_tile(tile_c0(it + NS - 1), (it + NS - 1) % NS);
 
-        // Which part of this tile the wave's rows may see.
-        bool skip = wend <= wr0 || c0 >= Lkv;
-        bool full = !skip && (c0 + BN <= Lkv) && (wend - wr0 == 32);
-        if (!BSA && !skip) {
-            const int r0 = wr0, r1 = wend - 1, cl = c0 + BN - 1;
-            switch (mode) {
-            case 0:
-                if (mbase) {
-                    full = false;
-                    skip = cl < r0 - pre || c0 > r1 + next;
-                }
-                break;
-            case 1: full = false; break;
-            case 2: skip = c0 > r1; full = full && cl <= r0; break;
-            case 3: skip = c0 > r1 + delta; full = full && cl <= r0 + delta; break;
-            case 4:
-                skip = cl < r0 + delta - pre || c0 > r1 + delta + next;
-                full = full && c0 >= r1 + delta - pre && cl <= r0 + delta + next;
-                break;
-            default: break;
-            }
-        }
+        // Which part of this tile the wave's rows may see: none (skip), all
+        // (full), or some (element mask).
+        const bool skip = c0 < tlo_skip || c0 > thi_skip;
+        const bool full = c0 >= tlo_full && c0 <= thi_full;
         if (skip) continue;
 
         const uint16_t* ks = smem + buf * STAGE;
@@ -475,19 +489,8 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd(AttnArgs a)
         // explicit mask in modes 0/1.
         if (!full) {
             const int base = c0 + 4 * hh;
-            int jlo = -base, jhi = Lkv - 1 - base;
-            if (row >= qend) jhi = -1;
-            if (!BSA) {
-                if (mode == 2) jhi = min(jhi, row - base);
-                else if (mode == 3) jhi = min(jhi, row + delta - base);
-                else if (mode == 4) {
-                    jlo = max(jlo, row + delta - pre - base);
-                    jhi = min(jhi, row + delta + next - base);
-                } else if (mode == 0 && mbase) {
-                    jlo = max(jlo, row - pre - base);
-                    jhi = min(jhi, row + next - base);
-                }
-            }
+            const int jlo = (int)max<int64_t>(-base, (int64_t)row + lo_off - base);
+            const int jhi = row >= qend ? -1 : (int)min<int64_t>(Lkv - 1 - base, (int64_t)row + hi_off - base);
             const uint8_t* mrow =
                 (!BSA && mbase && row < qend) ? mbase + (int64_t)row * a.mask_rstride + base : nullptr;
 #pragma unroll
@@ -503,10 +506,17 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd(AttnArgs a)
             }
         }
 
-        // row max over the tile (raw score units; c > 0)
-        float mt = vmax(s0[0], s1[0]);
+        // row max over the tile (raw score units; c > 0): four independent
+        // three-input chains, then their combination (short dependency path)
+        float mq[4];
 #pragma unroll
-        for (int r = 1; r < 16; ++r) mt = vmax(mt, vmax(s0[r], s1[r]));
+        for (int q = 0; q < 4; ++q) {
+            mq[q] = vmax(s0[4 * q], vmax(s0[4 * q + 1], s1[4 * q]));
+            mq[q] = vmax(mq[q], vmax(s0[4 * q + 2], s1[4 * q + 1]));
+            mq[q] = vmax(mq[q], vmax(s0[4 * q + 3], s1[4 * q + 2]));
+            mq[q] = vmax(mq[q], s1[4 * q + 3]);
+        }
+        float mt = vmax(vmax(mq[0], vmax(mq[1], mq[2])), mq[3]);
         mt = other_half_max(mt);
         const float mn = fmaxf(m, mt);
         const bool grow = (m == -INFINITY) ? (mn > -INFINITY) : (mn > m + lazy_raw);
