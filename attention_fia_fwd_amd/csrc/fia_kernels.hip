@@ -261,6 +261,28 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd(AttnArgs a)
     const int hg = BSA ? 1 : a.hg;
     const Tile t = a.tiles[blockIdx.x];
     const BatchInfo bi = a.batch[t.b];
+    if (!BSA && t.h < 0) {
+        // zero fill: padding rows [t.q0, t.q1) of batch t.b, every head
+        const BatchInfo& zb = bi;
+        constexpr int CH = DV / 8;         // 16-byte chunks per (row, head)
+        const int nrow = t.q1 - t.q0, QN = a.QN;
+        const bool head_inner = a.o_sH == DV;   // heads adjacent in memory (BSND, BSH)
+        uint16_t* ob = (uint16_t*)a.o + zb.q_row0 * a.o_rowmul;
+        for (int e = tid; e < nrow * QN * CH; e += NW * 64) {
+            const int ch = e % CH, rest = e / CH;
+            const int r = head_inner ? rest / QN : rest % nrow;
+            const int hd = head_inner ? rest % QN : rest / nrow;
+            *(uint4*)(ob + (int64_t)hd * a.o_sH + (int64_t)(t.q0 + r) * a.o_sS + 8 * ch) = make_uint4(0, 0, 0, 0);
+        }
+        if (a.return_lse) {
+            float* lb = a.lse + zb.q_row0 * a.lse_rowmul;
+            for (int e = tid; e < nrow * QN; e += NW * 64) {
+                const int r = e % nrow, hd = e / nrow;
+                lb[(int64_t)hd * a.lse_sH + (int64_t)(t.q0 + r) * a.lse_sS] = INFINITY;
+            }
+        }
+        return;
+    }
     const int h = t.h + w % hg;
     const int q0 = t.q0, q1 = t.q1;
     const int Lq = bi.lq, Lkv = bi.lkv;

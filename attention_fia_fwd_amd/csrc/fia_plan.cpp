@@ -163,7 +163,7 @@ int64_t kv_tiles_of(int32_t mode, bool has_mask, int64_t pre, int64_t next, int6
 // i % kNumXcds, so position i takes the first remaining tile that prefers
 // that XCD; when none is left, the first remaining tile of any XCD.
 template <class Get, class Pref>
-std::vector<Tile> xcd_order(size_t n, Get get, Pref pref)
+std::vector<Tile> xcd_order(size_t n, Get get, Pref pref, size_t first_pos = 0)
 {
     std::vector<std::vector<size_t>> q((size_t)kNumXcds);
     for (size_t i = 0; i < n; ++i) q[(size_t)pref(i)].push_back(i);
@@ -171,7 +171,7 @@ std::vector<Tile> xcd_order(size_t n, Get get, Pref pref)
     std::vector<Tile> out;
     out.reserve(n);
     for (size_t pos = 0; pos < n; ++pos) {
-        size_t x = pos % (size_t)kNumXcds;
+        size_t x = (first_pos + pos) % (size_t)kNumXcds;
         if (head[x] == q[x].size()) {
             size_t best = n;
             for (size_t y = 0; y < (size_t)kNumXcds; ++y)
@@ -614,9 +614,12 @@ fia_status fia_get_workspace_size(const fia_tensor* query, const fia_tensor* key
     }
     // A workgroup covers hg heads of one GQA group (hg the largest power of
     // two dividing G, at most kDenseWaves) and 32 kDenseWaves / hg query
-    // rows: the heads share every K/V tile.  Padded layouts also cover the
-    // padding rows (written as zeros).  Longest-first order, with the tiles
-    // of one kv head kept on one XCD so that they share its L2.
+    // rows: the heads share every K/V tile.  Longest-first order, with the
+    // tiles of one kv head kept on one XCD so that they share its L2.
+    // Padded layouts: the rows past the last row block that holds a valid
+    // query row are written (out = 0, lse = +inf) by zero-fill workgroups of
+    // about 256 KB of output each over all heads (h = -1 marks them); they
+    // go first, where their stores overlap the MFMA-bound workgroups.
     const int64_t G = QN / KVN;
     int64_t hg = 1;
     while (hg < kDenseWaves && G % (2 * hg) == 0) hg *= 2;
@@ -624,9 +627,14 @@ fia_status fia_get_workspace_size(const fia_tensor* query, const fia_tensor* key
     const int64_t rows_per = 32 * kDenseWaves / hg;
     struct W { int64_t work; Tile t; };
     std::vector<W> tl;
+    std::vector<Tile> zero_fill;
+    const int64_t zrows = std::max<int64_t>(1, ((int64_t)256 << 10) / (QN * Dv * 2));
     for (int64_t b = 0; b < B; ++b) {
         const int64_t rows = layout == LAYOUT_TND ? lq[(size_t)b] : gq.S;
-        for (int64_t q0 = 0; q0 < rows; q0 += rows_per) {
+        const int64_t zfrom = std::min(rows, (lq[(size_t)b] + rows_per - 1) / rows_per * rows_per);
+        for (int64_t z0 = zfrom; z0 < rows; z0 += zrows)
+            zero_fill.push_back(Tile{(int32_t)b, -1, (int32_t)z0, (int32_t)std::min(z0 + zrows, rows)});
+        for (int64_t q0 = 0; q0 < zfrom; q0 += rows_per) {
             const int64_t q1 = std::min<int64_t>(q0 + rows_per, rows);
             const int64_t w = kv_tiles_of(mode, mask != nullptr, a.pre, a.next, lq[(size_t)b],
                                           lkv[(size_t)b], q0, q1);
@@ -635,8 +643,11 @@ fia_status fia_get_workspace_size(const fia_tensor* query, const fia_tensor* key
         }
     }
     std::stable_sort(tl.begin(), tl.end(), [](const W& x, const W& y) { return x.work > y.work; });
-    std::vector<Tile> tiles = xcd_order(tl.size(), [&](size_t i) { return tl[i].t; },
-                                        [&](size_t i) { return (int)((tl[i].t.h / (QN / KVN)) % kNumXcds); });
+    std::vector<Tile> tiles = zero_fill;
+    const std::vector<Tile> ordered =
+        xcd_order(tl.size(), [&](size_t i) { return tl[i].t; },
+                  [&](size_t i) { return (int)((tl[i].t.h / (QN / KVN)) % kNumXcds); }, zero_fill.size());
+    tiles.insert(tiles.end(), ordered.begin(), ordered.end());
     if (tiles.size() > (size_t)INT32_MAX) return FIA_ERR_UNSUPPORTED;
     p->n_tiles = (int64_t)tiles.size();
     a.n_tiles = (int32_t)tiles.size();

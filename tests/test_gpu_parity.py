@@ -79,6 +79,57 @@ def test_prefill_gqa_explicit_mask():
     check_fia(case)
 
 
+def _repeat_runs(case, plan, rows, ref_o, ref_l, runs=3):
+    # The prefill and block-sparse workgroups are persistent and take their
+    # tiles from a queue held by the plan, which the last workgroup of a run
+    # resets: every run must compute every tile again.  Outputs are filled
+    # with NaN before each run; each run must match the oracle on the sampled
+    # rows and reproduce the first run bit for bit.
+    first = None
+    for rep in range(runs):
+        plan.out.fill_(float("nan"))
+        if plan.lse is not None:
+            plan.lse.fill_(float("nan"))
+        out, lse = run(plan)
+        assert not torch.isnan(out.float()).any(), f"run {rep}: tiles left unwritten"
+        assert lse is None or not torch.isnan(lse).any(), f"run {rep}: lse left unwritten"
+        if first is None:
+            go, gl = gather_rows(case, out, lse, rows)
+            err = float(np.max(np.abs(go - ref_o)))
+            lerr = float(np.max(np.abs(gl - ref_l)))
+            say(f"[repeat] {case.name}: max out err {err:.3e}, max lse err {lerr:.3e}")
+            assert err <= TOL_OUT[case.dtype] and lerr <= TOL_LSE
+            first = (out.clone(), None if lse is None else lse.clone())
+        else:
+            assert torch.equal(out, first[0]), f"run {rep} differs from the first"
+            assert lse is None or torch.equal(lse, first[1])
+
+
+def test_prefill_repeated_runs_of_one_plan():
+    # 2 x 8 kv heads x 64 row blocks = 1024 tiles: more than the resident
+    # workgroups, so queues run dry and workgroups steal from other XCDs
+    case = W.make_fia("prefill_repeat", layout="BSND", dtype=torch.bfloat16, B=2, QN=32, KVN=8,
+                      Sq=2048, Dqk=128, sparse_mode=3, lq=[2048, 1500], lkv=[2048, 1500], seed=150)
+    say(f"[repeat] {case.name}")
+    rows = sample_rows(case, 48, seed=5)
+    ref_o, ref_l = oracle.attention(case, rows=rows)
+    to_dev(case)
+    plan = fia_plan(case)
+    _repeat_runs(case, plan, rows, ref_o, ref_l)
+    plan.close()
+
+
+def test_bsa_repeated_runs_of_one_plan():
+    case = W.make_bsa("bsa_repeat", layout="BNSD", B=1, QN=16, KVN=4, Sq=8192, D=128, X=128, Y=128,
+                      p=0.1, seed=151, device="cuda")
+    say(f"[repeat] {case.name}")
+    rows = sample_rows(case, 48, seed=6)
+    ref_o, ref_l = oracle.block_sparse(case, rows=rows)
+    plan = bsa_plan(case)
+    _repeat_runs(case, plan, rows, ref_o, ref_l)
+    plan.close()
+
+
 def test_prefill_tnd_192_128():
     L = [200, 1, 64, 129, 511]
     case = W.make_fia("prefill_tnd_192", layout="TND", dtype=torch.bfloat16, B=5, QN=4, KVN=4,
