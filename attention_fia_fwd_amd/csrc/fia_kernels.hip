@@ -351,8 +351,23 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd(AttnArgs a)
             ntiles = (hi - kv_lo + BN - 1) / BN;
         }
     }
+    // Block-sparse: 64 entries of the row's block list live in one register
+    // per lane (lane l: entry bsa_cb + l) and each tile's block comes from
+    // v_readlane, so no scalar load sits between a tile and its loads.  The
+    // window is reloaded when an index passes its end; it starts NS entries
+    // behind the index that moved it (the current tile is asked for after
+    // the next one).
+    int bsa_cb = 0, bsa_bc = 0;
+    if (BSA && ntiles > 0) bsa_bc = lane < a.nkb ? blist[lane] : 0;
     auto tile_c0 = [&](int it) -> int {
-        if (BSA) return blist[it / per] * a.by + BN * (it % per);
+        if (BSA) {
+            const int idx = it / per;
+            if (idx >= bsa_cb + 64) {
+                bsa_cb = idx - NS;
+                bsa_bc = bsa_cb + lane < a.nkb ? blist[bsa_cb + lane] : 0;
+            }
+            return __builtin_amdgcn_readlane(bsa_bc, idx - bsa_cb) * a.by + BN * (it % per);
+        }
         return kv_lo + BN * it;
     };
 
