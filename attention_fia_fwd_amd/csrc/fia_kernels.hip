@@ -172,6 +172,33 @@ __device__ __forceinline__ void dma16(i32x4 rs, uint32_t lds_wave, uint32_t voff
                  : "=&s"(keep) : "s"(m0v), "v"(voff), "s"(rs) : "memory");
 }
 
+// N (2 or 4) such loads with one M0 value: load u writes LDS lds_base +
+// 1024 u + 16 lane and reads voff[u] + 1024 u (the instruction offset
+// applies to both addresses), so the callers pass offsets reduced by 1024 u.
+// Fewer M0 writes between queued LDS loads stall the issuing wave less.
+template <int N>
+__device__ __forceinline__ void dma16_burst(i32x4 rs, uint32_t lds_base, const uint32_t* voff)
+{
+    static_assert(N == 2 || N == 4, "burst of 2 or 4");
+    const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_base);
+    uint32_t keep;
+    if (N == 2)
+        asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
+                     "buffer_load_dwordx4 %2, %4, 0 offen lds\n\t"
+                     "buffer_load_dwordx4 %3, %4, 0 offen offset:1024 lds\n\t"
+                     "s_mov_b32 m0, %0"
+                     : "=&s"(keep) : "s"(m0v), "v"(voff[0]), "v"(voff[1]), "s"(rs) : "memory");
+    else
+        asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
+                     "buffer_load_dwordx4 %2, %6, 0 offen lds\n\t"
+                     "buffer_load_dwordx4 %3, %6, 0 offen offset:1024 lds\n\t"
+                     "buffer_load_dwordx4 %4, %6, 0 offen offset:2048 lds\n\t"
+                     "buffer_load_dwordx4 %5, %6, 0 offen offset:3072 lds\n\t"
+                     "s_mov_b32 m0, %0"
+                     : "=&s"(keep)
+                     : "s"(m0v), "v"(voff[0]), "v"(voff[1]), "v"(voff[2]), "v"(voff[3]), "s"(rs) : "memory");
+}
+
 // The same resource moved `d` bytes further (fewer valid bytes, never < 0);
 // offsets past the valid range still read as zero.
 __device__ __forceinline__ i32x4 rsrc_advance(i32x4 r, uint32_t d)
@@ -396,20 +423,38 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd(AttnArgs a)
         const int r = sl / VCH;
         return r * a.v_sS + 8 * ((sl % VCH) ^ (VSW * (r & 3)));
     };
+    // Load bursts: wave w fills the consecutive slots NKI w .. NKI w + NKI - 1
+    // (NVI w .. for V) with one M0 value per burst.  The reduced offsets
+    // off(slot) - 1024 u stay >= 0: slot NKI w + u starts at least 4u rows
+    // into the tile (rows of >= 128 elements apart) for D = 64, 128 and for
+    // V; the D_qk = 192 panels do not guarantee that, so K there takes one
+    // M0 per load (slot NW u + w).
+    constexpr bool KB = DQK != 192 && (NKI == 2 || NKI == 4);
+    constexpr bool VB = NVI == 2 || NVI == 4;
     uint32_t koff[NKI], voff[NVI];
 #pragma unroll
-    for (int u = 0; u < NKI; ++u) koff[u] = (uint32_t)k_off(NW * u + w, lane) * 2u;
+    for (int u = 0; u < NKI; ++u)
+        koff[u] = KB ? (uint32_t)k_off(NKI * w + u, lane) * 2u - 1024u * u : (uint32_t)k_off(NW * u + w, lane) * 2u;
 #pragma unroll
-    for (int u = 0; u < NVI; ++u) voff[u] = (uint32_t)v_off(NW * u + w, lane) * 2u;
+    for (int u = 0; u < NVI; ++u)
+        voff[u] = VB ? (uint32_t)v_off(NVI * w + u, lane) * 2u - 1024u * u : (uint32_t)v_off(NW * u + w, lane) * 2u;
     auto load_tile = [&](int c0, int buf) {
         const uint32_t ks = smem_lds + 2u * (uint32_t)(buf * STAGE);
         const uint32_t vs = ks + 2u * KT;
         const i32x4 kr = rows_rsrc(kp, c0, Lkv, a.k_sS, DQK);
         const i32x4 vr = rows_rsrc(vp, c0, Lkv, a.v_sS, DV);
+        if constexpr (KB) {
+            dma16_burst<NKI>(kr, ks + 1024u * (NKI * w), koff);
+        } else {
 #pragma unroll
-        for (int u = 0; u < NKI; ++u) dma16(kr, ks + 1024u * (NW * u + w), koff[u]);
+            for (int u = 0; u < NKI; ++u) dma16(kr, ks + 1024u * (NW * u + w), koff[u]);
+        }
+        if constexpr (VB) {
+            dma16_burst<NVI>(vr, vs + 1024u * (NVI * w), voff);
+        } else {
 #pragma unroll
-        for (int u = 0; u < NVI; ++u) dma16(vr, vs + 1024u * (NW * u + w), voff[u]);
+            for (int u = 0; u < NVI; ++u) dma16(vr, vs + 1024u * (NW * u + w), voff[u]);
+        }
     };
 
     // per-lane LDS offsets of the MFMA operand reads
