@@ -71,6 +71,14 @@ struct AttnArgs {
     int32_t return_lse;
     int32_t n_tiles;
     int32_t hg;                    // heads per dense workgroup (a divisor of G)
+    // paged K/V (prefill): kv token j of batch b is row j % block_size of
+    // pool block block_table[b][j / block_size]; k/v_sH and k/v_sS are then
+    // the pool's head and token strides and p_blk its block stride
+    const int32_t* block_table;
+    int64_t bt_stride;
+    int64_t p_blk;
+    int32_t block_size;            // a multiple of 64 (tiles never cross a block)
+    int32_t paged;
 };
 
 // Decode schedule.  A segment is (batch b, kv head, chunk of <= 16 query

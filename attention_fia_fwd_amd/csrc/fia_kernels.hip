@@ -255,7 +255,7 @@ __device__ __forceinline__ float vmax(float x, float y) { return __builtin_eleme
 // the contraction pairs each P value with its V row.  K and V tiles are
 // double buffered; the next tile's loads go out at the top of an iteration.
 // ---------------------------------------------------------------------------
-template <int DT, int DQK, int DV, int KIND, int NW, int NS>
+template <int DT, int DQK, int DV, int KIND, int NW, int NS, bool PG>
 __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd(AttnArgs a)
 {
     constexpr bool BSA = KIND == kSparse;
@@ -438,11 +438,36 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd(AttnArgs a)
 #pragma unroll
     for (int u = 0; u < NVI; ++u)
         voff[u] = VB ? (uint32_t)v_off(NVI * w + u, lane) * 2u - 1024u * u : (uint32_t)v_off(NW * u + w, lane) * 2u;
+    // Paged K/V: a tile lies inside one pool block (block_size % 64 == 0).
+    // 64 consecutive block-table entries of the batch live in one register
+    // per lane (lane l: entry pg_cb + l) and each tile's block id comes from
+    // v_readlane; tiles are loaded in ascending order, so the window only
+    // moves forward.  Entries at or past ceil(Lkv / block_size) are never
+    // read.
+    const int32_t* bt = PG ? a.block_table + (int64_t)t.b * a.bt_stride : nullptr;
+    const int npages = PG ? (Lkv + a.block_size - 1) / a.block_size : 0;
+    int pg_cb = PG ? kv_lo / a.block_size : 0;
+    int pg_bc = 0;
+    if (PG && ntiles > 0) pg_bc = pg_cb + lane < npages ? bt[pg_cb + lane] : 0;
     auto load_tile = [&](int c0, int buf) {
         const uint32_t ks = smem_lds + 2u * (uint32_t)(buf * STAGE);
         const uint32_t vs = ks + 2u * KT;
-        const i32x4 kr = rows_rsrc(kp, c0, Lkv, a.k_sS, DQK);
-        const i32x4 vr = rows_rsrc(vp, c0, Lkv, a.v_sS, DV);
+        i32x4 kr, vr;
+        if constexpr (PG) {
+            const int pi = c0 / a.block_size;
+            if (pi >= pg_cb + 64) {
+                pg_cb = pi;
+                pg_bc = pg_cb + lane < npages ? bt[pg_cb + lane] : 0;
+            }
+            const int64_t blk = __builtin_amdgcn_readlane(pg_bc, pi - pg_cb);
+            const int r0 = c0 - pi * a.block_size;          // row of the tile in its block
+            const int r1 = r0 + min(Lkv - c0, BN);           // rows past Lkv read as zero
+            kr = rows_rsrc(kp + blk * a.p_blk, r0, r1, a.k_sS, DQK);
+            vr = rows_rsrc(vp + blk * a.p_blk, r0, r1, a.v_sS, DV);
+        } else {
+            kr = rows_rsrc(kp, c0, Lkv, a.k_sS, DQK);
+            vr = rows_rsrc(vp, c0, Lkv, a.v_sS, DV);
+        }
         if constexpr (KB) {
             dma16_burst<NKI>(kr, ks + 1024u * (NKI * w), koff);
         } else {
@@ -1010,7 +1035,7 @@ void raise_lds_limit(K kernel, size_t lds, bool& configured)
     }
 }
 
-template <int DT, int DQK, int DV, int KIND>
+template <int DT, int DQK, int DV, int KIND, bool PG = false>
 int launch_attn(const fia_plan& p, const AttnArgs& a, hipStream_t stream)
 {
     // 4 waves, two workgroups per CU, K/V double buffered (measured faster
@@ -1019,10 +1044,10 @@ int launch_attn(const fia_plan& p, const AttnArgs& a, hipStream_t stream)
     constexpr int NS = 2;
     const size_t lds = (size_t)NS * kBlockN * (DQK + DV) * sizeof(uint16_t);
     static bool configured = false;
-    raise_lds_limit(attn_fwd<DT, DQK, DV, KIND, NW, NS>, lds, configured);
+    raise_lds_limit(attn_fwd<DT, DQK, DV, KIND, NW, NS, PG>, lds, configured);
     if (p.n_tiles == 0) return 0;
-    hipLaunchKernelGGL((attn_fwd<DT, DQK, DV, KIND, NW, NS>), dim3((unsigned)p.n_tiles), dim3(NW * 64), lds,
-                       stream, a);
+    hipLaunchKernelGGL((attn_fwd<DT, DQK, DV, KIND, NW, NS, PG>), dim3((unsigned)p.n_tiles), dim3(NW * 64),
+                       lds, stream, a);
     return (int)hipGetLastError();
 }
 
@@ -1042,6 +1067,9 @@ int launch_dec(const fia_plan& p, const DecodeArgs& a, hipStream_t stream)
 template <int DT, int DQK, int DV>
 int launch_prefill_kind(const fia_plan& p, const AttnArgs& a, hipStream_t s)
 {
+    if (a.paged)
+        return a.has_mask ? launch_attn<DT, DQK, DV, kMasked, true>(p, a, s)
+                          : launch_attn<DT, DQK, DV, kDense, true>(p, a, s);
     return a.has_mask ? launch_attn<DT, DQK, DV, kMasked>(p, a, s) : launch_attn<DT, DQK, DV, kDense>(p, a, s);
 }
 

@@ -315,13 +315,15 @@ fia_status fia_get_workspace_size(const fia_tensor* query, const fia_tensor* key
     int64_t pool_blocks = 0;
     int32_t pool_layout = 0;
     if (paged) {
-        // PageAttention (constraints, page attention scenario): decode only
-        // here; paged prefill is not provided.
-        if (!decode) return FIA_ERR_UNSUPPORTED;
+        // PageAttention (constraints, page attention scenario).  Query S == 1:
+        // block_size a multiple of 16; query S > 1: a multiple of 128 in
+        // [128, 512].  A TND query with a paged cache is not provided.
+        if (layout == LAYOUT_TND) return FIA_ERR_UNSUPPORTED;
         if (!block_table->data) return FIA_ERR_NULLPTR;
         if (block_table->dtype != FIA_I32) return FIA_ERR_DTYPE;
         if (block_table->ndim != 2 || block_table->dims[0] != gq.B) return FIA_ERR_SHAPE;
         if (prm->block_size <= 0 || prm->block_size % 16 != 0) return FIA_ERR_PARAM;
+        if (!decode && (prm->block_size % 128 != 0 || prm->block_size > 512)) return FIA_ERR_PARAM;
         if (!prm->actual_seq_kvlen) return FIA_ERR_PARAM;
         if (key->ndim != value->ndim) return FIA_ERR_SHAPE;
         for (int i = 0; i < key->ndim; ++i)
@@ -440,7 +442,9 @@ fia_status fia_get_workspace_size(const fia_tensor* query, const fia_tensor* key
                 } else {
                     return FIA_ERR_SHAPE;
                 }
-                if (m->ndim < 2 || rows < gq.S || cols < Skv) return FIA_ERR_SHAPE;
+                // paged: the mask's KV_S covers maxBlockNumPerSeq * block_size
+                const int64_t need_cols = paged ? max_blocks * prm->block_size : Skv;
+                if (m->ndim < 2 || rows < gq.S || cols < need_cols) return FIA_ERR_SHAPE;
                 if (mb != 1 && mb != B) return FIA_ERR_SHAPE;
                 mask = (const uint8_t*)m->data;
                 mask_rstride = cols;
@@ -602,13 +606,25 @@ fia_status fia_get_workspace_size(const fia_tensor* query, const fia_tensor* key
     a.q_rowmul = QN * Dq;
     a.k_rowmul = KVN * Dq;
     a.v_rowmul = KVN * Dv;
+    a.paged = paged;
+    if (paged) {
+        // pool (blocknum, KV_N, block_size, D) or (blocknum, block_size, KV_N * D)
+        const int64_t bs = prm->block_size;
+        a.block_table = (const int32_t*)block_table->data;
+        a.bt_stride = block_table->dims[1];
+        a.block_size = (int32_t)bs;
+        a.p_blk = bs * KVN * Dq;
+        a.k_sH = a.v_sH = pool_layout == 0 ? bs * Dq : Dq;
+        a.k_sS = a.v_sS = pool_layout == 0 ? Dq : KVN * Dq;
+        a.k_rowmul = a.v_rowmul = 0;
+    }
     a.o_rowmul = QN * Dv;
     a.lse_rowmul = QN;
 
     std::vector<BatchInfo> bi((size_t)B);
     for (int64_t b = 0; b < B; ++b) {
         bi[(size_t)b].q_row0 = layout == LAYOUT_TND ? qstart[(size_t)b] : b * gq.S;
-        bi[(size_t)b].kv_row0 = layout == LAYOUT_TND ? kvstart[(size_t)b] : b * Skv;
+        bi[(size_t)b].kv_row0 = paged ? 0 : layout == LAYOUT_TND ? kvstart[(size_t)b] : b * Skv;
         bi[(size_t)b].lq = (int32_t)lq[(size_t)b];
         bi[(size_t)b].lkv = (int32_t)lkv[(size_t)b];
     }

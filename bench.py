@@ -1,7 +1,8 @@
 #!/usr/bin/env python3
 """Benchmark of the MI355X fused inference attention forward.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2] [--secondary c1,c3,c4,c5]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2]
+                    [--secondary c1,c3,c4,c5,paged_prefill,mtp_decode]
 
 One step is one fia_run (phase 2) of the headline workload: the GQA causal
 prefill, bf16, B=4, Q_N=32, KV_N=8, max S=4096, D=128, BSND, per-batch
@@ -13,9 +14,11 @@ pairs counted exactly from the lengths and the mask mode (masked pairs and
 skipped tiles are not counted).
 
 The other workloads (dense causal fp16 prefill, paged GQA decode, varlen TND
-prefill, block-sparse prefill) are timed the same way and reported under
-"secondary"; the decode line is in GB/s of algorithmic bytes (every KV byte of
-every kv head once, plus q, out, lse and the block-table entries read).
+prefill, block-sparse prefill, chunked prefill against a paged cache,
+multi-token decode against a paged cache) are timed the same way and reported
+under "secondary"; the two decode lines are in GB/s of algorithmic bytes
+(every KV byte of every kv head once, plus q, out, lse and the block-table
+entries read).
 
 The JSON line carries the roofline of the headline kernel (achieved from HIP
 events on the stream the kernel runs on) and the fp64 CPU oracle timed on a
@@ -86,8 +89,9 @@ def decode_bytes(case) -> int:
     import numpy as np
     L = case.lkv.astype(np.int64)
     kv = int(L.sum()) * case.KVN * (case.Dqk + case.Dv) * 2
-    qo = case.B * case.QN * (case.Dqk + case.Dv) * 2
-    lse = case.B * case.QN * 4 if case.return_lse else 0
+    rows = case.B * case.QN * case.Sq          # query rows (decode: S = 1)
+    qo = rows * (case.Dqk + case.Dv) * 2
+    lse = rows * 4 if case.return_lse else 0
     bt = 4 * int(((L + case.block_size - 1) // case.block_size).sum()) if case.block_table is not None else 0
     return kv + qo + lse + bt
 
@@ -152,7 +156,7 @@ def measure(name, steps, warmup):
     wall, ev = time_plan(plan, steps, warmup)
     res = {"workload": case.name, "steps": steps, "ms_per_step": wall * 1e3,
            "kernel_ms": ev * 1e3, "phase1_us": round(phase1_us, 1)}
-    if name == "c3":
+    if name in ("c3", "mtp_decode"):
         nbytes = decode_bytes(case)
         res.update(value=nbytes / wall / 1e9, unit="GB/s", algorithmic_bytes=nbytes,
                    roofline={"bound": "hbm", "achieved": nbytes / ev / 1e9, "peak": PEAK_HBM_GBS,
@@ -218,7 +222,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="c2")
-    ap.add_argument("--secondary", default="c1,c3,c4,c5",
+    ap.add_argument("--secondary", default="c1,c3,c4,c5,paged_prefill,mtp_decode",
                     help="comma list of other workloads to time ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",

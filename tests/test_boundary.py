@@ -205,9 +205,23 @@ def test_paged_decode_validation():
     assert run(bt=torch.zeros(B, 2, dtype=torch.int32)) == _abi.FIA_ERR_SHAPE
     assert run(bt=torch.zeros(B, 3, dtype=torch.int64)) == _abi.FIA_ERR_DTYPE
     assert run(pool=torch.zeros(4, KVN, bs, D, dtype=torch.bfloat16)) == _abi.FIA_ERR_SHAPE
-    # paged prefill is not provided
+    # query S > 1 (paged prefill, multi-token decode): block_size a multiple
+    # of 128 in [128, 512]
     q2 = torch.zeros(B, QN, 4, D, dtype=torch.bfloat16)
-    assert run(q=q2) == _abi.FIA_ERR_UNSUPPORTED
+    assert run(q=q2) == _abi.FIA_ERR_PARAM
+    for bs2, code in ((128, _abi.FIA_OK), (384, _abi.FIA_OK), (512, _abi.FIA_OK),
+                      (64, _abi.FIA_ERR_PARAM), (640, _abi.FIA_ERR_PARAM)):
+        pool2 = torch.zeros(nblk, KVN, bs2, D, dtype=torch.bfloat16)
+        assert run(q=q2, pool=pool2, block_size=bs2, bt=torch.zeros(B, 1, dtype=torch.int32)) == code, bs2
+    # a TND query with a paged cache is not provided
+    p = _params(input_layout="TND", num_heads=QN, num_key_value_heads=KVN, block_size=128,
+                sparse_mode=3)
+    cq = np.array([3, 7], dtype=np.int64)
+    p.actual_seq_qlen, p.n_actual_seq_qlen = cq.ctypes.data, 2
+    p.actual_seq_kvlen, p.n_actual_seq_kvlen = lkv.ctypes.data, 2
+    qt = torch.zeros(7, QN, D, dtype=torch.bfloat16)
+    pool3 = torch.zeros(nblk, KVN, 128, D, dtype=torch.bfloat16)
+    assert _phase1(qt, pool3, pool3, p, bt=torch.zeros(B, 1, dtype=torch.int32))[0] == _abi.FIA_ERR_UNSUPPORTED
 
 
 def test_tnd_requires_cumulative_lengths():

@@ -396,6 +396,64 @@ def test_paged_equals_contiguous_after_gather(pool_layout):
     np.testing.assert_array_equal(lse, lc)
 
 
+def _gather_pool(case):
+    """Contiguous BNSD copies [B, KVN, cols * bs, D] of a paged pool (rows of
+    unused table entries stay zero)."""
+    bt = case.block_table.numpy()
+    bs, KVN, D = case.block_size, case.KVN, case.Dqk
+    kp, vp = case.k, case.v
+    if case.pool_layout == 1:
+        kp = kp.reshape(kp.shape[0], bs, KVN, D).permute(0, 2, 1, 3)
+        vp = vp.reshape(vp.shape[0], bs, KVN, D).permute(0, 2, 1, 3)
+    S = bt.shape[1] * bs
+    kc = torch.zeros(case.B, KVN, S, D, dtype=kp.dtype)
+    vc = torch.zeros(case.B, KVN, S, D, dtype=vp.dtype)
+    for b in range(case.B):
+        for c in range(bt.shape[1]):
+            if bt[b, c] >= 0:
+                kc[b, :, c * bs:(c + 1) * bs] = kp[bt[b, c]]
+                vc[b, :, c * bs:(c + 1) * bs] = vp[bt[b, c]]
+    return kc, vc
+
+
+@pytest.mark.parametrize("pool_layout", [0, 1])
+@pytest.mark.parametrize("mode", [0, 3, 4])
+def test_paged_prefill_equals_contiguous_after_gather(pool_layout, mode):
+    # chunked prefill: query chunks shorter than the cached kv
+    case = W.make_paged_prefill(layout="BNSD", B=3, QN=4, KVN=2, D=16, Sq=12, lq=[12, 5, 9],
+                                lkv=[40, 5, 130], block_size=32, pool_layout=pool_layout,
+                                sparse_mode=mode, pre_tokens=20, next_tokens=3, seed=56,
+                                extra_blocks=3)
+    out, lse = oracle.attention(case)
+    kc, vc = _gather_pool(case)
+    cont = W.make_fia(layout="BNSD", dtype=torch.bfloat16, B=3, QN=4, KVN=2, Sq=12,
+                      Skv=kc.shape[2], Dqk=16, lq=case.lq, lkv=case.lkv, sparse_mode=mode,
+                      pre_tokens=20, next_tokens=3, seed=0)
+    cont.q, cont.k, cont.v = case.q, kc, vc
+    oc, lc = oracle.attention(cont)
+    np.testing.assert_array_equal(out, oc)
+    np.testing.assert_array_equal(lse, lc)
+
+
+def test_multi_token_decode_equals_last_rows_of_causal_prefill():
+    # sparse_mode 3 aligns the query rows bottom-right: the Q_S query tokens
+    # of a decode step see what the last Q_S rows of a full causal prefill see
+    L, QS = [37, 9, 64], 4
+    full = W.make_fia(layout="BNSD", dtype=torch.bfloat16, B=3, QN=4, KVN=2, Sq=64, Dqk=16,
+                      sparse_mode=3, lq=L, lkv=L, seed=57)
+    of, lf = oracle.attention(full)
+    mtp = W.make_fia(layout="BNSD", dtype=torch.bfloat16, B=3, QN=4, KVN=2, Sq=QS, Skv=64,
+                     Dqk=16, sparse_mode=3, lkv=L, seed=0)
+    mtp.q = torch.stack([full.q[b, :, L[b] - QS:L[b]] for b in range(3)]).contiguous()
+    mtp.k, mtp.v = full.k, full.v
+    om, lm = oracle.attention(mtp)
+    for b in range(3):
+        np.testing.assert_array_equal(om[b], of[b, :, L[b] - QS:L[b]])
+        np.testing.assert_array_equal(lm[b], lf[b, :, L[b] - QS:L[b]])
+    # the first query token of the step sees every key but the last QS - 1
+    assert np.all(np.isfinite(lm))
+
+
 def test_row_subset_matches_full_run():
     case = W.make_fia(layout="BSND", dtype=torch.bfloat16, B=2, QN=4, KVN=2, Sq=20, Dqk=16,
                       sparse_mode=3, lq=[20, 13], lkv=[20, 13], seed=52)

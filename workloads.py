@@ -251,6 +251,69 @@ def make_paged_decode(name="custom", *, dtype=torch.bfloat16, B=2, QN=4, KVN=2, 
                    meta={"NB": NB})
 
 
+def make_paged_prefill(name="custom", *, layout="BNSD", dtype=torch.bfloat16, B=2, QN=4,
+                       KVN=2, D=64, Sq=64, lq=None, lkv=(300, 170), block_size=128,
+                       pool_layout=0, sparse_mode=3, pre_tokens=INT_MAX, next_tokens=INT_MAX,
+                       mask_kind=None, scale=None, seed=0, device="cpu", extra_blocks=0,
+                       table_cols=None, nan_pool=False, return_lse=True) -> FiaCase:
+    """Prefill (query S > 1) against a paged KV cache: the query in ``layout``
+    (BNSD/BSND/BSH) with per-batch lengths ``lq`` (None = Sq), K/V in a shared
+    physical pool addressed through a block table holding a seeded
+    permutation of the pool's block ids (unused entries -1).  ``nan_pool``
+    fills the pool's unreferenced blocks and the tail rows of each batch's
+    last block with NaN (they must never be read).  ``mask_kind`` as in
+    :func:`make_fia` ("random"/"zeros" masks are [B, 1, Sq, cols * block_size])."""
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    ss = _streams(seed)
+    lkv = np.asarray(lkv, dtype=np.int64)
+    if lq is not None:
+        lq = np.asarray(lq, dtype=np.int64)
+    nblk = [(int(L) + block_size - 1) // block_size for L in lkv]
+    NB = sum(nblk) + extra_blocks
+    cols = max(max(nblk), 1) if table_cols is None else table_cols
+    rng = np.random.default_rng(ss[STREAM_TABLE])
+    perm = rng.permutation(NB).astype(np.int32)
+    table = np.full((B, cols), -1, dtype=np.int32)
+    pos = 0
+    for b in range(B):
+        table[b, :nblk[b]] = perm[pos:pos + nblk[b]]
+        pos += nblk[b]
+    q = normal_tensor(_shape(layout, B, QN, Sq, D), dtype, ss[STREAM_Q], device)
+    pshape = (NB, KVN, block_size, D) if pool_layout == 0 else (NB, block_size, KVN * D)
+    k = normal_tensor(pshape, dtype, ss[STREAM_K], device)
+    v = normal_tensor(pshape, dtype, ss[STREAM_V], device)
+    if nan_pool:
+        used = set(int(x) for x in table.reshape(-1) if x >= 0)
+        for blk in range(NB):
+            if blk not in used:
+                k[blk] = float("nan")
+                v[blk] = float("nan")
+        for b in range(B):
+            if nblk[b] == 0:
+                continue
+            last, tail = int(table[b, nblk[b] - 1]), int(lkv[b]) - (nblk[b] - 1) * block_size
+            if pool_layout == 0:
+                k[last, :, tail:] = float("nan")
+                v[last, :, tail:] = float("nan")
+            else:
+                k[last, tail:] = float("nan")
+                v[last, tail:] = float("nan")
+    Skv = cols * block_size
+    mask = None
+    if mask_kind == "template":
+        mask = torch.triu(torch.ones(2048, 2048, dtype=torch.uint8), diagonal=1).to(device)
+    elif mask_kind == "random":
+        mrng = np.random.default_rng(ss[STREAM_MASK])
+        mask = torch.from_numpy(mrng.integers(0, 2, size=(B, 1, Sq, Skv), dtype=np.uint8)).to(device)
+    elif mask_kind == "zeros":
+        mask = torch.zeros(B, 1, Sq, Skv, dtype=torch.uint8, device=device)
+    return FiaCase(name=name, layout=layout, dtype=dtype, B=B, QN=QN, KVN=KVN, Sq=Sq, Skv=Skv,
+                   Dqk=D, Dv=D, scale=scale, sparse_mode=sparse_mode, pre_tokens=pre_tokens,
+                   next_tokens=next_tokens, lq=lq, lkv=lkv, q=q, k=k, v=v, atten_mask=mask,
+                   block_table=torch.from_numpy(table).to(device), block_size=block_size,
+                   pool_layout=pool_layout, return_lse=return_lse, meta={"NB": NB})
+
+
 def make_bsa(name="custom", *, layout="BNSD", dtype=torch.bfloat16, B=1, QN=2, KVN=1,
              Sq=256, Skv=None, D=64, X=128, Y=128, p=0.25, lq=None, lkv=None, scale=None,
              seed=0, device="cpu", mask_kind="bernoulli", return_lse=True) -> BsaCase:
@@ -361,10 +424,43 @@ def c5_block_sparse_bf16(device="cpu") -> BsaCase:
                     p=0.25, seed=1005, device=device)
 
 
+def paged_prefill_lengths():
+    rng = np.random.default_rng(_streams(1006)[STREAM_LENGTHS])
+    lq = rng.integers(512, 2048, size=8, endpoint=True).astype(np.int64)
+    hist = rng.integers(0, 14336, size=8, endpoint=True).astype(np.int64)
+    return lq, lq + hist
+
+
+def paged_chunked_prefill_bf16(device="cpu") -> FiaCase:
+    """Chunked prefill against a paged cache: B=8, Q_N=32, KV_N=8, D=128,
+    bf16, query BSND padded to 2048 rows with chunk lengths ~ U{512..2048},
+    KV lengths = chunk + history ~ U{0..14336}, page 128 tokens, pool
+    (NB, 128, KV_N * D), bottom-right causal (sparse_mode 3), LSE on."""
+    lq, lkv = paged_prefill_lengths()
+    return make_paged_prefill("paged_chunked_prefill_bf16_b8_n32_kv8_d128_bs128", layout="BSND",
+                              dtype=torch.bfloat16, B=8, QN=32, KVN=8, D=128, Sq=2048, lq=lq,
+                              lkv=lkv, block_size=128, pool_layout=1, sparse_mode=3,
+                              mask_kind="template", seed=1006, device=device)
+
+
+def paged_mtp_decode_bf16(device="cpu") -> FiaCase:
+    """Multi-token decode (4 query tokens per sequence) against a paged cache:
+    B=64, Q_S=4, Q_N=32, KV_N=8, D=128, bf16, BNSD, KV lengths ~ U{512..32768},
+    page 128 tokens, pool (NB, KV_N, 128, 128), bottom-right causal, LSE on."""
+    rng = np.random.default_rng(_streams(1007)[STREAM_LENGTHS])
+    lkv = rng.integers(512, 32768, size=64, endpoint=True).astype(np.int64)
+    return make_paged_prefill("paged_mtp4_decode_bf16_b64_n32_kv8_d128_bs128", layout="BNSD",
+                              dtype=torch.bfloat16, B=64, QN=32, KVN=8, D=128, Sq=4, lq=None,
+                              lkv=lkv, block_size=128, pool_layout=0, sparse_mode=3,
+                              mask_kind="template", seed=1007, device=device)
+
+
 WORKLOADS = {
     "c1": c1_dense_causal_fp16,
     "c2": c2_gqa_causal_bf16,
     "c3": c3_paged_decode_bf16,
     "c4": c4_varlen_tnd_bf16,
     "c5": c5_block_sparse_bf16,
+    "paged_prefill": paged_chunked_prefill_bf16,
+    "mtp_decode": paged_mtp_decode_bf16,
 }
