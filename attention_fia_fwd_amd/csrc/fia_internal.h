@@ -22,7 +22,8 @@ constexpr int kBlockN = 64;
 constexpr int kNumXcds = 8;
 // Tokens per inner step of the decode kernel; a decode split is a multiple.
 constexpr int kDecodeStep = 32;
-// Query heads one decode wave serves (a GQA group is cut into chunks of this).
+// Query rows (head, token) one decode wave serves; the G x S rows of a kv
+// head are cut into chunks of this.
 constexpr int kDecodeHeads = 16;
 // Compute units of one MI355X and decode waves resident per CU, used only to
 // size the decode schedule.
@@ -81,16 +82,20 @@ struct AttnArgs {
     int32_t paged;
 };
 
-// Decode schedule.  A segment is (batch b, kv head, chunk of <= 16 query
-// heads of its GQA group) over kv tokens [0, Lkv_b).  The token streams of
-// all segments are concatenated and cut into equal per-wave quotas; a piece
-// is the part of one segment that one wave processes.
+// Decode schedule.  The query rows of one (batch, kv head) are the G x S
+// pairs (head of the GQA group, query token), row r = head * S + token; a
+// segment is (batch b, kv head, chunk of <= 16 such rows) over kv tokens
+// [0, Lkv_b).  The token streams of all segments are concatenated and cut
+// into equal per-wave quotas; a piece is the part of one segment that one
+// wave processes.
 struct DecSeg {
     int64_t kv_row0;     // contiguous KV: first row of batch b
     int32_t b;
     int32_t lkv;
     int32_t first;       // first piece of this segment
     int32_t count;       // pieces of this segment (0 when lkv == 0)
+    int32_t lq;          // valid query tokens of batch b (rows past it: out 0, lse +inf)
+    int32_t pad;
 };
 
 struct DecPiece {
@@ -100,11 +105,15 @@ struct DecPiece {
 };
 
 struct DecodeArgs {
-    const void* q;                 // [B, QN, 1, D] / [B, 1, QN, D] / [B, 1, QN*D]
+    const void* q;                 // [B, QN, S, D] / [B, S, QN, D] / [B, S, QN*D]
     const void* k;
     const void* v;
-    void* o;
-    float* lse;                    // [B, QN, 1, 1]
+    void* o;                       // the query's layout with D = Dv
+    float* lse;                    // [B, QN, S, 1]
+    // query / output element strides: batch, head, token
+    int64_t q_sB, q_sH, q_sS, o_sB, o_sH, o_sS;
+    int32_t S;                     // query tokens per sequence (<= 16)
+    int32_t causal;                // sparse_mode 3: token t sees keys j <= Lkv - Lq + t
     const int32_t* block_table;    // paged only
     int64_t bt_stride;
     int32_t block_size;            // paged only
@@ -118,7 +127,7 @@ struct DecodeArgs {
     const int32_t* wave_first;     // [n_waves + 1]: pieces of wave w
     float* part_o;                 // [n_pieces, Gc, Dv]
     float* part_lse;               // [n_pieces, Gc]
-    int32_t B, QN, KVN, G, Gc, nhc;
+    int32_t B, QN, KVN, G, Gc, nhc; // Gc rows per chunk, nhc chunks of G * S rows
     int32_t n_waves, n_pieces;
     float scale_log2;
     int32_t return_lse;

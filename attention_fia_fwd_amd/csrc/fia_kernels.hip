@@ -754,15 +754,29 @@ __global__ __launch_bounds__(64) void decode_split(DecodeArgs a)
         const int kvh = (pc_.seg / a.nhc) % a.KVN;
         const int t0 = pc_.t0;
         const int t1 = pc_.t1;
-        const int nh = min(kDecodeHeads, a.G - kDecodeHeads * hc);
-        const int hq = kvh * a.G + kDecodeHeads * hc + n;
+        // column n is query row r = 16 hc + n of the kv head: head r / S of
+        // the GQA group, query token r % S
+        const int S = a.S;
+        const int r0 = kDecodeHeads * hc;
+        const int nh = min(kDecodeHeads, a.G * S - r0);
+        const int rq = r0 + n;
+        const int tq = rq % S;
+        const int hq = kvh * a.G + rq / S;
         const float c = fmaxf(fabsf(a.scale_log2), kMinScale);
         const uint32_t qflip = a.scale_log2 < 0.f ? 0x80008000u : 0u;
+        // sparse_mode 3 (S > 1): token tq sees keys j <= Lkv - Lq + tq; jmin is
+        // the smallest such bound over the chunk's columns (wave-uniform), so
+        // only the steps that reach past it evaluate the per-column bound
+        const int jbase = db.lkv - db.lq;
+        const int tq_min = (r0 % S) + nh > S ? 0 : r0 % S;
+        const int jmax = a.causal ? jbase + tq : INT32_MAX;
+        const int jmin = a.causal ? jbase + tq_min : INT32_MAX;
 
-        // Q^T as the B operand: column n = head hq, d = 32s + 8qd.
+        // Q^T as the B operand: column n = (head hq, token tq), d = 32s + 8qd.
         uint4 qf[NK];
         if (n < nh) {
-            const uint16_t* src = (const uint16_t*)a.q + ((int64_t)b * a.QN + hq) * D + 8 * qd;
+            const uint16_t* src = (const uint16_t*)a.q + (int64_t)b * a.q_sB + (int64_t)hq * a.q_sH +
+                                  (int64_t)tq * a.q_sS + 8 * qd;
 #pragma unroll
             for (int s = 0; s < NK; ++s) {
                 uint4 v = *(const uint4*)(src + 32 * s);
@@ -879,11 +893,11 @@ __global__ __launch_bounds__(64) void decode_split(DecodeArgs a)
                 x[i] = s0[i];
                 x[4 + i] = s1[i];
             }
-            if (tt0 + ST > t1) {
+            if (tt0 + ST > t1 || tt0 + ST - 1 > jmin) {
 #pragma unroll
                 for (int r = 0; r < 8; ++r) {
                     const int tk = tt0 + 16 * (r >> 2) + 4 * qd + (r & 3);
-                    if (tk >= t1) x[r] = -INFINITY;
+                    if (tk >= t1 || tk > jmax) x[r] = -INFINITY;
                 }
             }
             float mt = x[0];
@@ -953,20 +967,24 @@ __global__ __launch_bounds__(64) void decode_split(DecodeArgs a)
     }
 }
 
-// Merge the kv splits of one (batch, head): weights exp(lse_s - max lse).
+// Merge the kv splits of one (batch, head, query token): weights
+// exp(lse_s - max lse).  Tokens at or past the batch's query length are
+// written as out = 0, lse = +inf.
 template <int DT, int D>
 __global__ __launch_bounds__(64) void decode_combine(DecodeArgs a)
 {
     using O = Ops<DT>;
-    const int bh = blockIdx.x;
-    const int b = bh / a.QN, h = bh % a.QN;
-    const int kvh = h / a.G, r = h % a.G;
+    const int bht = blockIdx.x;
+    const int S = a.S;
+    const int t = bht % S;
+    const int b = bht / (a.QN * S), h = (bht / S) % a.QN;
+    const int kvh = h / a.G, r = (h % a.G) * S + t;
     const int hc = r / kDecodeHeads, n = r % kDecodeHeads;
     const DecSeg sg = a.segs[((int64_t)b * a.KVN + kvh) * a.nhc + hc];
-    const int ns = sg.count;
+    const int ns = t < sg.lq ? sg.count : 0;
     const int64_t slot0 = sg.first;
     const int lane = threadIdx.x;
-    uint16_t* op = (uint16_t*)a.o + ((int64_t)b * a.QN + h) * D;
+    uint16_t* op = (uint16_t*)a.o + (int64_t)b * a.o_sB + (int64_t)h * a.o_sH + (int64_t)t * a.o_sS;
 
     float M = -INFINITY;
     for (int s = 0; s < ns; ++s) M = fmaxf(M, a.part_lse[(slot0 + s) * a.Gc + n]);
@@ -991,7 +1009,7 @@ __global__ __launch_bounds__(64) void decode_combine(DecodeArgs a)
         op[lane + 64 * e] = (uint16_t)(pk & 0xffffu);
     }
     if (a.return_lse && lane == 0)
-        a.lse[(int64_t)b * a.QN + h] = wsum > 0.f ? M + __logf(wsum) : INFINITY;
+        a.lse[((int64_t)b * a.QN + h) * S + t] = wsum > 0.f ? M + __logf(wsum) : INFINITY;
 }
 
 // ---------------------------------------------------------------------------
@@ -1058,7 +1076,7 @@ int launch_dec(const fia_plan& p, const DecodeArgs& a, hipStream_t stream)
         hipLaunchKernelGGL((decode_split<DT, D>), dim3((unsigned)p.n_waves), dim3(64), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return (int)e;
-    hipLaunchKernelGGL((decode_combine<DT, D>), dim3((unsigned)(p.B * p.QN)), dim3(64), 0, stream, a);
+    hipLaunchKernelGGL((decode_combine<DT, D>), dim3((unsigned)(p.B * p.QN * a.S)), dim3(64), 0, stream, a);
     return (int)hipGetLastError();
 }
 

@@ -466,7 +466,17 @@ fia_status fia_get_workspace_size(const fia_tensor* query, const fia_tensor* key
 
     const double scale_log2 = prm->scale_value * kLog2e;
 
-    if (decode) {
+    // Kernel choice.  Query S == 1, and multi-token decode (S <= 16 with all
+    // G x S (head, token) rows of a kv head in one 16-column chunk, sparse_mode
+    // 3 or 0 without a mask), run on the split-KV decode kernel: each K/V
+    // byte is read once for all those rows and the kv range is spread over
+    // the whole GPU.  Everything else runs on the prefill kernel.
+    const bool dec_kernel =
+        decode || (layout != LAYOUT_TND && gq.S <= kDecodeHeads && p->G * gq.S <= kDecodeHeads &&
+                   mask == nullptr && (mode == 3 || mode == 0) && Dv == gq.D &&
+                   (gq.D == 64 || gq.D == 128));
+
+    if (dec_kernel) {
         p->kind = KIND_DECODE;
         DecodeArgs& d = p->dec;
         d.q = query->data;
@@ -477,6 +487,15 @@ fia_status fia_get_workspace_size(const fia_tensor* query, const fia_tensor* key
         d.return_lse = want_lse;
         d.paged = paged;
         const int64_t D = gq.D;
+        const int64_t S = gq.S;
+        d.S = (int32_t)S;
+        d.causal = !decode && mode == 3;
+        if (layout == LAYOUT_BNSD) {
+            d.q_sB = QN * S * D; d.q_sH = S * D; d.q_sS = D;
+        } else {
+            d.q_sB = S * QN * D; d.q_sH = D; d.q_sS = QN * D;
+        }
+        d.o_sB = d.q_sB; d.o_sH = d.q_sH; d.o_sS = d.q_sS;   // D_v == D
         if (paged) {
             const int64_t bs = prm->block_size;
             d.block_table = (const int32_t*)block_table->data;
@@ -491,8 +510,9 @@ fia_status fia_get_workspace_size(const fia_tensor* query, const fia_tensor* key
             d.c_tok = layout == LAYOUT_BNSD ? D : KVN * D;
         }
         const int64_t G = QN / KVN;
-        const int64_t Gc = std::min<int64_t>(G, kDecodeHeads);
-        const int64_t nhc = (G + kDecodeHeads - 1) / kDecodeHeads;
+        const int64_t R = G * S;       // (head, token) rows of one kv head
+        const int64_t Gc = std::min<int64_t>(R, kDecodeHeads);
+        const int64_t nhc = (R + kDecodeHeads - 1) / kDecodeHeads;
         // Balanced schedule: one wave per resident slot, each with an equal
         // quota of the concatenated token stream (a multiple of 16 tokens, so
         // a 16-token sub-tile never crosses a page).
@@ -519,6 +539,7 @@ fia_status fia_get_workspace_size(const fia_tensor* query, const fia_tensor* key
                 sg.kv_row0 = paged ? 0 : b * Skv;
                 sg.b = (int32_t)b;
                 sg.lkv = (int32_t)L;
+                sg.lq = (int32_t)lq[(size_t)b];
                 sg.first = (int32_t)pieces.size();
                 for (int64_t t = 0; t < L;) {
                     if (remaining < 16) {                  // next wave

@@ -87,6 +87,30 @@ def test_multi_token_decode_paged(QS, G):
     check(case)
 
 
+@pytest.mark.parametrize("layout, QS, G, mode, dtype, D", [
+    ("BSND", 8, 2, 3, torch.bfloat16, 128),
+    ("BNSD", 4, 4, 0, torch.bfloat16, 128),
+    ("BSH", 2, 8, 3, torch.float16, 64),
+    ("BNSD", 16, 1, 3, torch.float16, 128),
+    ("BSND", 3, 5, 3, torch.bfloat16, 64),
+])
+def test_multi_token_decode_contiguous(layout, QS, G, mode, dtype, D):
+    # contiguous KV, per-batch query lengths below S (padding rows) and one
+    # batch with fewer keys than query tokens (rows without keys under mode 3)
+    case = W.make_fia(f"mtp_{layout}_s{QS}_g{G}_m{mode}", layout=layout, dtype=dtype, B=4,
+                      QN=2 * G, KVN=2, Sq=QS, Skv=1300, Dqk=D, sparse_mode=mode,
+                      lq=[QS, max(QS - 1, 1), QS, 0], lkv=[1300, 77, QS - 1, 50],
+                      mask_kind="template" if mode == 3 else None, seed=360 + QS + G,
+                      nan_padding=True)
+    say(f"[mtp] {case.name}")
+    ref_out, ref_lse = oracle.attention(case)
+    to_dev(case)
+    plan = fia_plan(case)
+    out, lse = run(plan)
+    compare(case, out, lse, ref_out, ref_lse)
+    plan.close()
+
+
 def test_multi_token_decode_equals_last_prefill_rows_on_gpu():
     L, QS = [900, 131], 4
     full = W.make_fia("mtp_vs_prefill", layout="BNSD", dtype=torch.bfloat16, B=2, QN=8, KVN=2,
