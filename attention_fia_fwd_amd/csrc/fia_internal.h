@@ -114,6 +114,10 @@ struct DecodeArgs {
     int64_t q_sB, q_sH, q_sS, o_sB, o_sH, o_sS;
     int32_t S;                     // query tokens per sequence (<= 16)
     int32_t causal;                // sparse_mode 3: token t sees keys j <= Lkv - Lq + t
+    // query S == 1 atten_mask, one byte per (batch, kv token), nonzero =
+    // masked; batch b's row starts at mask + b * mask_bstride (0: broadcast)
+    const uint8_t* mask;
+    int64_t mask_bstride;
     const int32_t* block_table;    // paged only
     int64_t bt_stride;
     int32_t block_size;            // paged only

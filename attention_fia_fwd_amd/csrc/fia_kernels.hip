@@ -729,7 +729,7 @@ __device__ __forceinline__ float quad_sum(float x)
 }
 
 
-template <int DT, int D>
+template <int DT, int D, bool MASK>
 __global__ __launch_bounds__(64) void decode_split(DecodeArgs a)
 {
     constexpr int ST = kDecodeStep;       // 32 tokens per step
@@ -823,7 +823,14 @@ __global__ __launch_bounds__(64) void decode_split(DecodeArgs a)
         const int vr_in = lane / VCH, vpc = lane % VCH;
         auto vswz = [](int r) { return VCH >= 16 ? 2 * (r & 7) : 2 * ((r >> 1) & 3); };
 
-        auto issue = [&](int tt0, int pg0, int off0, int pg1, int off1, uint4 (&kf)[2][NK], uint16_t* vb) {
+        // atten_mask (query S == 1): lane l (and l + 32) loads the byte of
+        // token tt0 + l of each step, issued with the step's K/V loads; the
+        // step turns the 32 bytes into one wave-uniform bit mask by a ballot.
+        const uint8_t* mrow = MASK ? a.mask + (int64_t)b * a.mask_bstride : nullptr;
+        const int l32 = lane & 31;
+        auto issue = [&](int tt0, int pg0, int off0, int pg1, int off1, uint4 (&kf)[2][NK], uint16_t* vb,
+                         uint32_t& mbyte) {
+            if constexpr (MASK) mbyte = tt0 + l32 < t1 ? mrow[tt0 + l32] : 0u;
 #pragma unroll
             for (int cc = 0; cc < 2; ++cc) {
                 const int pg = cc ? pg1 : pg0, off = cc ? off1 : off0, tb = tt0 + 16 * cc;
@@ -865,17 +872,20 @@ __global__ __launch_bounds__(64) void decode_split(DecodeArgs a)
         };
 
         uint4 kfa[2][NK], kfb[2][NK];
-        auto step = [&](int st, uint4 (&kcur)[2][NK], uint4 (&knext)[2][NK], uint16_t* vcur, uint16_t* vnext) {
+        uint32_t mba = 0, mbb = 0;
+        auto step = [&](int st, uint4 (&kcur)[2][NK], uint4 (&knext)[2][NK], uint16_t* vcur, uint16_t* vnext,
+                        uint32_t mcur, uint32_t& mnext) {
             const int tt0 = t0 + ST * st;
             // pg/off point at the first sub-tile of step st + 1 here
             if (st + 1 < nsteps) {
                 int pg1 = pg, off1 = off;
                 advance16(pg1, off1);
                 __builtin_amdgcn_s_waitcnt(FIA_LGKMCNT0);   // reads of the other V buffer done
-                issue(tt0 + ST, pg, off, pg1, off1, knext, vnext);
+                issue(tt0 + ST, pg, off, pg1, off1, knext, vnext, mnext);
                 pg = pg1; off = off1;
                 advance16(pg, off);
-                __builtin_amdgcn_s_waitcnt(FIA_VMCNT(2 * (NK + NVI)));   // step st landed
+                // step st landed (step st + 1's loads, mask byte first, stay in flight)
+                __builtin_amdgcn_s_waitcnt(FIA_VMCNT(2 * (NK + NVI) + (MASK ? 1 : 0)));
             } else {
                 __builtin_amdgcn_s_waitcnt(FIA_VMCNT(0));
             }
@@ -898,6 +908,15 @@ __global__ __launch_bounds__(64) void decode_split(DecodeArgs a)
                 for (int r = 0; r < 8; ++r) {
                     const int tk = tt0 + 16 * (r >> 2) + 4 * qd + (r & 3);
                     if (tk >= t1 || tk > jmax) x[r] = -INFINITY;
+                }
+            }
+            if constexpr (MASK) {
+                // bit i: token tt0 + i is masked
+                const uint32_t mm = (uint32_t)__ballot(mcur != 0u);
+                if (mm) {
+#pragma unroll
+                    for (int r = 0; r < 8; ++r)
+                        if ((mm >> (16 * (r >> 2) + 4 * qd + (r & 3))) & 1u) x[r] = -INFINITY;
                 }
             }
             float mt = x[0];
@@ -941,13 +960,13 @@ __global__ __launch_bounds__(64) void decode_split(DecodeArgs a)
         if (nsteps > 0) {
             int pg1 = pg, off1 = off;
             advance16(pg1, off1);
-            issue(t0, pg, off, pg1, off1, kfa, vbuf0);
+            issue(t0, pg, off, pg1, off1, kfa, vbuf0, mba);
             pg = pg1; off = off1;
             advance16(pg, off);
         }
         for (int st = 0; st < nsteps; st += 2) {
-            step(st, kfa, kfb, vbuf0, vbuf1);
-            if (st + 1 < nsteps) step(st + 1, kfb, kfa, vbuf1, vbuf0);
+            step(st, kfa, kfb, vbuf0, vbuf1, mba, mbb);
+            if (st + 1 < nsteps) step(st + 1, kfb, kfa, vbuf1, vbuf0, mbb, mba);
         }
 
         // partial: normalised O and natural-log LSE of this split
@@ -1072,8 +1091,10 @@ int launch_attn(const fia_plan& p, const AttnArgs& a, hipStream_t stream)
 template <int DT, int D>
 int launch_dec(const fia_plan& p, const DecodeArgs& a, hipStream_t stream)
 {
-    if (p.n_waves > 0)
-        hipLaunchKernelGGL((decode_split<DT, D>), dim3((unsigned)p.n_waves), dim3(64), 0, stream, a);
+    if (p.n_waves > 0 && a.mask)
+        hipLaunchKernelGGL((decode_split<DT, D, true>), dim3((unsigned)p.n_waves), dim3(64), 0, stream, a);
+    else if (p.n_waves > 0)
+        hipLaunchKernelGGL((decode_split<DT, D, false>), dim3((unsigned)p.n_waves), dim3(64), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return (int)e;
     hipLaunchKernelGGL((decode_combine<DT, D>), dim3((unsigned)(p.B * p.QN * a.S)), dim3(64), 0, stream, a);

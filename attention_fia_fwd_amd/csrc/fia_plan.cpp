@@ -451,8 +451,25 @@ fia_status fia_get_workspace_size(const fia_tensor* query, const fia_tensor* key
                 mask_bstride = mb == 1 ? 0 : rows * cols;
             }
         }
-    } else if (prm->inner_precise > 1) {
-        return FIA_ERR_PARAM;           // Q_S == 1: inner_precise 0 or 1 only
+    } else {
+        if (prm->inner_precise > 1) return FIA_ERR_PARAM;   // Q_S == 1: inner_precise 0 or 1 only
+        // Q_S == 1: an atten_mask masks kv tokens per batch, shapes (B, KV_S),
+        // (B, 1, KV_S) or (B, 1, 1, KV_S) (atten_mask parameter description;
+        // a leading 1 broadcasts); with a paged cache KV_S covers
+        // maxBlockNumPerSeq * block_size
+        if (atten_mask) {
+            const fia_tensor* m = atten_mask;
+            if (!mask_dtype_ok(m->dtype)) return FIA_ERR_DTYPE;
+            if (!m->data) return FIA_ERR_NULLPTR;
+            if (m->ndim < 2 || m->ndim > 4) return FIA_ERR_SHAPE;
+            for (int i = 1; i + 1 < m->ndim; ++i)
+                if (m->dims[i] != 1) return FIA_ERR_SHAPE;
+            const int64_t mb = m->dims[0], cols = m->dims[m->ndim - 1];
+            const int64_t need_cols = paged ? max_blocks * prm->block_size : Skv;
+            if ((mb != 1 && mb != B) || cols < need_cols) return FIA_ERR_SHAPE;
+            mask = (const uint8_t*)m->data;
+            mask_bstride = mb == 1 ? 0 : cols;
+        }
     }
 
     // ----- supported head dims -----
@@ -490,6 +507,8 @@ fia_status fia_get_workspace_size(const fia_tensor* query, const fia_tensor* key
         const int64_t S = gq.S;
         d.S = (int32_t)S;
         d.causal = !decode && mode == 3;
+        d.mask = decode ? mask : nullptr;     // S > 1 reaches here only without one
+        d.mask_bstride = mask_bstride;
         if (layout == LAYOUT_BNSD) {
             d.q_sB = QN * S * D; d.q_sH = S * D; d.q_sS = D;
         } else {

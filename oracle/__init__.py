@@ -148,7 +148,14 @@ def attention(case, rows=None):
     a.sparse_mode = int(case.sparse_mode)
     a.decode = 1 if case.decode else 0
     a.pre_tokens, a.next_tokens = int(case.pre_tokens), int(case.next_tokens)
-    if case.atten_mask is not None and case.sparse_mode in (0, 1) and not case.decode:
+    if case.atten_mask is not None and case.decode:
+        # query S == 1: one value per (batch, kv token), leading 1 broadcasts
+        mn = np.ascontiguousarray(case.atten_mask.detach().to("cpu").to(torch.uint8).numpy())
+        keep.append(mn)
+        a.mask = _ptr(mn)
+        a.mask_rstride = 0
+        a.mask_bstride = 0 if mn.shape[0] == 1 else mn.shape[-1]
+    elif case.atten_mask is not None and case.sparse_mode in (0, 1):
         m = case.atten_mask.detach().to("cpu").contiguous()
         mn = m.to(torch.uint8).numpy()
         keep.append(mn)

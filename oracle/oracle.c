@@ -34,7 +34,10 @@
  *   mode 3          : j <= i + delta               (bottom-right causal)
  *   mode 4          : -pre <= j - i - delta <= next (bottom-right band)
  * Decode (query S == 1 outside TND) ignores sparse_mode, pre and next (v2
- * parameter description of sparse_mode, pre_tokens, next_tokens).
+ * parameter description of sparse_mode, pre_tokens, next_tokens); an
+ * atten_mask there holds one value per (batch, kv token) (v2 atten_mask
+ * description, query S == 1 shapes (B, KV_S), (B, 1, KV_S), (B, 1, 1, KV_S)):
+ *   decode          : mask[b][j] == 0
  * A mask value of nonzero means "masked" (PFA parameter description of
  * atten_mask: padding is filled with 1).
  *
@@ -144,7 +147,7 @@ static int64_t kv_off(const oracle_args* a, int64_t b, int64_t g, int64_t j, int
 static int allowed_dense(const oracle_args* a, int64_t b, int64_t i, int64_t j)
 {
     if (a->decode)
-        return 1;
+        return a->mask ? a->mask[b * a->mask_bstride + j] == 0 : 1;
     int64_t delta = a->lkv[b] - a->lq[b];
     int masked_by_tensor = 0;
     if (a->mask && (a->sparse_mode == 0 || a->sparse_mode == 1))

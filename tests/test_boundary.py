@@ -224,6 +224,24 @@ def test_paged_decode_validation():
     assert _phase1(qt, pool3, pool3, p, bt=torch.zeros(B, 1, dtype=torch.int32))[0] == _abi.FIA_ERR_UNSUPPORTED
 
 
+def test_decode_atten_mask_validation():
+    B, QN, KVN, S, D = 2, 8, 2, 40, 128
+    q = torch.zeros(B, QN, 1, D, dtype=torch.bfloat16)
+    k = torch.zeros(B, KVN, S, D, dtype=torch.bfloat16)
+    p = _params(num_heads=QN, num_key_value_heads=KVN, input_layout="BNSD")
+
+    def code(mask):
+        return _phase1(q, k, k, p, mask=mask)[0]
+
+    for shape in ((B, S), (B, 1, S), (B, 1, 1, S), (1, S), (B, S + 24)):
+        assert code(torch.zeros(shape, dtype=torch.uint8)) == _abi.FIA_OK, shape
+    assert code(torch.zeros(B, 1, 1, S, dtype=torch.bool)) == _abi.FIA_OK
+    assert code(torch.zeros(B, 2, S, dtype=torch.uint8)) == _abi.FIA_ERR_SHAPE
+    assert code(torch.zeros(B, S - 1, dtype=torch.uint8)) == _abi.FIA_ERR_SHAPE
+    assert code(torch.zeros(3, S, dtype=torch.uint8)) == _abi.FIA_ERR_SHAPE
+    assert code(torch.zeros(B, S, dtype=torch.float16)) == _abi.FIA_ERR_DTYPE
+
+
 def test_tnd_requires_cumulative_lengths():
     q = torch.zeros(30, 4, 128, dtype=torch.bfloat16)
     k = torch.zeros(30, 4, 128, dtype=torch.bfloat16)

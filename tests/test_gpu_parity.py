@@ -217,6 +217,38 @@ def test_decode_paged(pool_layout, D):
     check_fia(case)
 
 
+@pytest.mark.parametrize("layout, G, D", [("BNSD", 1, 128), ("BSND", 4, 64), ("BSH", 8, 128)])
+def test_decode_atten_mask_contiguous(layout, G, D):
+    # query S == 1 with a (B, 1, 1, KV_S) mask, half of the kv tokens masked
+    KVN = 2
+    case = W.make_fia(f"decode_mask_{layout}_g{G}", layout=layout, dtype=torch.bfloat16, B=3,
+                      QN=KVN * G, KVN=KVN, Sq=1, Skv=1500, Dqk=D, lkv=[1500, 3, 777],
+                      mask_kind="random", seed=180 + G)
+    check_fia(case)
+
+
+@pytest.mark.parametrize("mask_shape", ["BS", "B1S"])
+def test_decode_atten_mask_paged(mask_shape):
+    case = W.make_paged_decode(f"decode_mask_paged_{mask_shape}", dtype=torch.float16, B=4, QN=8,
+                               KVN=2, D=128, lkv=[3000, 17, 1, 640], block_size=64,
+                               pool_layout=1, seed=185, extra_blocks=2, mask_p=0.3,
+                               mask_shape=mask_shape)
+    check_fia(case)
+
+
+def test_decode_atten_mask_fully_masked_batch_and_broadcast():
+    case = W.make_fia("decode_mask_full", layout="BNSD", dtype=torch.bfloat16, B=3, QN=8, KVN=2,
+                      Sq=1, Skv=900, Dqk=128, lkv=[900, 500, 64], seed=187)
+    m = (np.random.default_rng(3).random((3, 900)) < 0.2).astype(np.uint8)
+    m[1] = 1                                   # batch 1: no key left
+    case.atten_mask = torch.from_numpy(m)
+    check_fia(case)
+    bc = W.make_fia("decode_mask_bcast", layout="BNSD", dtype=torch.bfloat16, B=3, QN=8, KVN=2,
+                    Sq=1, Skv=900, Dqk=128, lkv=[900, 500, 64], seed=187)
+    bc.atten_mask = torch.from_numpy(m[:1].copy())   # a leading 1 broadcasts
+    check_fia(bc)
+
+
 def test_decode_fp16_gqa32_and_empty_kv():
     case = W.make_paged_decode("decode_fp16_g32", dtype=torch.float16, B=2, QN=32, KVN=1, D=128,
                                lkv=[900, 0], block_size=128, seed=150)

@@ -454,6 +454,49 @@ def test_multi_token_decode_equals_last_rows_of_causal_prefill():
     assert np.all(np.isfinite(lm))
 
 
+def test_decode_mask_equals_decode_over_the_kept_keys():
+    # query S == 1 with a per-(batch, kv token) mask: the same as decoding
+    # against only the unmasked keys, gathered into a shorter cache
+    case = W.make_fia(layout="BSND", dtype=torch.bfloat16, B=3, QN=4, KVN=2, Sq=1, Skv=50,
+                      Dqk=16, lkv=[50, 7, 33], mask_kind="random", seed=58)
+    out, lse = oracle.attention(case)
+    m = case.atten_mask.numpy().reshape(3, -1)
+    for b in range(3):
+        keep = np.nonzero(m[b, :int(case.lkv[b])] == 0)[0]
+        sub = W.make_fia(layout="BSND", dtype=torch.bfloat16, B=1, QN=4, KVN=2, Sq=1,
+                         Skv=max(len(keep), 1), Dqk=16, lkv=[len(keep)], seed=0)
+        sub.q = case.q[b:b + 1]
+        if len(keep):
+            sub.k = case.k[b:b + 1, torch.from_numpy(keep)].contiguous()
+            sub.v = case.v[b:b + 1, torch.from_numpy(keep)].contiguous()
+        else:
+            sub.k = case.k[b:b + 1, :1].contiguous()
+            sub.v = case.v[b:b + 1, :1].contiguous()
+        os_, ls_ = oracle.attention(sub)
+        np.testing.assert_array_equal(out[b], os_[0])
+        np.testing.assert_array_equal(lse[b], ls_[0])
+
+
+def test_decode_mask_fully_masked_batch_and_broadcast():
+    case = W.make_fia(layout="BNSD", dtype=torch.bfloat16, B=2, QN=2, Sq=1, Skv=20, Dqk=8,
+                      seed=59)
+    m = np.zeros((2, 20), dtype=np.uint8)
+    m[1] = 1                                   # batch 1: every key masked
+    m[0, 5:9] = 1
+    case.atten_mask = torch.from_numpy(m)
+    out, lse = oracle.attention(case)
+    assert np.all(out[1] == 0) and np.all(np.isposinf(lse[1]))
+    assert np.all(np.isfinite(lse[0]))
+    # a leading 1 broadcasts over the batch
+    case.atten_mask = torch.from_numpy(m[:1].copy())
+    ob, lb = oracle.attention(case)
+    np.testing.assert_array_equal(ob[0], out[0])
+    case.atten_mask = torch.from_numpy(np.repeat(m[:1], 2, axis=0))
+    orep, lrep = oracle.attention(case)
+    np.testing.assert_array_equal(ob, orep)
+    np.testing.assert_array_equal(lb, lrep)
+
+
 def test_row_subset_matches_full_run():
     case = W.make_fia(layout="BSND", dtype=torch.bfloat16, B=2, QN=4, KVN=2, Sq=20, Dqk=16,
                       sparse_mode=3, lq=[20, 13], lkv=[20, 13], seed=52)

@@ -223,9 +223,11 @@ def make_fia(name="custom", *, layout="BNSD", dtype=torch.bfloat16, B=1, QN=2, K
 def make_paged_decode(name="custom", *, dtype=torch.bfloat16, B=2, QN=4, KVN=2, D=64,
                       lkv=(100, 37), block_size=16, pool_layout=0, scale=None, seed=0,
                       device="cpu", q_layout="BNSD", extra_blocks=0, table_cols=None,
-                      return_lse=True) -> FiaCase:
+                      return_lse=True, mask_p=None, mask_shape="B1S") -> FiaCase:
     """Paged decode: Q_S = 1, K/V in a shared physical pool addressed through a
-    block table holding a seeded permutation of the pool's block ids."""
+    block table holding a seeded permutation of the pool's block ids.
+    ``mask_p``: an atten_mask with iid Bernoulli(mask_p) masked kv tokens, of
+    shape (B, KV_S) ("BS") or (B, 1, 1, KV_S) ("B1S"), KV_S = cols * block_size."""
     scale = 1.0 / math.sqrt(D) if scale is None else scale
     ss = _streams(seed)
     lkv = np.asarray(lkv, dtype=np.int64)
@@ -244,9 +246,16 @@ def make_paged_decode(name="custom", *, dtype=torch.bfloat16, B=2, QN=4, KVN=2, 
     pshape = (NB, KVN, block_size, D) if pool_layout == 0 else (NB, block_size, KVN * D)
     k = normal_tensor(pshape, dtype, ss[STREAM_K], device)
     v = normal_tensor(pshape, dtype, ss[STREAM_V], device)
+    mask = None
+    if mask_p is not None:
+        mrng = np.random.default_rng(ss[STREAM_MASK])
+        m = (mrng.random((B, cols * block_size)) < mask_p).astype(np.uint8)
+        if mask_shape == "B1S":
+            m = m.reshape(B, 1, 1, -1)
+        mask = torch.from_numpy(np.ascontiguousarray(m)).to(device)
     return FiaCase(name=name, layout=q_layout, dtype=dtype, B=B, QN=QN, KVN=KVN, Sq=1,
                    Skv=cols * block_size, Dqk=D, Dv=D, scale=scale, lq=None, lkv=lkv,
-                   q=q, k=k, v=v, block_table=torch.from_numpy(table).to(device),
+                   q=q, k=k, v=v, atten_mask=mask, block_table=torch.from_numpy(table).to(device),
                    block_size=block_size, pool_layout=pool_layout, return_lse=return_lse,
                    meta={"NB": NB})
 
