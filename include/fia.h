@@ -10,8 +10,11 @@
  *
  * in three forms:
  *   - prefill (query S > 1, or TND): causal / band / explicit-mask sparse modes,
- *     per-batch actual lengths, BNSD / BSND / BSH / TND layouts, GQA;
- *   - decode (query S == 1 outside TND) against a contiguous or paged KV cache;
+ *     per-batch actual lengths, BNSD / BSND / BSH / TND layouts, GQA, against
+ *     a contiguous or (outside TND) paged KV cache;
+ *   - decode (query S == 1 outside TND) against a contiguous or paged KV cache,
+ *     with an optional per-(batch, kv token) mask; multi-token decode (query
+ *     S up to 16, sparse_mode 3) takes the same split-KV path;
  *   - block-sparse prefill (page "aclnnBlockSparseAttentionV2"), where a
  *     block mask selects the KV blocks each Q block attends to.
  *
@@ -104,7 +107,9 @@ typedef struct fia_params {
      * Ignored when the query S is 1 outside TND (decode). */
     int64_t sparse_mode;
     /* PageAttention block size (block_size); 0 = contiguous KV.  With a
-     * block_table it must be a positive multiple of 16. */
+     * block_table and query S == 1 it must be a positive multiple of 16; with
+     * query S > 1 a multiple of 128 in [128, 512] (page attention scenario
+     * constraints of the v2 page). */
     int64_t block_size;
     /* inner_precise 0..3 (bit0 precision/performance, bit1 row-invalid
      * correction).  Accepted; softmax is always computed in fp32 and rows
@@ -139,9 +144,19 @@ void fia_params_init(fia_params* p);
  *                be padded past KV_S).  Modes 2/3/4: the 2048x2048 lower-
  *                triangular template ([2048,2048], [1,2048,2048] or
  *                [1,1,2048,2048]) or NULL; its contents are not read (the mask
- *                follows from the indices).  Ignored for decode.
+ *                follows from the indices).  Query S == 1 (decode): one
+ *                value per (batch, kv token), [B|1,KV_S], [B|1,1,KV_S] or
+ *                [B|1,1,1,KV_S] (v2 atten_mask description); sparse_mode and
+ *                pre/next do not apply there.  With a paged cache KV_S must
+ *                cover maxBlockNumPerSeq * block_size.
  *   block_table  optional int32 [B, >= max blocks per sequence]: PageAttention
- *                block ids.  Only for decode (query S == 1); ids are not checked.
+ *                block ids (page attention scenario of the v2 page): kv token
+ *                j of batch b is row j % block_size of pool block
+ *                block_table[b][j / block_size].  Any query S outside TND (a
+ *                TND query with a paged cache returns FIA_ERR_UNSUPPORTED).
+ *                Ids are not checked: each referenced id must be in
+ *                [0, blocknum), as the page requires; entries past
+ *                ceil(Lkv_b / block_size) are never read.
  *   attention_out same shape as query with D = value's D, same dtype.
  *   softmax_lse  fp32 [B, Q_N, Q_S, 1] (TND: [T, Q_N, 1]); required when
  *                return_softmax_lse, else ignored.
