@@ -95,6 +95,8 @@ class FiaPlan:
                  pre_tokens: int = INT_MAX, next_tokens: int = INT_MAX,
                  input_layout: str = "BSH", sparse_mode: int = 0, block_size: int = 0,
                  inner_precise: int = 0, return_softmax_lse: bool = False,
+                 dequant_scale_key=None, dequant_scale_value=None, dequant_offset_key=None,
+                 dequant_offset_value=None, key_quant_mode: int = 0, value_quant_mode: int = 0,
                  out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None):
         self.plan = None
         kvn = num_key_value_heads or num_heads
@@ -119,7 +121,8 @@ class FiaPlan:
                 lse = torch.empty(query.shape[0], num_heads, S, 1, dtype=torch.float32,
                                   device=query.device)
         self.out, self.lse = out, (lse if return_softmax_lse else None)
-        self._keep = (query, key, value, atten_mask, block_table, out, lse)
+        quant = (dequant_scale_key, dequant_scale_value, dequant_offset_key, dequant_offset_value)
+        self._keep = (query, key, value, atten_mask, block_table, out, lse) + quant
         p = fia_params()
         fia_params_init(p)
         self._layout = input_layout.encode()
@@ -136,6 +139,10 @@ class FiaPlan:
         kp, kn, ka = _host_i64(actual_seq_kvlen)
         p.actual_seq_qlen, p.n_actual_seq_qlen = qp, qn
         p.actual_seq_kvlen, p.n_actual_seq_kvlen = kp, kn
+        self._qdesc = [describe(t) for t in quant]
+        (p.dequant_scale_key, p.dequant_scale_value, p.dequant_offset_key,
+         p.dequant_offset_value) = [ctypes.pointer(d) if d is not None else None for d in self._qdesc]
+        p.key_quant_mode, p.value_quant_mode = key_quant_mode, value_quant_mode
         st, ws, plan = fia_get_workspace_size(describe(query), describe(key), describe(value),
                                               describe(atten_mask), describe(block_table), p,
                                               describe(out),

@@ -45,6 +45,12 @@ class fia_params(ctypes.Structure):
         ("n_actual_seq_qlen", ctypes.c_int64),
         ("actual_seq_kvlen", ctypes.c_void_p),
         ("n_actual_seq_kvlen", ctypes.c_int64),
+        ("dequant_scale_key", ctypes.POINTER(fia_tensor)),
+        ("dequant_scale_value", ctypes.POINTER(fia_tensor)),
+        ("dequant_offset_key", ctypes.POINTER(fia_tensor)),
+        ("dequant_offset_value", ctypes.POINTER(fia_tensor)),
+        ("key_quant_mode", ctypes.c_int64),
+        ("value_quant_mode", ctypes.c_int64),
     ]
 
 

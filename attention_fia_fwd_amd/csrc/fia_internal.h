@@ -118,6 +118,16 @@ struct DecodeArgs {
     // masked; batch b's row starts at mask + b * mask_bstride (0: broadcast)
     const uint8_t* mask;
     int64_t mask_bstride;
+    // int8 key/value (kv pseudo-quantization): dequantized value
+    // scale * (x + offset); mode 0 per channel (bf16 [KV_N * D]), mode 1 per
+    // token (fp32 [B, tok_stride]); offsets nullable (0)
+    int32_t kv_i8;
+    int32_t kmode, vmode;
+    const void* k_scale;
+    const void* k_off;
+    const void* v_scale;
+    const void* v_off;
+    int64_t tok_stride;
     const int32_t* block_table;    // paged only
     int64_t bt_stride;
     int32_t block_size;            // paged only

@@ -986,6 +986,330 @@ __global__ __launch_bounds__(64) void decode_split(DecodeArgs a)
     }
 }
 
+// ---------------------------------------------------------------------------
+// Decode against an int8 KV cache (kv pseudo-quantization; contiguous KV, as
+// the pages allow it only without page attention).  A cached value x stands
+// for scale * (x + offset), per channel (bf16 scale/offset [KV_N * D]) or per
+// token (fp32 [B, KV_S]), K and V each with their own mode.  K bytes are read
+// as u = x + 128 (0..255, exact in bf16) for the bf16 QK MFMAs; V bytes as the
+// signed x (exact in fp16) for fp16 P V MFMAs, whose 11-bit P rounding keeps
+// the output error below that of the 16-bit path.  Each affine part goes
+// where it is cheapest:
+//   K per channel: s_j = sum_d q'_d u_jd + C, q'_d = q_d sk_d held as two bf16
+//                  parts hi + lo (two MFMAs per k-step, so q' keeps ~16 bits),
+//                  C = sum_d q'_d (ok_d - 128) per column;
+//   K per token:   s_j = sk_j (sum_d q_d u_jd + (ok_j - 128) sum_d q_d);
+//   V per token:   p_j sv_j feeds the P V MFMA and T = sum_j p_j sv_j ov_j per
+//                  column; partial O = (P' X + T) / l;
+//   V per channel: partial O = P X / l in raw units; the combine writes
+//                  sv_d (O_d + ov_d).
+// K comes straight into registers (lane (token n, quarter qd) holds the
+// contiguous d range [KB qd, KB qd + KB) of its row; Q uses the same d order);
+// V rows go direct-to-LDS as bytes and are widened into the swizzled bf16
+// layout the transposed reads of the 16-bit decode kernel use.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
+
+template <int D, int KM, int VM>
+__global__ __launch_bounds__(64) void decode_split_i8(DecodeArgs a)
+{
+    constexpr int ST = kDecodeStep;       // 32 tokens per step
+    constexpr int NK = D / 32;            // k-steps of S^T = K Q^T
+    constexpr int NO = D / 16;            // 16-row d tiles of O^T
+    constexpr int VCH = D / 8;            // 16-byte bf16 chunks per V row
+    constexpr int KB = NK * 8;            // K bytes per lane and token row
+    constexpr int NKL = KB / 16;          // 16-byte K loads per lane and sub-tile
+    constexpr int VCH8 = D / 16;          // 16-byte int8 chunks per V row
+    constexpr int RPI8 = 64 / VCH8;       // V rows per DMA instruction
+    constexpr int NVI8 = 16 / RPI8;       // DMA instructions per sub-tile
+    constexpr int NCV = ST * VCH8 / 64;   // int8 chunks each lane widens per step
+    static_assert(NKL >= 1 && NKL * 16 == KB && NVI8 >= 1 && NCV >= 1, "shape");
+    using O = Ops<FIA_BF16>;                 // Q K^T
+    using OV = Ops<FIA_F16>;                 // P V
+    __shared__ __attribute__((aligned(16))) uint16_t vbuf[ST * D];   // widened x (fp16), swizzled
+    __shared__ __attribute__((aligned(16))) uint8_t vst0[ST * D];    // bytes as loaded
+    __shared__ __attribute__((aligned(16))) uint8_t vst1[ST * D];
+
+    const int lane = threadIdx.x;
+    const int n = lane & 15, qd = lane >> 4;
+    const int wv = blockIdx.x;
+    const int p_end = a.wave_first[wv + 1];
+    auto vswz = [](int r) { return VCH >= 16 ? 2 * (r & 7) : 2 * ((r >> 1) & 3); };
+    for (int item = a.wave_first[wv]; item < p_end; ++item) {
+        const DecPiece pc_ = a.pieces[item];
+        const DecSeg db = a.segs[pc_.seg];
+        const int b = db.b;
+        const int hc = pc_.seg % a.nhc;
+        const int kvh = (pc_.seg / a.nhc) % a.KVN;
+        const int t0 = pc_.t0;
+        const int t1 = pc_.t1;
+        const int S = a.S;
+        const int r0 = kDecodeHeads * hc;
+        const int nh = min(kDecodeHeads, a.G * S - r0);
+        const int rq = r0 + n;
+        const int tq = rq % S;
+        const int hq = kvh * a.G + rq / S;
+        const float c = fmaxf(fabsf(a.scale_log2), kMinScale);
+        const float qsign = a.scale_log2 < 0.f ? -1.f : 1.f;
+        const int jbase = db.lkv - db.lq;
+        const int tq_min = (r0 % S) + nh > S ? 0 : r0 % S;
+        const int jmax = a.causal ? jbase + tq : INT32_MAX;
+        const int jmin = a.causal ? jbase + tq_min : INT32_MAX;
+
+        // Q^T as the B operand: column n, k-step s covers d = KB qd + 8 s + (0..7)
+        uint4 qf[NK], ql[NK];             // ql: low part of q' (K per channel)
+        float cpart = 0.f, qpart = 0.f;
+        if (n < nh) {
+            const uint16_t* src = (const uint16_t*)a.q + (int64_t)b * a.q_sB + (int64_t)hq * a.q_sH +
+                                  (int64_t)tq * a.q_sS + KB * qd;
+            const int64_t ch0 = (int64_t)kvh * D + KB * qd;
+#pragma unroll
+            for (int s = 0; s < NK; ++s) {
+                const uint4 v = *(const uint4*)(src + 8 * s);
+                const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+                float qv[8];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    qv[2 * e] = qsign * bf16_to_f32(w4[e] & 0xffffu);
+                    qv[2 * e + 1] = qsign * bf16_to_f32(w4[e] >> 16);
+                }
+                if constexpr (KM == 0) {
+                    const uint4 sv = *(const uint4*)((const uint16_t*)a.k_scale + ch0 + 8 * s);
+                    const uint4 ov = a.k_off ? *(const uint4*)((const uint16_t*)a.k_off + ch0 + 8 * s)
+                                             : make_uint4(0, 0, 0, 0);
+                    const uint32_t s4[4] = {sv.x, sv.y, sv.z, sv.w};
+                    const uint32_t o4[4] = {ov.x, ov.y, ov.z, ov.w};
+                    uint32_t pk[4], pl[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float x0 = qv[2 * e] * bf16_to_f32(s4[e] & 0xffffu);
+                        const float x1 = qv[2 * e + 1] * bf16_to_f32(s4[e] >> 16);
+                        pk[e] = O::pack2(x0, x1);
+                        const float h0 = bf16_to_f32(pk[e] & 0xffffu), h1 = bf16_to_f32(pk[e] >> 16);
+                        pl[e] = O::pack2(x0 - h0, x1 - h1);
+                        // C uses the q' = hi + lo that the MFMAs see
+                        const float y0 = h0 + bf16_to_f32(pl[e] & 0xffffu);
+                        const float y1 = h1 + bf16_to_f32(pl[e] >> 16);
+                        cpart += y0 * (bf16_to_f32(o4[e] & 0xffffu) - 128.f);
+                        cpart += y1 * (bf16_to_f32(o4[e] >> 16) - 128.f);
+                    }
+                    qf[s] = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+                    ql[s] = make_uint4(pl[0], pl[1], pl[2], pl[3]);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) qpart += qv[e];
+                    uint32_t pk[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) pk[e] = O::pack2(qv[2 * e], qv[2 * e + 1]);
+                    qf[s] = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int s = 0; s < NK; ++s) qf[s] = ql[s] = make_uint4(0, 0, 0, 0);
+        }
+        const float Cn = quad_sum(cpart);     // K per channel: constant of column n
+        const float Qs = quad_sum(qpart);     // K per token: sum_d q_d of column n
+
+        const int64_t tokstride = a.c_tok;
+        const int64_t hoff = db.kv_row0 * a.c_rowmul + (int64_t)kvh * a.c_head;
+        const uint8_t* kbase = (const uint8_t*)a.k + hoff;
+        const uint8_t* vbase = (const uint8_t*)a.v + hoff;
+        auto sub_rsrc = [&](const uint8_t* base, int tb) {
+            // rows [tb, t1) (at most 16) of the piece; rows past t1 read as zero
+            const int nvalid = min(16, t1 - tb);
+            const int64_t bytes = nvalid > 0 ? (int64_t)(nvalid - 1) * tokstride + D : 0;
+            return __builtin_amdgcn_make_buffer_rsrc((void*)(base + (int64_t)tb * tokstride), (short)0,
+                                                     (int)min(bytes, (int64_t)0x7fffffff), 0x00020000);
+        };
+        const float* ksrow = KM == 1 ? (const float*)a.k_scale + (int64_t)b * a.tok_stride : nullptr;
+        const float* korow = KM == 1 && a.k_off ? (const float*)a.k_off + (int64_t)b * a.tok_stride : nullptr;
+        const float* vsrow = VM == 1 ? (const float*)a.v_scale + (int64_t)b * a.tok_stride : nullptr;
+        const float* vorow = VM == 1 && a.v_off ? (const float*)a.v_off + (int64_t)b * a.tok_stride : nullptr;
+        // per-token values of the lane's 8 tokens of a step (0 past t1)
+        auto tok8 = [&](const float* row, int tt0, float (&out)[8]) {
+#pragma unroll
+            for (int r = 0; r < 8; ++r) {
+                const int tk = tt0 + 16 * (r >> 2) + 4 * qd + (r & 3);
+                out[r] = (row && tk < t1) ? row[tk] : 0.f;
+            }
+        };
+
+        const uint32_t k_voff = (uint32_t)(n * tokstride + KB * qd);
+        const int vr_in = lane / VCH8, vpc = lane % VCH8;
+        struct Tok { float ks[8], ko[8], vs[8], vo[8]; };
+        auto issue = [&](int tt0, uint4 (&kf)[2][NKL], uint8_t* vb, Tok& tk) {
+            if constexpr (KM == 1) { tok8(ksrow, tt0, tk.ks); tok8(korow, tt0, tk.ko); }
+            if constexpr (VM == 1) { tok8(vsrow, tt0, tk.vs); tok8(vorow, tt0, tk.vo); }
+#pragma unroll
+            for (int cc = 0; cc < 2; ++cc) {
+                const int tb = tt0 + 16 * cc;
+                const __amdgpu_buffer_rsrc_t kr = sub_rsrc(kbase, tb);
+#pragma unroll
+                for (int l = 0; l < NKL; ++l)
+                    kf[cc][l] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(kr, k_voff + 16 * l, 0, 0));
+                const __amdgpu_buffer_rsrc_t vr = sub_rsrc(vbase, tb);
+#pragma unroll
+                for (int u = 0; u < NVI8; ++u) {
+                    const int r = RPI8 * u + vr_in;
+                    dma16_tracked(vr, (uint16_t*)(vb + (16 * cc + RPI8 * u) * D), (uint32_t)(r * tokstride + 16 * vpc));
+                }
+            }
+        };
+        // bytes 8s .. 8s + 7 of the lane's K row part as 8 bf16 values u = x + 128
+        auto kop = [&](const uint4 (&raw)[NKL], int s) -> uint4 {
+            const uint4 q4 = raw[s / 2];
+            uint32_t w0 = (s & 1) ? q4.z : q4.x, w1 = (s & 1) ? q4.w : q4.y;
+            w0 ^= 0x80808080u;
+            w1 ^= 0x80808080u;
+            uint4 o;
+            o.x = O::pack2((float)(w0 & 0xffu), (float)((w0 >> 8) & 0xffu));
+            o.y = O::pack2((float)((w0 >> 16) & 0xffu), (float)(w0 >> 24));
+            o.z = O::pack2((float)(w1 & 0xffu), (float)((w1 >> 8) & 0xffu));
+            o.w = O::pack2((float)((w1 >> 16) & 0xffu), (float)(w1 >> 24));
+            return o;
+        };
+
+        // V^T A operand reads (as in the 16-bit kernel)
+        const int vi = lane & 15;
+        const int trow = 4 * qd + (vi >> 2);
+        const int tsw = vswz(trow);
+        const int tcol_lo = (vi & 3) >> 1, tsub = 4 * (vi & 1);
+
+        f32x4 acc[NO];
+#pragma unroll
+        for (int o = 0; o < NO; ++o) acc[o] = f32x4{0.f, 0.f, 0.f, 0.f};
+        float m = -INFINITY, l = 0.f, tpart = 0.f;
+        const float lazy_raw = kLazy / c;
+        const int nsteps = (t1 - t0 + ST - 1) / ST;
+
+        uint4 kfa[2][NKL], kfb[2][NKL];
+        Tok ta, tb_;
+        auto step = [&](int st, uint4 (&kcur)[2][NKL], uint4 (&knext)[2][NKL], uint8_t* vcur, uint8_t* vnext,
+                        const Tok& tcur, Tok& tnext) {
+            const int tt0 = t0 + ST * st;
+            if (st + 1 < nsteps) {
+                __builtin_amdgcn_s_waitcnt(FIA_LGKMCNT0);   // widening reads of the other byte buffer done
+                issue(tt0 + ST, knext, vnext, tnext);
+                // step st landed; the next step's K and V loads (issued after its
+                // per-token values) stay in flight
+                __builtin_amdgcn_s_waitcnt(FIA_VMCNT(2 * (NKL + NVI8)));
+            } else {
+                __builtin_amdgcn_s_waitcnt(FIA_VMCNT(0));
+            }
+            __syncthreads();
+            // widen this step's V bytes (signed) into the fp16 layout
+#pragma unroll
+            for (int i = 0; i < NCV; ++i) {
+                const int e = lane + 64 * i;
+                const int r = e / VCH8, c8 = e % VCH8;
+                const uint4 raw = *(const uint4*)(vcur + r * D + 16 * c8);
+                const uint32_t w4[4] = {raw.x, raw.y, raw.z, raw.w};
+                uint32_t pk[8];
+#pragma unroll
+                for (int e4 = 0; e4 < 4; ++e4) {
+                    const int w = (int)w4[e4];
+                    pk[2 * e4] = OV::pack2((float)((w << 24) >> 24), (float)((w << 16) >> 24));
+                    pk[2 * e4 + 1] = OV::pack2((float)((w << 8) >> 24), (float)(w >> 24));
+                }
+                *(uint4*)(vbuf + r * D + 8 * ((2 * c8) ^ vswz(r))) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+                *(uint4*)(vbuf + r * D + 8 * ((2 * c8 + 1) ^ vswz(r))) = make_uint4(pk[4], pk[5], pk[6], pk[7]);
+            }
+
+            f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < NK; ++s) {
+                const uint4 k0 = kop(kcur[0], s), k1 = kop(kcur[1], s);
+                s0 = O::mma16(k0, qf[s], s0);
+                s1 = O::mma16(k1, qf[s], s1);
+                if constexpr (KM == 0) {
+                    s0 = O::mma16(k0, ql[s], s0);
+                    s1 = O::mma16(k1, ql[s], s1);
+                }
+            }
+            float x[8];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                x[i] = s0[i];
+                x[4 + i] = s1[i];
+            }
+#pragma unroll
+            for (int r = 0; r < 8; ++r) {
+                if constexpr (KM == 0) x[r] += Cn;
+                else x[r] = tcur.ks[r] * (x[r] + (tcur.ko[r] - 128.f) * Qs);
+            }
+            if (tt0 + ST > t1 || tt0 + ST - 1 > jmin) {
+#pragma unroll
+                for (int r = 0; r < 8; ++r) {
+                    const int tk = tt0 + 16 * (r >> 2) + 4 * qd + (r & 3);
+                    if (tk >= t1 || tk > jmax) x[r] = -INFINITY;
+                }
+            }
+            float mt = x[0];
+#pragma unroll
+            for (int r = 1; r < 8; ++r) mt = fmaxf(mt, x[r]);
+            mt = quad_max(mt);
+            const float mn = fmaxf(m, mt);
+            const bool grow = (m == -INFINITY) ? (mn > -INFINITY) : (mn > m + lazy_raw);
+            if (__ballot(grow)) {
+                float alpha = 1.f;
+                if (m == -INFINITY) alpha = 0.f;
+                else if (mn != -INFINITY) alpha = fast_exp2((m - mn) * c);
+                m = mn;
+                l *= alpha;
+                tpart *= alpha;
+#pragma unroll
+                for (int o = 0; o < NO; ++o) acc[o] *= alpha;
+            }
+            const float mc = (m == -INFINITY) ? 0.f : m * c;
+            float ps = 0.f;
+#pragma unroll
+            for (int r = 0; r < 8; ++r) {
+                x[r] = fast_exp2(__builtin_fmaf(x[r], c, -mc));
+                ps += x[r];
+                if constexpr (VM == 1) {
+                    tpart += x[r] * tcur.vs[r] * tcur.vo[r];
+                    x[r] *= tcur.vs[r];
+                }
+            }
+            l += ps;
+            uint4 pb;
+            pb.x = OV::pack2(x[0], x[1]);
+            pb.y = OV::pack2(x[2], x[3]);
+            pb.z = OV::pack2(x[4], x[5]);
+            pb.w = OV::pack2(x[6], x[7]);
+#pragma unroll
+            for (int o = 0; o < NO; ++o) {
+                const int pc = (2 * o + tcol_lo) ^ tsw;
+                const uint2 lo = lds_read_tr16(vbuf + trow * D + 8 * pc + tsub);
+                const uint2 hi = lds_read_tr16(vbuf + (trow + 16) * D + 8 * pc + tsub);
+                acc[o] = OV::mma16(make_uint4(lo.x, lo.y, hi.x, hi.y), pb, acc[o]);
+            }
+        };
+
+        if (nsteps > 0) issue(t0, kfa, vst0, ta);
+        for (int st = 0; st < nsteps; st += 2) {
+            step(st, kfa, kfb, vst0, vst1, ta, tb_);
+            if (st + 1 < nsteps) step(st + 1, kfb, kfa, vst1, vst0, tb_, ta);
+        }
+
+        const float lt = quad_sum(l);
+        const float tt = quad_sum(tpart);
+        if (n < nh) {
+            const float inv = lt > 0.f ? 1.f / lt : 0.f;
+            float* po = a.part_o + ((int64_t)item * a.Gc + n) * D;
+#pragma unroll
+            for (int o = 0; o < NO; ++o) {
+                f32x4 v = (acc[o] + tt) * inv;
+                *(f32x4*)(po + 16 * o + 4 * qd) = v;
+            }
+            if (qd == 0)
+                a.part_lse[(int64_t)item * a.Gc + n] = lt > 0.f ? (m * c + __log2f(lt)) * kLn2 : -INFINITY;
+        }
+        __syncthreads();     // the LDS buffers are reused by the next piece
+    }
+}
+
 // Merge the kv splits of one (batch, head, query token): weights
 // exp(lse_s - max lse).  Tokens at or past the batch's query length are
 // written as out = 0, lse = +inf.
@@ -1024,7 +1348,15 @@ __global__ __launch_bounds__(64) void decode_combine(DecodeArgs a)
     const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
 #pragma unroll
     for (int e = 0; e < PER; ++e) {
-        const uint32_t pk = O::pack2(accv[e] * inv, 0.f);
+        float val = accv[e] * inv;
+        if (a.kv_i8 && a.vmode == 0 && wsum > 0.f) {
+            // int8 V per channel: the partials are in raw int8 units
+            const int64_t ch = (int64_t)kvh * D + lane + 64 * e;
+            const float sv = __uint_as_float((uint32_t)((const uint16_t*)a.v_scale)[ch] << 16);
+            const float ov = a.v_off ? __uint_as_float((uint32_t)((const uint16_t*)a.v_off)[ch] << 16) : 0.f;
+            val = sv * (val + ov);
+        }
+        const uint32_t pk = O::pack2(val, 0.f);
         op[lane + 64 * e] = (uint16_t)(pk & 0xffffu);
     }
     if (a.return_lse && lane == 0)
@@ -1088,10 +1420,22 @@ int launch_attn(const fia_plan& p, const AttnArgs& a, hipStream_t stream)
     return (int)hipGetLastError();
 }
 
+template <int D>
+void launch_split_i8(const fia_plan& p, const DecodeArgs& a, hipStream_t stream)
+{
+    const dim3 g((unsigned)p.n_waves), blk(64);
+    if (a.kmode == 0 && a.vmode == 0) hipLaunchKernelGGL((decode_split_i8<D, 0, 0>), g, blk, 0, stream, a);
+    else if (a.kmode == 0) hipLaunchKernelGGL((decode_split_i8<D, 0, 1>), g, blk, 0, stream, a);
+    else if (a.vmode == 0) hipLaunchKernelGGL((decode_split_i8<D, 1, 0>), g, blk, 0, stream, a);
+    else hipLaunchKernelGGL((decode_split_i8<D, 1, 1>), g, blk, 0, stream, a);
+}
+
 template <int DT, int D>
 int launch_dec(const fia_plan& p, const DecodeArgs& a, hipStream_t stream)
 {
-    if (p.n_waves > 0 && a.mask)
+    if (p.n_waves > 0 && a.kv_i8)
+        launch_split_i8<D>(p, a, stream);
+    else if (p.n_waves > 0 && a.mask)
         hipLaunchKernelGGL((decode_split<DT, D, true>), dim3((unsigned)p.n_waves), dim3(64), 0, stream, a);
     else if (p.n_waves > 0)
         hipLaunchKernelGGL((decode_split<DT, D, false>), dim3((unsigned)p.n_waves), dim3(64), 0, stream, a);

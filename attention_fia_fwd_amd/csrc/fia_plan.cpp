@@ -277,10 +277,22 @@ fia_status fia_get_workspace_size(const fia_tensor* query, const fia_tensor* key
     }
     if (!query->data || !key->data || !value->data || !attention_out->data) return FIA_ERR_NULLPTR;
 
-    // dtypes: q/k/v fp16 or bf16 and equal; output in the query dtype.
+    // dtypes: q/k/v fp16 or bf16 and equal; output in the query dtype.  KV
+    // pseudo-quantization: int8 key/value with a bf16 query and output, both
+    // dequant scales given (kv pseudo-quant constraints).
+    const bool kv_i8 = key->dtype == FIA_I8;
+    const bool any_quant = prm->dequant_scale_key || prm->dequant_scale_value ||
+                           prm->dequant_offset_key || prm->dequant_offset_value;
     if (!is_half(query->dtype)) return FIA_ERR_DTYPE;
-    if (key->dtype != query->dtype || value->dtype != query->dtype) return FIA_ERR_DTYPE;
     if (attention_out->dtype != query->dtype) return FIA_ERR_DTYPE;
+    if (kv_i8) {
+        if (value->dtype != FIA_I8 || query->dtype != FIA_BF16) return FIA_ERR_DTYPE;
+        if (!prm->dequant_scale_key || !prm->dequant_scale_value) return FIA_ERR_NULLPTR;
+        if (block_table) return FIA_ERR_PARAM;          // no page attention with pseudo-quant
+    } else {
+        if (key->dtype != query->dtype || value->dtype != query->dtype) return FIA_ERR_DTYPE;
+        if (any_quant) return FIA_ERR_PARAM;
+    }
 
     int32_t layout;
     bool bsh;
@@ -493,6 +505,52 @@ fia_status fia_get_workspace_size(const fia_tensor* query, const fia_tensor* key
                    mask == nullptr && (mode == 3 || mode == 0) && Dv == gq.D &&
                    (gq.D == 64 || gq.D == 128));
 
+    // ----- KV pseudo-quantization parameters -----
+    const void *k_scale = nullptr, *k_off = nullptr, *v_scale = nullptr, *v_off = nullptr;
+    int64_t tok_stride = 0;
+    if (kv_i8) {
+        if (layout == LAYOUT_TND || gq.S > kDecodeHeads) return FIA_ERR_PARAM;   // query S <= 16
+        if (!dec_kernel || mask) return FIA_ERR_UNSUPPORTED;
+        const int64_t km = prm->key_quant_mode, vm = prm->value_quant_mode;
+        if ((km != 0 && km != 1) || (vm != 0 && vm != 1)) return FIA_ERR_PARAM;
+        // per channel: bf16 [KV_N, D] or [KV_N * D]; per token: fp32 [B, KV_S'], KV_S' >= S_kv
+        auto check = [&](const fia_tensor* t, int64_t md, int64_t* stride) -> fia_status {
+            if (!t->data) return FIA_ERR_NULLPTR;
+            if (md == 0) {
+                if (t->dtype != FIA_BF16) return FIA_ERR_DTYPE;
+                if (!dims_are(t, {KVN, gq.D}) && !dims_are(t, {KVN * gq.D})) return FIA_ERR_SHAPE;
+            } else {
+                if (t->dtype != FIA_F32) return FIA_ERR_DTYPE;
+                if (t->ndim != 2 || t->dims[0] != B || t->dims[1] < Skv) return FIA_ERR_SHAPE;
+                *stride = t->dims[1];
+            }
+            return FIA_OK;
+        };
+        auto same = [](const fia_tensor* x, const fia_tensor* y) {
+            if (x->dtype != y->dtype || x->ndim != y->ndim) return false;
+            for (int i = 0; i < x->ndim; ++i)
+                if (x->dims[i] != y->dims[i]) return false;
+            return true;
+        };
+        int64_t ks = 0, vs = 0;
+        if ((st = check(prm->dequant_scale_key, km, &ks)) != FIA_OK) return st;
+        if ((st = check(prm->dequant_scale_value, vm, &vs)) != FIA_OK) return st;
+        if (km == 1 && vm == 1 && ks != vs) return FIA_ERR_SHAPE;
+        if (prm->dequant_offset_key) {
+            if (!prm->dequant_offset_key->data) return FIA_ERR_NULLPTR;
+            if (!same(prm->dequant_offset_key, prm->dequant_scale_key)) return FIA_ERR_SHAPE;
+        }
+        if (prm->dequant_offset_value) {
+            if (!prm->dequant_offset_value->data) return FIA_ERR_NULLPTR;
+            if (!same(prm->dequant_offset_value, prm->dequant_scale_value)) return FIA_ERR_SHAPE;
+        }
+        k_scale = prm->dequant_scale_key->data;
+        v_scale = prm->dequant_scale_value->data;
+        k_off = prm->dequant_offset_key ? prm->dequant_offset_key->data : nullptr;
+        v_off = prm->dequant_offset_value ? prm->dequant_offset_value->data : nullptr;
+        tok_stride = km == 1 ? ks : vs;
+    }
+
     if (dec_kernel) {
         p->kind = KIND_DECODE;
         DecodeArgs& d = p->dec;
@@ -509,6 +567,14 @@ fia_status fia_get_workspace_size(const fia_tensor* query, const fia_tensor* key
         d.causal = !decode && mode == 3;
         d.mask = decode ? mask : nullptr;     // S > 1 reaches here only without one
         d.mask_bstride = mask_bstride;
+        d.kv_i8 = kv_i8;
+        d.kmode = (int32_t)prm->key_quant_mode;
+        d.vmode = (int32_t)prm->value_quant_mode;
+        d.k_scale = k_scale;
+        d.k_off = k_off;
+        d.v_scale = v_scale;
+        d.v_off = v_off;
+        d.tok_stride = tok_stride;
         if (layout == LAYOUT_BNSD) {
             d.q_sB = QN * S * D; d.q_sH = S * D; d.q_sS = D;
         } else {

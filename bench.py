@@ -2,7 +2,7 @@
 """Benchmark of the MI355X fused inference attention forward.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2]
-                    [--secondary c1,c3,c4,c5,paged_prefill,mtp_decode]
+                    [--secondary c1,c3,c4,c5,paged_prefill,mtp_decode,int8_decode]
 
 One step is one fia_run (phase 2) of the headline workload: the GQA causal
 prefill, bf16, B=4, Q_N=32, KV_N=8, max S=4096, D=128, BSND, per-batch
@@ -15,10 +15,10 @@ skipped tiles are not counted).
 
 The other workloads (dense causal fp16 prefill, paged GQA decode, varlen TND
 prefill, block-sparse prefill, chunked prefill against a paged cache,
-multi-token decode against a paged cache) are timed the same way and reported
-under "secondary"; the two decode lines are in GB/s of algorithmic bytes
-(every KV byte of every kv head once, plus q, out, lse and the block-table
-entries read).
+multi-token decode against a paged cache, decode against an int8 KV cache) are
+timed the same way and reported under "secondary"; the decode lines are in
+GB/s of algorithmic bytes (every KV byte of every kv head once, plus q, out,
+lse, the block-table entries and the dequant scales read).
 
 The JSON line carries the roofline of the headline kernel (achieved from HIP
 events on the stream the kernel runs on) and the fp64 CPU oracle timed on a
@@ -88,7 +88,15 @@ def allowed_pairs_bsa(case) -> int:
 def decode_bytes(case) -> int:
     import numpy as np
     L = case.lkv.astype(np.int64)
-    kv = int(L.sum()) * case.KVN * (case.Dqk + case.Dv) * 2
+    kv = int(L.sum()) * case.KVN * (case.Dqk + case.Dv) * case.k.element_size()
+    if getattr(case, "quant", None):
+        # dequant scales/offsets: per channel whole, per token the tokens read
+        for key in ("dequant_scale_key", "dequant_offset_key", "dequant_scale_value",
+                    "dequant_offset_value"):
+            t = case.quant.get(key)
+            mode = case.quant["key_quant_mode" if "key" in key else "value_quant_mode"]
+            if t is not None:
+                kv += t.numel() * t.element_size() if mode == 0 else int(L.sum()) * 4
     rows = case.B * case.QN * case.Sq          # query rows (decode: S = 1)
     qo = rows * (case.Dqk + case.Dv) * 2
     lse = rows * 4 if case.return_lse else 0
@@ -156,7 +164,7 @@ def measure(name, steps, warmup):
     wall, ev = time_plan(plan, steps, warmup)
     res = {"workload": case.name, "steps": steps, "ms_per_step": wall * 1e3,
            "kernel_ms": ev * 1e3, "phase1_us": round(phase1_us, 1)}
-    if name in ("c3", "mtp_decode"):
+    if name in ("c3", "mtp_decode", "int8_decode"):
         nbytes = decode_bytes(case)
         res.update(value=nbytes / wall / 1e9, unit="GB/s", algorithmic_bytes=nbytes,
                    roofline={"bound": "hbm", "achieved": nbytes / ev / 1e9, "peak": PEAK_HBM_GBS,
@@ -222,7 +230,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="c2")
-    ap.add_argument("--secondary", default="c1,c3,c4,c5,paged_prefill,mtp_decode",
+    ap.add_argument("--secondary", default="c1,c3,c4,c5,paged_prefill,mtp_decode,int8_decode",
                     help="comma list of other workloads to time ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",

@@ -124,6 +124,23 @@ typedef struct fia_params {
     int64_t        n_actual_seq_qlen;
     const int64_t* actual_seq_kvlen;
     int64_t        n_actual_seq_kvlen;
+    /* KV pseudo-quantization (kv pseudo-quant parameters and their
+     * constraints, v2 page): int8 key and value with a bf16 query and output,
+     * a contiguous KV cache (no block_table) and query S <= 16 (S > 1:
+     * sparse_mode 3, or 0 without a mask, with G * S <= 16).  A cached value x
+     * stands for scale * (x + offset).  key_quant_mode / value_quant_mode:
+     *   0  per channel: scale / offset bf16 [KV_N, D] or [KV_N * D];
+     *   1  per token:   scale / offset fp32 [B, KV_S'] with KV_S' >= the
+     *      key's S (both per token: one shape for key and value).
+     * Offsets are optional (NULL = 0) and take their scale's shape and dtype.
+     * Both scales are required for int8 key/value and must be NULL for
+     * fp16/bf16 key/value (FIA_ERR_PARAM).  The plan keeps the pointers. */
+    const fia_tensor* dequant_scale_key;
+    const fia_tensor* dequant_scale_value;
+    const fia_tensor* dequant_offset_key;
+    const fia_tensor* dequant_offset_value;
+    int64_t key_quant_mode;
+    int64_t value_quant_mode;
 } fia_params;
 
 /* Fill `p` with the defaults listed above (layout "BSH", scale 1.0,

@@ -53,6 +53,10 @@ class _Args(ctypes.Structure):
         ("block_mask", ctypes.c_void_p), ("nqb", ctypes.c_int64), ("nkb", ctypes.c_int64),
         ("X", ctypes.c_int64), ("Y", ctypes.c_int64),
         ("rows", ctypes.c_void_p), ("n_rows", ctypes.c_int64),
+        ("kv_i8", ctypes.c_int32), ("kmode", ctypes.c_int32), ("vmode", ctypes.c_int32),
+        ("k_scale", ctypes.c_void_p), ("k_off", ctypes.c_void_p),
+        ("v_scale", ctypes.c_void_p), ("v_off", ctypes.c_void_p),
+        ("tok_stride", ctypes.c_int64),
     ]
 
 
@@ -82,8 +86,15 @@ def read_half(bits: int, dtype: torch.dtype) -> float:
 
 def _bits(t: torch.Tensor) -> np.ndarray:
     t = t.detach().to("cpu").contiguous()
+    if t.dtype == torch.int8:
+        return t.numpy()
     assert t.dtype in (torch.float16, torch.bfloat16), t.dtype
     return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def _exact_f64(t: torch.Tensor) -> np.ndarray:
+    # bf16 / fp32 values widened exactly to double
+    return np.ascontiguousarray(t.detach().to("cpu").to(torch.float64).numpy().reshape(-1))
 
 
 def _ptr(a: np.ndarray):
@@ -170,6 +181,19 @@ def attention(case, rows=None):
         a.bt_stride = bt.shape[1]
         a.block_size = case.block_size
         a.pool_layout = case.pool_layout
+    quant = getattr(case, "quant", None)
+    if quant is not None:
+        a.kv_i8 = 1
+        a.kmode, a.vmode = int(quant["key_quant_mode"]), int(quant["value_quant_mode"])
+        for fld, key in (("k_scale", "dequant_scale_key"), ("k_off", "dequant_offset_key"),
+                         ("v_scale", "dequant_scale_value"), ("v_off", "dequant_offset_value")):
+            t = quant.get(key)
+            if t is not None:
+                arr = _exact_f64(t)
+                keep.append(arr)
+                setattr(a, fld, _ptr(arr))
+                if (fld[0] == "k" and a.kmode == 1) or (fld[0] == "v" and a.vmode == 1):
+                    a.tok_stride = t.shape[-1]
     r, n = _rows_arg(rows)
     if r is not None:
         keep.append(r)

@@ -49,6 +49,13 @@
  * kv-blocks kb < ceil(Lkv_b / Y) in ascending order (tail -1).
  *
  * Inputs are fp16/bf16 bit patterns, each read as its exact value in double.
+ *
+ * KV pseudo-quantization (v2 page, kv pseudo-quant parameters): key and value
+ * hold int8 values x; each stands for scale * (x + offset) (the page's table
+ * of the quantization formulas is lost; this affine reading is taken), with
+ *   mode 0 (per channel): scale[g][d], offset[g][d] of kv head g, channel d;
+ *   mode 1 (per token):   scale[b][j], offset[b][j] of batch b, kv token j;
+ * the scales and offsets are passed in as exact double values.
  */
 #include <math.h>
 #include <stdint.h>
@@ -117,6 +124,14 @@ typedef struct {
     /* optional row subset: n_rows triples (b, h, i); NULL = every row */
     const int64_t* rows;
     int64_t n_rows;
+    /* int8 key/value (KV pseudo-quantization); offsets may be NULL (0) */
+    int32_t kv_i8;
+    int32_t kmode, vmode;            /* 0 per channel [KVN * D], 1 per token [B, tok_stride] */
+    const double* k_scale;
+    const double* k_off;
+    const double* v_scale;
+    const double* v_off;
+    int64_t tok_stride;
 } oracle_args;
 
 static int64_t q_off(const oracle_args* a, int64_t b, int64_t h, int64_t i, int64_t D)
@@ -176,9 +191,24 @@ static int allowed_bsa(const oracle_args* a, int64_t b, int64_t h, int64_t i, in
     return a->block_mask[((b * a->QN + h) * a->nqb + qb) * a->nkb + kb] != 0;
 }
 
+/* Element d of key (is_v = 0) or value (is_v = 1) token j of kv head g,
+ * batch b, at flat index idx of the tensor. */
+static double kv_elem(const oracle_args* a, const void* t, int64_t idx, int is_v, int64_t b,
+                      int64_t g, int64_t j, int64_t d, int64_t D)
+{
+    if (!a->kv_i8)
+        return elem((const uint16_t*)t, idx, a->dtype);
+    const double x = (double)((const int8_t*)t)[idx];
+    const int md = is_v ? a->vmode : a->kmode;
+    const double* sc = is_v ? a->v_scale : a->k_scale;
+    const double* of = is_v ? a->v_off : a->k_off;
+    const int64_t p = md == 0 ? g * D + d : b * a->tok_stride + j;
+    return sc[p] * (x + (of ? of[p] : 0.0));
+}
+
 /* One output row: out[0..Dv) and *lse.  Returns 0, or -1 on allocation failure. */
-static int one_row(const oracle_args* a, const uint16_t* q, const uint16_t* k,
-                   const uint16_t* v, int bsa, int64_t b, int64_t h, int64_t i,
+static int one_row(const oracle_args* a, const uint16_t* q, const void* k,
+                   const void* v, int bsa, int64_t b, int64_t h, int64_t i,
                    double* out, double* lse)
 {
     int64_t e;
@@ -209,7 +239,7 @@ static int one_row(const oracle_args* a, const uint16_t* q, const uint16_t* k,
         const int64_t ko = kv_off(a, b, g, j, a->Dqk);
         double acc = 0.0;
         for (d = 0; d < a->Dqk; ++d)
-            acc += elem(q, qo + d, a->dtype) * elem(k, ko + d, a->dtype);
+            acc += elem(q, qo + d, a->dtype) * kv_elem(a, k, ko + d, 0, b, g, j, d, a->Dqk);
         s[j] = a->scale * acc;
         if (s[j] > m)
             m = s[j];
@@ -224,7 +254,7 @@ static int one_row(const oracle_args* a, const uint16_t* q, const uint16_t* k,
             const int64_t vo = kv_off(a, b, g, j, a->Dv);
             l += p;
             for (e = 0; e < a->Dv; ++e)
-                out[e] += p * elem(v, vo + e, a->dtype);
+                out[e] += p * kv_elem(a, v, vo + e, 1, b, g, j, e, a->Dv);
         }
         for (e = 0; e < a->Dv; ++e)
             out[e] /= l;
@@ -238,7 +268,7 @@ static int one_row(const oracle_args* a, const uint16_t* q, const uint16_t* k,
 /* Output addressing: out follows the query layout with D = Dv; lse is
  * [B, QN, Sq] (TND: [T, QN]).  With a row subset, out is [n_rows, Dv] and
  * lse is [n_rows]. */
-static int run(const oracle_args* a, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+static int run(const oracle_args* a, const uint16_t* q, const void* k, const void* v,
                int bsa, double* out, double* lse)
 {
     int failed = 0;
@@ -283,10 +313,12 @@ static int run(const oracle_args* a, const uint16_t* q, const uint16_t* k, const
     return failed ? -1 : 0;
 }
 
-int oracle_attention(const oracle_args* a, const uint16_t* q, const uint16_t* k,
-                     const uint16_t* v, double* out, double* lse)
+int oracle_attention(const oracle_args* a, const uint16_t* q, const void* k,
+                     const void* v, double* out, double* lse)
 {
     if (!a || !q || !k || !v || !out || !lse || a->KVN <= 0 || a->QN % a->KVN)
+        return -2;
+    if (a->kv_i8 && (!a->k_scale || !a->v_scale))
         return -2;
     return run(a, q, k, v, 0, out, lse);
 }
@@ -295,7 +327,7 @@ int oracle_block_sparse(const oracle_args* a, const uint16_t* q, const uint16_t*
                         const uint16_t* v, double* out, double* lse)
 {
     if (!a || !q || !k || !v || !out || !lse || !a->block_mask || a->X <= 0 || a->Y <= 0 ||
-        a->KVN <= 0 || a->QN % a->KVN)
+        a->KVN <= 0 || a->QN % a->KVN || a->kv_i8)
         return -2;
     return run(a, q, k, v, 1, out, lse);
 }

@@ -22,6 +22,11 @@ def to_dev(case, device="cuda"):
         t = getattr(case, name, None)
         if t is not None and t.device.type != "cuda":
             setattr(case, name, t.to(device))
+    quant = getattr(case, "quant", None)
+    if quant:
+        for key, t in quant.items():
+            if isinstance(t, torch.Tensor) and t.device.type != "cuda":
+                quant[key] = t.to(device)
     return case
 
 
@@ -39,6 +44,8 @@ def fia_plan(case, **over):
         kw["actual_seq_qlen"] = ql
     if kl is not None:
         kw["actual_seq_kvlen"] = kl
+    if getattr(case, "quant", None):
+        kw.update(case.quant)
     kw.update(over)
     return fia.FiaPlan(case.q, case.k, case.v, **kw)
 

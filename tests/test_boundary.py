@@ -3,6 +3,7 @@ function include/fia.h declares, and phase 1 validates inputs with the
 status codes the header documents (constraints of the fused-infer-attention
 and block-sparse pages).  Phase 1 never launches or reads device data, so
 CPU tensors stand in for device tensors here."""
+import ctypes
 import os
 import re
 
@@ -240,6 +241,56 @@ def test_decode_atten_mask_validation():
     assert code(torch.zeros(B, S - 1, dtype=torch.uint8)) == _abi.FIA_ERR_SHAPE
     assert code(torch.zeros(3, S, dtype=torch.uint8)) == _abi.FIA_ERR_SHAPE
     assert code(torch.zeros(B, S, dtype=torch.float16)) == _abi.FIA_ERR_DTYPE
+
+
+def test_int8_kv_validation():
+    B, QN, KVN, S, D = 2, 8, 2, 40, 128
+    q = torch.zeros(B, QN, 1, D, dtype=torch.bfloat16)
+    k8 = torch.zeros(B, KVN, S, D, dtype=torch.int8)
+    ch = torch.ones(KVN, D, dtype=torch.bfloat16)
+    tok = torch.ones(B, S, dtype=torch.float32)
+
+    def code(q=q, k=k8, ks=ch, vs=ch, ko=None, vo=None, km=0, vm=0, bt=None, block_size=0,
+             mode=0):
+        p = _params(num_heads=QN, num_key_value_heads=KVN, input_layout="BNSD",
+                    block_size=block_size, sparse_mode=mode)
+        keep = []
+        for fld, t in (("dequant_scale_key", ks), ("dequant_scale_value", vs),
+                       ("dequant_offset_key", ko), ("dequant_offset_value", vo)):
+            if t is not None:
+                d = fia.describe(t)
+                keep.append((t, d))
+                setattr(p, fld, ctypes.pointer(d))
+        p.key_quant_mode, p.value_quant_mode = km, vm
+        if bt is not None:
+            lk = np.array([S, S], dtype=np.int64)
+            keep.append(lk)
+            p.actual_seq_kvlen, p.n_actual_seq_kvlen = lk.ctypes.data, 2
+        return _phase1(q, k, k, p, bt=bt)[0]
+
+    assert code() == _abi.FIA_OK
+    assert code(ks=tok, vs=tok, km=1, vm=1) == _abi.FIA_OK
+    assert code(vs=tok, vm=1, ko=ch) == _abi.FIA_OK
+    assert code(ks=ch.reshape(-1), vs=ch.reshape(-1)) == _abi.FIA_OK
+    assert code(q=q.half()) == _abi.FIA_ERR_DTYPE                 # query must be bf16
+    assert code(ks=None) == _abi.FIA_ERR_NULLPTR
+    assert code(km=2) == _abi.FIA_ERR_PARAM
+    assert code(ks=ch.float()) == _abi.FIA_ERR_DTYPE              # per channel: bf16
+    assert code(ks=tok.to(torch.bfloat16), km=1) == _abi.FIA_ERR_DTYPE
+    assert code(ks=torch.ones(KVN, D + 1, dtype=torch.bfloat16)) == _abi.FIA_ERR_SHAPE
+    assert code(ks=torch.ones(B, S - 1), km=1) == _abi.FIA_ERR_SHAPE
+    assert code(ks=tok, vs=torch.ones(B, S + 3), km=1, vm=1) == _abi.FIA_ERR_SHAPE
+    assert code(ko=torch.ones(KVN, D)) == _abi.FIA_ERR_SHAPE      # offset: its scale's dtype
+    # no page attention with pseudo-quant
+    pool = torch.zeros(2, KVN, 128, D, dtype=torch.int8)
+    assert code(k=pool, bt=torch.zeros(B, 1, dtype=torch.int32), block_size=128) == _abi.FIA_ERR_PARAM
+    # query S <= 16; G * S > 16 is not provided
+    assert code(q=torch.zeros(B, QN, 17, D, dtype=torch.bfloat16), mode=3) == _abi.FIA_ERR_PARAM
+    assert code(q=torch.zeros(B, QN, 5, D, dtype=torch.bfloat16), mode=3) == _abi.FIA_ERR_UNSUPPORTED
+    assert code(q=torch.zeros(B, QN, 2, D, dtype=torch.bfloat16), mode=3) == _abi.FIA_OK
+    # dequant tensors with fp16/bf16 key/value
+    kb = torch.zeros(B, KVN, S, D, dtype=torch.bfloat16)
+    assert code(k=kb) == _abi.FIA_ERR_PARAM
 
 
 def test_tnd_requires_cumulative_lengths():

@@ -612,3 +612,76 @@ def test_workload_generator_is_deterministic():
     assert torch.equal(a.q, b.q) and torch.equal(a.k, b.k) and torch.equal(a.v, b.v)
     assert list(W.c2_lengths()) == list(W.c2_lengths())
     assert W.c4_lengths().min() >= 64 and W.c4_lengths().max() <= 8192
+
+
+# ---------------------------------------------------------------------------
+# KV pseudo-quantization (int8 key/value, value = scale * (x + offset))
+# ---------------------------------------------------------------------------
+
+def _dequantized(case):
+    """bf16 copy of an int8 case with the dequantized cache, built with
+    torch ops from the same reading; exact when the values fit bf16."""
+    qt = case.quant
+    B, KVN, D = case.B, case.KVN, case.Dqk
+
+    def deq(x, mode, sc, of):
+        xb = x.to(torch.float64)
+        if case.layout == "BNSD":
+            xb = xb                                   # [B, KVN, S, D]
+        else:
+            xb = xb.permute(0, 2, 1, 3)               # BSND -> [B, KVN, S, D]
+        if mode == 0:
+            s = sc.to(torch.float64).reshape(1, KVN, 1, D)
+            o = of.to(torch.float64).reshape(1, KVN, 1, D) if of is not None else 0.0
+        else:
+            S = xb.shape[2]
+            s = sc.to(torch.float64)[:, :S].reshape(B, 1, S, 1)
+            o = of.to(torch.float64)[:, :S].reshape(B, 1, S, 1) if of is not None else 0.0
+        y = s * (xb + o)
+        if case.layout != "BNSD":
+            y = y.permute(0, 2, 1, 3)
+        yb = y.to(torch.bfloat16)
+        assert torch.equal(yb.to(torch.float64), y), "dequantized cache not exact in bf16"
+        return yb.contiguous()
+
+    k = deq(case.k, qt["key_quant_mode"], qt["dequant_scale_key"], qt["dequant_offset_key"])
+    v = deq(case.v, qt["value_quant_mode"], qt["dequant_scale_value"], qt["dequant_offset_value"])
+    ref = W.make_fia(layout=case.layout, dtype=torch.bfloat16, B=B, QN=case.QN, KVN=KVN,
+                     Sq=case.Sq, Skv=case.Skv, Dqk=D, lkv=case.lkv, sparse_mode=case.sparse_mode,
+                     seed=0)
+    ref.q, ref.k, ref.v = case.q, k, v
+    return ref
+
+
+@pytest.mark.parametrize("kmode, vmode", [(0, 0), (1, 1), (0, 1), (1, 0)])
+@pytest.mark.parametrize("layout", ["BNSD", "BSND"])
+def test_int8_kv_equals_bf16_on_the_dequantized_cache(kmode, vmode, layout):
+    # power-of-two scales and integer offsets: the dequantized cache is exact
+    # in bf16, so the int8 oracle must equal the bf16 oracle on it exactly
+    case = W.make_quant_decode(layout=layout, B=3, QN=4, KVN=2, D=16, lkv=[40, 3, 17],
+                               kmode=kmode, vmode=vmode, pow2=True, seed=70 + 2 * kmode + vmode)
+    out, lse = oracle.attention(case)
+    ro, rl = oracle.attention(_dequantized(case))
+    np.testing.assert_array_equal(out, ro)
+    np.testing.assert_array_equal(lse, rl)
+
+
+def test_int8_kv_unit_scale_is_the_raw_integers():
+    case = W.make_quant_decode(layout="BNSD", B=2, QN=2, KVN=1, D=8, lkv=[9, 4], kmode=1, vmode=0,
+                               unit=True, seed=75)
+    out, lse = oracle.attention(case)
+    ref = W.make_fia(layout="BNSD", dtype=torch.bfloat16, B=2, QN=2, KVN=1, Sq=1, Skv=9, Dqk=8,
+                     lkv=[9, 4], seed=0)
+    ref.q, ref.k, ref.v = case.q, case.k.to(torch.bfloat16), case.v.to(torch.bfloat16)
+    ro, rl = oracle.attention(ref)
+    np.testing.assert_array_equal(out, ro)
+    np.testing.assert_array_equal(lse, rl)
+
+
+def test_int8_kv_multi_token_causal():
+    case = W.make_quant_decode(layout="BNSD", B=2, QN=4, KVN=2, D=16, Sq=3, lkv=[20, 2],
+                               kmode=0, vmode=1, pow2=True, sparse_mode=3, seed=76)
+    out, lse = oracle.attention(case)
+    ro, rl = oracle.attention(_dequantized(case))
+    np.testing.assert_array_equal(out, ro)
+    np.testing.assert_array_equal(lse, rl)

@@ -53,6 +53,13 @@ def normal_tensor(shape, dtype: torch.dtype, ss: np.random.SeedSequence,
     return x.to(dtype)
 
 
+def int8_tensor(shape, ss: np.random.SeedSequence, device: str = "cpu") -> torch.Tensor:
+    """iid integers uniform in [-127, 127] as int8 on ``device``."""
+    g = torch.Generator(device=device)
+    g.manual_seed(_torch_seed(ss))
+    return torch.randint(-127, 128, tuple(shape), generator=g, device=device, dtype=torch.int8)
+
+
 @dataclass
 class FiaCase:
     """One fused-infer-attention invocation with its inputs."""
@@ -81,6 +88,10 @@ class FiaCase:
     pool_layout: int = 0        # 0: (NB, KVN, bs, D)   1: (NB, bs, KVN*D)
     return_lse: bool = True
     meta: dict = field(default_factory=dict)
+    # int8 key/value: {"dequant_scale_key": t, "dequant_scale_value": t,
+    # "dequant_offset_key": t|None, "dequant_offset_value": t|None,
+    # "key_quant_mode": 0|1, "value_quant_mode": 0|1}
+    quant: Optional[dict] = None
 
     @property
     def decode(self) -> bool:
@@ -323,6 +334,52 @@ def make_paged_prefill(name="custom", *, layout="BNSD", dtype=torch.bfloat16, B=
                    pool_layout=pool_layout, return_lse=return_lse, meta={"NB": NB})
 
 
+def make_quant_decode(name="custom", *, layout="BNSD", B=2, QN=4, KVN=2, D=64, Sq=1, Skv=None,
+                      lkv=(100, 37), kmode=0, vmode=0, offsets=True, sparse_mode=0, scale=None,
+                      seed=0, device="cpu", pow2=False, unit=False, return_lse=True) -> FiaCase:
+    """Decode (query S <= 16) against an int8 KV cache (kv pseudo-quantization):
+    bf16 query, int8 key/value uniform in [-127, 127], each value standing for
+    scale * (x + offset).  Mode 0 (per channel): bf16 scale ~ U[0.004, 0.02],
+    offset ~ U[-8, 8], shape [KV_N, D]; mode 1 (per token): fp32, shape
+    [B, KV_S].  ``pow2``: scales 2^-k (k in 5..7) and integer offsets (the
+    dequantized cache is then exact in bf16); ``unit``: scale 1, offset 0."""
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    ss = _streams(seed)
+    lkv = np.asarray(lkv, dtype=np.int64)
+    Skv = int(lkv.max()) if Skv is None else Skv
+    q = normal_tensor(_shape(layout, B, QN, Sq, D), torch.bfloat16, ss[STREAM_Q], device)
+    kshape = _shape(layout, B, KVN, Skv, D)
+    k = int8_tensor(kshape, ss[STREAM_K], device)
+    v = int8_tensor(kshape, ss[STREAM_V], device)
+    prng = np.random.default_rng(ss[STREAM_MASK])
+
+    def params(mode):
+        shp = (KVN, D) if mode == 0 else (B, Skv)
+        dt = torch.bfloat16 if mode == 0 else torch.float32
+        if unit:
+            sc, of = np.ones(shp), np.zeros(shp)
+        elif pow2:
+            sc = 2.0 ** -prng.integers(5, 8, size=shp)
+            of = prng.integers(-8, 9, size=shp).astype(np.float64)
+        else:
+            sc = prng.uniform(0.004, 0.02, size=shp)
+            of = prng.uniform(-8.0, 8.0, size=shp)
+        st = torch.from_numpy(sc).to(dt).to(device)
+        ot = torch.from_numpy(of).to(dt).to(device) if offsets else None
+        return st, ot
+
+    ks, ko = params(kmode)
+    vs, vo = params(vmode)
+    quant = {"dequant_scale_key": ks, "dequant_scale_value": vs, "dequant_offset_key": ko,
+             "dequant_offset_value": vo, "key_quant_mode": kmode, "value_quant_mode": vmode}
+    mask = None
+    if sparse_mode == 3 and Sq > 1:
+        mask = torch.triu(torch.ones(2048, 2048, dtype=torch.uint8), diagonal=1).to(device)
+    return FiaCase(name=name, layout=layout, dtype=torch.bfloat16, B=B, QN=QN, KVN=KVN, Sq=Sq,
+                   Skv=Skv, Dqk=D, Dv=D, scale=scale, sparse_mode=sparse_mode, lq=None, lkv=lkv,
+                   q=q, k=k, v=v, atten_mask=mask, return_lse=return_lse, quant=quant)
+
+
 def make_bsa(name="custom", *, layout="BNSD", dtype=torch.bfloat16, B=1, QN=2, KVN=1,
              Sq=256, Skv=None, D=64, X=128, Y=128, p=0.25, lq=None, lkv=None, scale=None,
              seed=0, device="cpu", mask_kind="bernoulli", return_lse=True) -> BsaCase:
@@ -464,6 +521,17 @@ def paged_mtp_decode_bf16(device="cpu") -> FiaCase:
                               mask_kind="template", seed=1007, device=device)
 
 
+def int8_kv_decode_bf16(device="cpu") -> FiaCase:
+    """Decode against an int8 KV cache with per-channel scales and offsets:
+    B=64, Q_S=1, Q_N=32, KV_N=8, D=128, bf16 query, BNSD, contiguous int8
+    K/V [64, 8, 32768, 128], KV lengths ~ U{512..32768}, LSE on."""
+    rng = np.random.default_rng(_streams(1008)[STREAM_LENGTHS])
+    lkv = rng.integers(512, 32768, size=64, endpoint=True).astype(np.int64)
+    return make_quant_decode("int8_kv_decode_perchannel_b64_n32_kv8_d128", layout="BNSD", B=64,
+                             QN=32, KVN=8, D=128, Skv=32768, lkv=lkv, kmode=0, vmode=0,
+                             seed=1008, device=device)
+
+
 WORKLOADS = {
     "c1": c1_dense_causal_fp16,
     "c2": c2_gqa_causal_bf16,
@@ -472,4 +540,5 @@ WORKLOADS = {
     "c5": c5_block_sparse_bf16,
     "paged_prefill": paged_chunked_prefill_bf16,
     "mtp_decode": paged_mtp_decode_bf16,
+    "int8_decode": int8_kv_decode_bf16,
 }
