@@ -287,7 +287,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd(AttnArgs a)
     // t.q0 + 32 (w / hg) + (0..31).
     const int hg = BSA ? 1 : a.hg;
     const Tile t = a.tiles[blockIdx.x];
-    const BatchInfo bi = a.batch[t.b];
+    const BatchInfo bi = t.bi;
     if (!BSA && t.h < 0) {
         // zero fill: padding rows [t.q0, t.q1) of batch t.b, every head
         const BatchInfo& zb = bi;

@@ -755,13 +755,14 @@ fia_status fia_get_workspace_size(const fia_tensor* query, const fia_tensor* key
         const int64_t rows = layout == LAYOUT_TND ? lq[(size_t)b] : gq.S;
         const int64_t zfrom = std::min(rows, (lq[(size_t)b] + rows_per - 1) / rows_per * rows_per);
         for (int64_t z0 = zfrom; z0 < rows; z0 += zrows)
-            zero_fill.push_back(Tile{(int32_t)b, -1, (int32_t)z0, (int32_t)std::min(z0 + zrows, rows)});
+            zero_fill.push_back(Tile{(int32_t)b, -1, (int32_t)z0, (int32_t)std::min(z0 + zrows, rows),
+                                     bi[(size_t)b]});
         for (int64_t q0 = 0; q0 < zfrom; q0 += rows_per) {
             const int64_t q1 = std::min<int64_t>(q0 + rows_per, rows);
             const int64_t w = kv_tiles_of(mode, mask != nullptr, a.pre, a.next, lq[(size_t)b],
                                           lkv[(size_t)b], q0, q1);
             for (int64_t h = 0; h < QN; h += hg)
-                tl.push_back({w, Tile{(int32_t)b, (int32_t)h, (int32_t)q0, (int32_t)q1}});
+                tl.push_back({w, Tile{(int32_t)b, (int32_t)h, (int32_t)q0, (int32_t)q1, bi[(size_t)b]}});
         }
     }
     std::stable_sort(tl.begin(), tl.end(), [](const W& x, const W& y) { return x.work > y.work; });
@@ -964,7 +965,7 @@ fia_status bsa_get_workspace_size(const fia_tensor* query, const fia_tensor* key
             for (int64_t q0 = qb * X; q0 < bend; q0 += kBlockMSparse) {
                 const int64_t q1 = std::min<int64_t>(q0 + kBlockMSparse, bend);
                 for (int64_t h = 0; h < N1; ++h)
-                    tiles.push_back(Tile{(int32_t)b, (int32_t)h, (int32_t)q0, (int32_t)q1});
+                    tiles.push_back(Tile{(int32_t)b, (int32_t)h, (int32_t)q0, (int32_t)q1, bi[(size_t)b]});
             }
         }
     }
