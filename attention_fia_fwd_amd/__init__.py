@@ -33,6 +33,7 @@ _DTYPES = {
     torch.float16: _abi.FIA_F16, torch.bfloat16: _abi.FIA_BF16, torch.float32: _abi.FIA_F32,
     torch.int8: _abi.FIA_I8, torch.uint8: _abi.FIA_U8, torch.bool: _abi.FIA_BOOL,
     torch.int32: _abi.FIA_I32, torch.int64: _abi.FIA_I64,
+    torch.float8_e4m3fn: _abi.FIA_F8E4M3,
 }
 
 
@@ -181,10 +182,13 @@ class BsaPlan:
                  num_key_value_heads: int = 0, scale_value: float = 1.0,
                  block_shape=(128, 128), input_layout: str = "BNSD",
                  actual_seq_lengths=None, actual_seq_lengths_kv=None,
-                 softmax_lse_flag: bool = False, out=None, lse=None):
+                 softmax_lse_flag: bool = False, dequant_scale_query=None,
+                 dequant_scale_key=None, dequant_scale_value=None, out=None, lse=None):
         self.plan = None
         if out is None:
-            out = torch.empty_like(query)
+            # FP8 inputs give a bf16 output
+            odt = torch.bfloat16 if query.dtype == torch.float8_e4m3fn else query.dtype
+            out = torch.empty(query.shape, dtype=odt, device=query.device)
         if softmax_lse_flag and lse is None:
             if input_layout == "TND":
                 lse = torch.empty(query.shape[0], num_heads, 1, dtype=torch.float32,
@@ -194,9 +198,13 @@ class BsaPlan:
                 lse = torch.empty(query.shape[0], num_heads, S, 1, dtype=torch.float32,
                                   device=query.device)
         self.out, self.lse = out, (lse if softmax_lse_flag else None)
-        self._keep = (query, key, value, block_sparse_mask, out, lse)
+        scales = (dequant_scale_query, dequant_scale_key, dequant_scale_value)
+        self._keep = (query, key, value, block_sparse_mask, out, lse) + scales
         p = bsa_params()
         bsa_params_init(p)
+        self._sdesc = [describe(t) for t in scales]
+        p.dequant_scale_query, p.dequant_scale_key, p.dequant_scale_value = [
+            ctypes.pointer(d) if d is not None else None for d in self._sdesc]
         self._layout = input_layout.encode()
         p.q_input_layout = self._layout
         p.kv_input_layout = self._layout

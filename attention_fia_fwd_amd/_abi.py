@@ -21,7 +21,7 @@ FIA_ERR_WORKSPACE = 7
 FIA_ERR_HIP = 8
 
 # fia_dtype
-FIA_F16, FIA_BF16, FIA_F32, FIA_I8, FIA_U8, FIA_BOOL, FIA_I32, FIA_I64 = range(8)
+FIA_F16, FIA_BF16, FIA_F32, FIA_I8, FIA_U8, FIA_BOOL, FIA_I32, FIA_I64, FIA_F8E4M3 = range(9)
 
 
 class fia_tensor(ctypes.Structure):
@@ -72,6 +72,9 @@ class bsa_params(ctypes.Structure):
         ("pre_tokens", ctypes.c_int64),
         ("next_tokens", ctypes.c_int64),
         ("softmax_lse_flag", ctypes.c_int32),
+        ("dequant_scale_query", ctypes.POINTER(fia_tensor)),
+        ("dequant_scale_key", ctypes.POINTER(fia_tensor)),
+        ("dequant_scale_value", ctypes.POINTER(fia_tensor)),
     ]
 
 

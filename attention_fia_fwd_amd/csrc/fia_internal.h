@@ -83,6 +83,12 @@ struct AttnArgs {
     int64_t p_blk;
     int32_t block_size;            // a multiple of 64 (tiles never cross a block)
     int32_t paged;
+    // block-sparse FP8 (E4M3FN) inputs: fp32 dequant scales per (batch, head,
+    // q block) and per (batch, kv head, kv block)
+    int32_t fp8;
+    const float* q_scale;          // [B, QN, nqb]
+    const float* k_scale;          // [B, KVN, nkb]
+    const float* v_scale;          // [B, KVN, nkb]
 };
 
 // Decode schedule.  The query rows of one (batch, kv head) are the G x S

@@ -698,6 +698,312 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd(AttnArgs a)
 }
 
 // ---------------------------------------------------------------------------
+// Block-sparse attention with FP8 (E4M3FN) query, key and value (FP8 feature
+// of the block-sparse page): each element stands for its value times the
+// fp32 scale of its block (query: 128-row blocks; key / value: the Y-token kv
+// blocks of the sparse mask, Y = 256 or 512).  A workgroup is the 128 rows of
+// one (batch, head, q block), as in the 16-bit kernel.  Per 64-token tile of
+// the compacted block list:
+//   S^T = K Q^T on v_mfma_f32_32x32x64_f8f6f4 (both operands E4M3FN; K from
+//     LDS, Q in registers); lane (row, hh) holds d = 64 s + 32 hh + (0..31)
+//     of k-step s in both operands, so every d meets its partner; the
+//     scores are then multiplied by qs * ks of the tile's blocks;
+//   online softmax as in the 16-bit kernel;
+//   O^T += V^T P^T on bf16 MFMAs: P times the tile's vs, rounded to bf16;
+//     V widened exactly from E4M3FN to bf16 in LDS (E4M3FN values are bf16
+//     values), into the swizzled layout of the 16-bit kernel's V tiles.
+// K and V bytes of tile it + 1 go direct-to-LDS at the top of iteration it;
+// its V bytes are widened at the end of iteration it by the lanes whose
+// loads brought them, so the next per-tile barrier also publishes them.
+// ---------------------------------------------------------------------------
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ i32x4 rows_rsrc8(const uint8_t* base, int64_t row0, int64_t lkv, int64_t stride,
+                                            int rowlen)
+{
+    const int64_t n = lkv - row0;
+    const int64_t bytes = n > 0 ? (n - 1) * stride + rowlen : 0;
+    return make_rsrc(base + row0 * stride, bytes);
+}
+
+__global__ __launch_bounds__(256, 2) void bsa_fp8(AttnArgs a)
+{
+    constexpr int NW = 4, BN = kBlockN, D = 128;
+    constexpr int K8 = BN * D;               // K tile bytes
+    constexpr int VS8 = 2 * K8;              // offset of the bf16 V tile in a stage
+    constexpr int STAGE = K8 + K8 + 2 * BN * D;   // K bytes, V bytes, V bf16
+    constexpr int NO = D / 32;
+    using O = Ops<FIA_BF16>;
+
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem8[];
+    const uint32_t smem_lds = (uint32_t)(uintptr_t)(lds_void*)smem8;
+
+    const int tid = threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int l32 = lane & 31;
+    const int hh = lane >> 5;
+
+    const Tile t = a.tiles[blockIdx.x];
+    const BatchInfo bi = t.bi;
+    const int h = t.h, q0 = t.q0, q1 = t.q1;
+    const int Lq = bi.lq, Lkv = bi.lkv;
+    const int g = h / a.G;
+    const int qend = min(q1, Lq);
+    const uint8_t* qp = (const uint8_t*)a.q + bi.q_row0 * a.q_rowmul + (int64_t)h * a.q_sH;
+    const uint8_t* kp = (const uint8_t*)a.k + bi.kv_row0 * a.k_rowmul + (int64_t)g * a.k_sH;
+    const uint8_t* vp = (const uint8_t*)a.v + bi.kv_row0 * a.v_rowmul + (int64_t)g * a.v_sH;
+    const int wr0 = q0 + 32 * w;
+    const int row = wr0 + l32;
+    const int wend = min(wr0 + 32, qend);
+    const float c = fmaxf(fabsf(a.scale_log2), kMinScale);
+    const uint32_t qflip = a.scale_log2 < 0.f ? 0x80808080u : 0u;   // E4M3FN sign bits
+
+    // the workgroup's q block, its scale and its compacted kv-block list
+    const int qb = q0 / a.bx;
+    const int64_t rowi = ((int64_t)t.b * a.QN + h) * a.nqb + qb;
+    const float qs = a.q_scale[rowi];
+    const int per = a.by / BN;
+    const int ntiles = qend > q0 ? a.bsa_cnt[rowi] * per : 0;
+    const int32_t* blist = a.bsa_idx + rowi * a.nkb;
+    const float* ksb = a.k_scale + ((int64_t)t.b * a.KVN + g) * a.nkb;
+    const float* vsb = a.v_scale + ((int64_t)t.b * a.KVN + g) * a.nkb;
+
+    // Q as the B operand of S^T = K Q^T: lane (row, hh), k-step s: 32 bytes
+    // at d = 64 s + 32 hh
+    uint4 qf[2][2];
+    if (row < qend) {
+        const uint8_t* src = qp + (int64_t)row * a.q_sS + 32 * hh;
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                uint4 v = *(const uint4*)(src + 64 * s + 16 * e);
+                v.x ^= qflip; v.y ^= qflip; v.z ^= qflip; v.w ^= qflip;
+                qf[s][e] = v;
+            }
+    } else {
+#pragma unroll
+        for (int s = 0; s < 2; ++s) qf[s][0] = qf[s][1] = make_uint4(0, 0, 0, 0);
+    }
+
+    // 64 entries of the block list (and their kv scales) in one register per
+    // lane each; the window moves forward as in the 16-bit kernel
+    int bsa_cb = 0, bsa_bc = 0;
+    float ks_w = 0.f, vs_w = 0.f;
+    auto reload = [&](int base) {
+        bsa_cb = base;
+        const int e = base + lane;
+        const int kb = e < a.nkb ? blist[e] : -1;
+        bsa_bc = kb < 0 ? 0 : kb;
+        ks_w = kb >= 0 ? ksb[kb] : 0.f;
+        vs_w = kb >= 0 ? vsb[kb] : 0.f;
+    };
+    if (ntiles > 0) reload(0);
+    auto entry = [&](int it) -> int {      // window slot of tile it
+        const int idx = it / per;
+        if (idx >= bsa_cb + 64) reload(idx - 2);
+        return idx - bsa_cb;
+    };
+    auto tile_c0 = [&](int it) -> int {
+        const int sl = entry(it);
+        return __builtin_amdgcn_readlane(bsa_bc, sl) * a.by + BN * (it % per);
+    };
+
+    // K: row r, 16-byte chunk c at position c ^ ((r >> 1) & 7) (the 16 rows of
+    // a quarter-wave operand read hit 16 distinct bank groups); V bytes: plain
+    // rows.  Instruction u of wave w fills slots 64 (NW u + w) + lane.
+    uint32_t koff[2], voff[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int sl = 64 * (NW * u + w) + lane;
+        const int r = sl >> 3, pos = sl & 7;
+        koff[u] = (uint32_t)(r * a.k_sS + 16 * (pos ^ ((r >> 1) & 7)));
+        voff[u] = (uint32_t)(r * a.v_sS + 16 * pos);
+    }
+    auto load_tile = [&](int c0, int st) {
+        const uint32_t kb = smem_lds + (uint32_t)(st * STAGE);
+        const i32x4 kr = rows_rsrc8(kp, c0, Lkv, a.k_sS, D);
+        const i32x4 vr = rows_rsrc8(vp, c0, Lkv, a.v_sS, D);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            dma16(kr, kb + 1024u * (NW * u + w), koff[u]);
+            dma16(vr, kb + K8 + 1024u * (NW * u + w), voff[u]);
+        }
+    };
+    // widen the V bytes this lane's loads brought into the bf16 tile
+    auto widen = [&](int st) {
+        uint8_t* base = smem8 + st * STAGE;
+        uint16_t* vbf = (uint16_t*)(base + VS8);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int sl = 64 * (NW * u + w) + lane;
+            const int r = sl >> 3, cc = sl & 7;
+            const uint4 raw = *(const uint4*)(base + K8 + 16 * sl);
+            const uint32_t w4[4] = {raw.x, raw.y, raw.z, raw.w};
+            uint32_t pk[8];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                pk[2 * e] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w4[e], 1.0f, false));
+                pk[2 * e + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w4[e], 1.0f, true));
+            }
+            const int sw = 4 * (r & 3);
+            *(uint4*)(vbf + r * D + 8 * ((2 * cc) ^ sw)) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+            *(uint4*)(vbf + r * D + 8 * ((2 * cc + 1) ^ sw)) = make_uint4(pk[4], pk[5], pk[6], pk[7]);
+        }
+    };
+
+    // per-lane LDS offsets of the operand reads (as in the 16-bit kernel for V)
+    const int kx = (l32 >> 1) & 7;          // same for rows l32 and 32 + l32
+    const int vi = lane & 15;
+    const int vrow = 4 * hh + (vi >> 2);
+    const int vswz = 4 * (vi >> 2);
+    const int vcol_lo = 2 * ((lane >> 4) & 1) + ((vi & 3) >> 1);
+    const int vsub = 4 * (vi & 1);
+
+    f32x16 acc[NO];
+#pragma unroll
+    for (int o = 0; o < NO; ++o)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[o][r] = 0.f;
+    float m = -INFINITY, l = 0.f;
+    const float lazy_real = kLazy / c;      // in score units
+
+    if (ntiles > 0) {
+        load_tile(tile_c0(0), 0);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        widen(0);
+    }
+    for (int it = 0; it < ntiles; ++it) {
+        const int st = it & 1;
+        __syncthreads();                   // tile it (K bytes, widened V) ready; stage st ^ 1 free
+        if (it + 1 < ntiles) load_tile(tile_c0(it + 1), st ^ 1);
+        const int sl = entry(it);
+        const int c0 = __builtin_amdgcn_readlane(bsa_bc, sl) * a.by + BN * (it % per);
+        const float f = qs * __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ks_w), sl));
+        const float vsc = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(vs_w), sl));
+
+        if (wend > wr0) {
+            const uint8_t* kt = smem8 + st * STAGE;
+            const uint16_t* vs = (const uint16_t*)(kt + VS8);
+            f32x16 s0, s1;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) s0[r] = s1[r] = 0.f;
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                const int ch = 4 * s + 2 * hh;
+                const uint8_t* r0p = kt + l32 * D;
+                const uint8_t* r1p = kt + (32 + l32) * D;
+                const uint4 a00 = *(const uint4*)(r0p + 16 * (ch ^ kx));
+                const uint4 a01 = *(const uint4*)(r0p + 16 * ((ch + 1) ^ kx));
+                const uint4 a10 = *(const uint4*)(r1p + 16 * (ch ^ kx));
+                const uint4 a11 = *(const uint4*)(r1p + 16 * ((ch + 1) ^ kx));
+                const i32x8 bq = {(int)qf[s][0].x, (int)qf[s][0].y, (int)qf[s][0].z, (int)qf[s][0].w,
+                                  (int)qf[s][1].x, (int)qf[s][1].y, (int)qf[s][1].z, (int)qf[s][1].w};
+                const i32x8 ka0 = {(int)a00.x, (int)a00.y, (int)a00.z, (int)a00.w,
+                                   (int)a01.x, (int)a01.y, (int)a01.z, (int)a01.w};
+                const i32x8 ka1 = {(int)a10.x, (int)a10.y, (int)a10.z, (int)a10.w,
+                                   (int)a11.x, (int)a11.y, (int)a11.z, (int)a11.w};
+                s0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ka0, bq, s0, 0, 0, 0, 0, 0, 0);
+                s1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ka1, bq, s1, 0, 0, 0, 0, 0, 0);
+            }
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                s0[r] *= f;
+                s1[r] *= f;
+            }
+            // keys past the length and rows past the query length
+            if (c0 + BN > Lkv || wend - wr0 < 32) {
+                const int base = c0 + 4 * hh;
+                const int jhi = row >= qend ? -1 : Lkv - 1 - base;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int k0 = 8 * (r >> 2) + (r & 3), k1 = 32 + k0;
+                    if (k0 > jhi) s0[r] = -INFINITY;
+                    if (k1 > jhi) s1[r] = -INFINITY;
+                }
+            }
+            float mq[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                mq[q] = vmax(s0[4 * q], vmax(s0[4 * q + 1], s1[4 * q]));
+                mq[q] = vmax(mq[q], vmax(s0[4 * q + 2], s1[4 * q + 1]));
+                mq[q] = vmax(mq[q], vmax(s0[4 * q + 3], s1[4 * q + 2]));
+                mq[q] = vmax(mq[q], s1[4 * q + 3]);
+            }
+            float mt = vmax(vmax(mq[0], vmax(mq[1], mq[2])), mq[3]);
+            mt = other_half_max(mt);
+            const float mn = fmaxf(m, mt);
+            const bool grow = (m == -INFINITY) ? (mn > -INFINITY) : (mn > m + lazy_real);
+            if (__ballot(grow)) {
+                float alpha = 1.f;
+                if (m == -INFINITY) alpha = 0.f;
+                else if (mn != -INFINITY) alpha = fast_exp2((m - mn) * c);
+                m = mn;
+                l *= alpha;
+#pragma unroll
+                for (int o = 0; o < NO; ++o)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) acc[o][r] *= alpha;
+            }
+            const float mc = (m == -INFINITY) ? 0.f : m * c;
+            float ps = 0.f;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                s0[r] = fast_exp2(__builtin_fmaf(s0[r], c, -mc));
+                s1[r] = fast_exp2(__builtin_fmaf(s1[r], c, -mc));
+                ps += s0[r] + s1[r];
+            }
+            l += ps;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const f32x16& src = (k < 2) ? s0 : s1;
+                const int b8 = 8 * (k & 1);
+                uint4 pb;
+                pb.x = O::pack2(src[b8 + 0] * vsc, src[b8 + 1] * vsc);
+                pb.y = O::pack2(src[b8 + 2] * vsc, src[b8 + 3] * vsc);
+                pb.z = O::pack2(src[b8 + 4] * vsc, src[b8 + 5] * vsc);
+                pb.w = O::pack2(src[b8 + 6] * vsc, src[b8 + 7] * vsc);
+                const uint16_t* vk = vs + (16 * k + vrow) * D + vsub;
+#pragma unroll
+                for (int o = 0; o < NO; ++o) {
+                    const int pc = (4 * o + vcol_lo) ^ vswz;
+                    const uint2 lo = lds_read_tr16(vk + 8 * pc);
+                    const uint2 hi = lds_read_tr16(vk + 8 * D + 8 * pc);
+                    acc[o] = O::mma32(make_uint4(lo.x, lo.y, hi.x, hi.y), pb, acc[o]);
+                }
+            }
+        }
+        if (it + 1 < ntiles) {
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            widen(st ^ 1);
+        }
+    }
+
+    // epilogue: rows < q1 are written; rows in [qend, q1) and rows with no
+    // allowed key get out = 0 and lse = +inf
+    const float lt = other_half_sum(l);
+    if (row < q1) {
+        const bool valid = row < qend && lt > 0.f;
+        const float inv = valid ? 1.f / lt : 0.f;
+        uint16_t* op = (uint16_t*)a.o + bi.q_row0 * a.o_rowmul + (int64_t)h * a.o_sH + (int64_t)row * a.o_sS;
+#pragma unroll
+        for (int o = 0; o < NO; ++o)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                uint2 v;
+                v.x = O::pack2(acc[o][4 * g4 + 0] * inv, acc[o][4 * g4 + 1] * inv);
+                v.y = O::pack2(acc[o][4 * g4 + 2] * inv, acc[o][4 * g4 + 3] * inv);
+                *(uint2*)(op + 32 * o + 8 * g4 + 4 * hh) = v;
+            }
+        if (a.return_lse && hh == 0) {
+            float* lp = a.lse + bi.q_row0 * a.lse_rowmul + (int64_t)h * a.lse_sH + (int64_t)row * a.lse_sS;
+            *lp = valid ? (m * c + __log2f(lt)) * kLn2 : INFINITY;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Decode: split-KV attention over (optionally paged) K/V.
 //
 // One wave per resident slot; it walks its pieces, each a token range of one
@@ -1478,6 +1784,14 @@ int launch_bsa(const fia_plan& p, const AttnArgs& a, void* stream)
                            (int)p.QN, (int)p.bsa_nqb, (int)p.bsa_nkb, a.bx, a.by, p.n_rows);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return (int)e;
+    }
+    if (a.fp8) {
+        const size_t lds = 2u * (2u * kBlockN * 128u + 2u * kBlockN * 128u);   // 2 stages of 32 KB
+        static bool configured = false;
+        raise_lds_limit(bsa_fp8, lds, configured);
+        if (p.n_tiles == 0) return 0;
+        hipLaunchKernelGGL(bsa_fp8, dim3((unsigned)p.n_tiles), dim3(256), lds, s, a);
+        return (int)hipGetLastError();
     }
     const bool bf = p.dtype == FIA_BF16;
     if (p.Dqk == 64)

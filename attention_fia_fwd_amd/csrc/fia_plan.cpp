@@ -817,9 +817,21 @@ fia_status bsa_get_workspace_size(const fia_tensor* query, const fia_tensor* key
     if (!query->data || !key->data || !value->data || !attention_out->data ||
         !block_sparse_mask->data)
         return FIA_ERR_NULLPTR;
-    if (!is_half(query->dtype) || key->dtype != query->dtype || value->dtype != query->dtype ||
-        attention_out->dtype != query->dtype)
-        return FIA_ERR_DTYPE;
+    // FP8 feature: query, key and value all E4M3FN with the three dequant
+    // scales, a bf16 output; otherwise fp16/bf16 throughout and no scales.
+    const bool fp8 = query->dtype == FIA_F8E4M3;
+    if (fp8) {
+        if (key->dtype != FIA_F8E4M3 || value->dtype != FIA_F8E4M3 || attention_out->dtype != FIA_BF16)
+            return FIA_ERR_DTYPE;
+        if (!prm->dequant_scale_query || !prm->dequant_scale_key || !prm->dequant_scale_value)
+            return FIA_ERR_NULLPTR;
+    } else {
+        if (!is_half(query->dtype) || key->dtype != query->dtype || value->dtype != query->dtype ||
+            attention_out->dtype != query->dtype)
+            return FIA_ERR_DTYPE;
+        if (prm->dequant_scale_query || prm->dequant_scale_key || prm->dequant_scale_value)
+            return FIA_ERR_PARAM;
+    }
     if (block_sparse_mask->dtype != FIA_U8 && block_sparse_mask->dtype != FIA_BOOL)
         return FIA_ERR_DTYPE;
 
@@ -884,6 +896,19 @@ fia_status bsa_get_workspace_size(const fia_tensor* query, const fia_tensor* key
     }
     const int64_t nqb = (maxq + X - 1) / X, nkb = (maxkv + Y - 1) / Y;
     if (!dims_are(block_sparse_mask, {B, N1, nqb, nkb})) return FIA_ERR_SHAPE;
+    // FP8: the quantization blocks are the sparse blocks, [128, 256] or
+    // [128, 512]; scales fp32 [B, N1, nqb, 1] and [B, N2, nkb, 1]
+    if (fp8) {
+        if (X != 128 || (Y != 256 && Y != 512)) return FIA_ERR_PARAM;
+        if (gq.D != 128) return FIA_ERR_UNSUPPORTED;
+        const fia_tensor* sq = prm->dequant_scale_query;
+        const fia_tensor* sk = prm->dequant_scale_key;
+        const fia_tensor* sv = prm->dequant_scale_value;
+        if (!sq->data || !sk->data || !sv->data) return FIA_ERR_NULLPTR;
+        if (sq->dtype != FIA_F32 || sk->dtype != FIA_F32 || sv->dtype != FIA_F32) return FIA_ERR_DTYPE;
+        if (!dims_are(sq, {B, N1, nqb, 1}) || !dims_are(sk, {B, N2, nkb, 1}) || !dims_are(sv, {B, N2, nkb, 1}))
+            return FIA_ERR_SHAPE;
+    }
     const bool want_lse = prm->softmax_lse_flag != 0;
     if (want_lse) {
         if (!softmax_lse || !softmax_lse->data) return FIA_ERR_NULLPTR;
@@ -927,6 +952,12 @@ fia_status bsa_get_workspace_size(const fia_tensor* query, const fia_tensor* key
     a.nkb = (int32_t)nkb;
     a.bx = (int32_t)X;
     a.by = (int32_t)Y;
+    a.fp8 = fp8;
+    if (fp8) {
+        a.q_scale = (const float*)prm->dequant_scale_query->data;
+        a.k_scale = (const float*)prm->dequant_scale_key->data;
+        a.v_scale = (const float*)prm->dequant_scale_value->data;
+    }
     const int64_t D = gq.D;
     if (layout == LAYOUT_BNSD) {
         a.q_sH = gq.S * D; a.q_sS = D;

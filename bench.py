@@ -2,7 +2,7 @@
 """Benchmark of the MI355X fused inference attention forward.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2]
-                    [--secondary c1,c3,c4,c5,paged_prefill,mtp_decode,int8_decode]
+                    [--secondary c1,c3,c4,c5,paged_prefill,mtp_decode,int8_decode,fp8_bsa]
 
 One step is one fia_run (phase 2) of the headline workload: the GQA causal
 prefill, bf16, B=4, Q_N=32, KV_N=8, max S=4096, D=128, BSND, per-batch
@@ -15,7 +15,8 @@ skipped tiles are not counted).
 
 The other workloads (dense causal fp16 prefill, paged GQA decode, varlen TND
 prefill, block-sparse prefill, chunked prefill against a paged cache,
-multi-token decode against a paged cache, decode against an int8 KV cache) are
+multi-token decode against a paged cache, decode against an int8 KV cache,
+block-sparse prefill with FP8 inputs) are
 timed the same way and reported under "secondary"; the decode lines are in
 GB/s of algorithmic bytes (every KV byte of every kv head once, plus q, out,
 lse, the block-table entries and the dequant scales read).
@@ -38,6 +39,7 @@ sys.path.insert(0, ROOT)
 sys.path.insert(0, os.path.join(ROOT, "tests"))
 
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16/fp16 MFMA
+PEAK_FP8_TFLOPS = 5000.0      # MI355X dense fp8 MFMA (the FP8 block-sparse inputs' dtype)
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 
 
@@ -150,7 +152,7 @@ def build_plan(name, case):
     from fia_gpu import bsa_plan, fia_plan, to_dev
     to_dev(case)
     t0 = time.perf_counter()
-    plan = bsa_plan(case) if name == "c5" else fia_plan(case)
+    plan = bsa_plan(case) if name in ("c5", "fp8_bsa") else fia_plan(case)
     t1 = time.perf_counter()
     return plan, (t1 - t0) * 1e6
 
@@ -170,16 +172,17 @@ def measure(name, steps, warmup):
                    roofline={"bound": "hbm", "achieved": nbytes / ev / 1e9, "peak": PEAK_HBM_GBS,
                              "unit": "GB/s", "frac": nbytes / ev / 1e9 / PEAK_HBM_GBS})
     else:
-        if name == "c5":
+        if name in ("c5", "fp8_bsa"):
             pairs = allowed_pairs_bsa(case)
             flops = 2 * (case.D + case.D) * pairs
         else:
             pairs = allowed_pairs_fia(case)
             flops = 2 * (case.Dqk + case.Dv) * pairs
+        peak = PEAK_FP8_TFLOPS if name == "fp8_bsa" else PEAK_BF16_TFLOPS
         res.update(value=flops / wall / 1e12, unit="TFLOP/s", algorithmic_flops=flops,
                    roofline={"bound": "mfma", "achieved": flops / ev / 1e12,
-                             "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                             "frac": flops / ev / 1e12 / PEAK_BF16_TFLOPS})
+                             "peak": peak, "unit": "TFLOP/s",
+                             "frac": flops / ev / 1e12 / peak})
     res["roofline"]["traffic"] = measured_traffic(name)
     plan.close()
     del case
@@ -230,7 +233,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="c2")
-    ap.add_argument("--secondary", default="c1,c3,c4,c5,paged_prefill,mtp_decode,int8_decode",
+    ap.add_argument("--secondary", default="c1,c3,c4,c5,paged_prefill,mtp_decode,int8_decode,fp8_bsa",
                     help="comma list of other workloads to time ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",

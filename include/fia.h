@@ -69,7 +69,8 @@ typedef enum fia_status {
 
 typedef enum fia_dtype {
     FIA_F16 = 0, FIA_BF16 = 1, FIA_F32 = 2, FIA_I8 = 3,
-    FIA_U8 = 4, FIA_BOOL = 5, FIA_I32 = 6, FIA_I64 = 7
+    FIA_U8 = 4, FIA_BOOL = 5, FIA_I32 = 6, FIA_I64 = 7,
+    FIA_F8E4M3 = 8           /* FLOAT8_E4M3FN (block-sparse FP8 inputs) */
 } fia_dtype;
 
 /* A dense row-major tensor: dims[0] is the slowest axis. */
@@ -220,6 +221,15 @@ typedef struct bsa_params {
     int64_t pre_tokens;            /* must be 2147483647                          */
     int64_t next_tokens;           /* must be 2147483647                          */
     int32_t softmax_lse_flag;      /* 0 / 1                                       */
+    /* FP8 inputs (FP8 feature of the block-sparse page): query, key and value
+     * all FLOAT8_E4M3FN, each element standing for value * its block's scale.
+     * Scales fp32, required for FP8 inputs and NULL otherwise (FIA_ERR_PARAM):
+     *   query  [B, N1, ceil(maxQS / 128), 1]   (block_shape[0] must be 128)
+     *   key / value  [B, N2, ceil(maxKVS / Y), 1], Y = block_shape[1] = 256 or 512.
+     * The output is bf16; D must be 128. */
+    const fia_tensor* dequant_scale_query;
+    const fia_tensor* dequant_scale_key;
+    const fia_tensor* dequant_scale_value;
 } bsa_params;
 
 /* Defaults: layouts "BNSD", scale 1.0, block_shape [128,128], inner_precise 4,

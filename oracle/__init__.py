@@ -57,6 +57,10 @@ class _Args(ctypes.Structure):
         ("k_scale", ctypes.c_void_p), ("k_off", ctypes.c_void_p),
         ("v_scale", ctypes.c_void_p), ("v_off", ctypes.c_void_p),
         ("tok_stride", ctypes.c_int64),
+        ("fp8", ctypes.c_int32),
+        ("q_bscale", ctypes.c_void_p), ("k_bscale", ctypes.c_void_p), ("v_bscale", ctypes.c_void_p),
+        ("nqs", ctypes.c_int64), ("nks", ctypes.c_int64), ("qblk", ctypes.c_int64),
+        ("kvblk", ctypes.c_int64),
     ]
 
 
@@ -73,6 +77,8 @@ def lib():
         _lib.oracle_read_half.restype = ctypes.c_double
         _lib.oracle_read_half.argtypes = [ctypes.c_uint16, ctypes.c_int]
         _lib.oracle_num_threads.restype = ctypes.c_int
+        _lib.oracle_read_e4m3fn.restype = ctypes.c_double
+        _lib.oracle_read_e4m3fn.argtypes = [ctypes.c_uint8]
     return _lib
 
 
@@ -84,10 +90,16 @@ def read_half(bits: int, dtype: torch.dtype) -> float:
     return lib().oracle_read_half(bits, 1 if dtype == torch.bfloat16 else 0)
 
 
+def read_e4m3fn(bits: int) -> float:
+    return lib().oracle_read_e4m3fn(bits)
+
+
 def _bits(t: torch.Tensor) -> np.ndarray:
     t = t.detach().to("cpu").contiguous()
     if t.dtype == torch.int8:
         return t.numpy()
+    if t.dtype == torch.float8_e4m3fn:
+        return t.view(torch.uint8).numpy()
     assert t.dtype in (torch.float16, torch.bfloat16), t.dtype
     return t.view(torch.int16).numpy().view(np.uint16)
 
@@ -228,6 +240,16 @@ def block_sparse(case, rows=None):
     a.block_mask = _ptr(bm)
     a.nqb, a.nkb = bm.shape[2], bm.shape[3]
     a.X, a.Y = case.X, case.Y
+    fp8 = getattr(case, "fp8", None)
+    if fp8 is not None:
+        a.fp8 = 1
+        for fld, key in (("q_bscale", "dequant_scale_query"), ("k_bscale", "dequant_scale_key"),
+                         ("v_bscale", "dequant_scale_value")):
+            arr = _exact_f64(fp8[key])
+            keep.append(arr)
+            setattr(a, fld, _ptr(arr))
+        a.nqs, a.nks = fp8["dequant_scale_query"].shape[2], fp8["dequant_scale_key"].shape[2]
+        a.qblk, a.kvblk = case.X, case.Y
     r, n = _rows_arg(rows)
     if r is not None:
         keep.append(r)

@@ -56,6 +56,12 @@
  *   mode 0 (per channel): scale[g][d], offset[g][d] of kv head g, channel d;
  *   mode 1 (per token):   scale[b][j], offset[b][j] of batch b, kv token j;
  * the scales and offsets are passed in as exact double values.
+ *
+ * Block-sparse FP8 (page "aclnnBlockSparseAttentionV2", FP8 feature): query,
+ * key and value hold FLOAT8_E4M3FN values, each standing for its value times
+ * the fp32 scale of its block: query row i of (b, h) uses
+ * qscale[b][h][i / qblk], key / value token j of (b, g) uses
+ * kscale[b][g][j / kvblk] (vscale likewise).
  */
 #include <math.h>
 #include <stdint.h>
@@ -97,6 +103,25 @@ static double elem(const uint16_t* p, int64_t idx, int dtype)
 /* Exported so a test can check the element reader against a library cast. */
 double oracle_read_half(uint16_t bits, int dtype) { return elem(&bits, 0, dtype); }
 
+/* Exact value of a FLOAT8_E4M3FN byte: 1 sign, 4 exponent (bias 7), 3
+ * mantissa bits; no infinities, S.1111.111 is NaN. */
+static double e4m3fn_to_double(uint8_t x)
+{
+    int sign = (x >> 7) & 1;
+    int e = (x >> 3) & 0xf;
+    int m = x & 7;
+    double v;
+    if (e == 0)
+        v = ldexp((double)m, -9);                /* subnormal: m/8 * 2^-6 */
+    else if (e == 15 && m == 7)
+        v = NAN;
+    else
+        v = ldexp((double)(8 + m), e - 10);      /* (1 + m/8) * 2^(e-7) */
+    return sign ? -v : v;
+}
+
+double oracle_read_e4m3fn(uint8_t bits) { return e4m3fn_to_double(bits); }
+
 typedef struct {
     int32_t layout;          /* OR_BNSD, OR_BSND (also BSH), OR_TND */
     int32_t dtype;           /* OR_F16 or OR_BF16 (q, k, v alike) */
@@ -132,6 +157,12 @@ typedef struct {
     const double* v_scale;
     const double* v_off;
     int64_t tok_stride;
+    /* block-sparse FP8 (E4M3FN) inputs with per-block scales */
+    int32_t fp8;
+    const double* q_bscale;          /* [B, QN, nqs] */
+    const double* k_bscale;          /* [B, KVN, nks] */
+    const double* v_bscale;
+    int64_t nqs, nks, qblk, kvblk;
 } oracle_args;
 
 static int64_t q_off(const oracle_args* a, int64_t b, int64_t h, int64_t i, int64_t D)
@@ -196,6 +227,10 @@ static int allowed_bsa(const oracle_args* a, int64_t b, int64_t h, int64_t i, in
 static double kv_elem(const oracle_args* a, const void* t, int64_t idx, int is_v, int64_t b,
                       int64_t g, int64_t j, int64_t d, int64_t D)
 {
+    if (a->fp8) {
+        const double* sc = is_v ? a->v_bscale : a->k_bscale;
+        return e4m3fn_to_double(((const uint8_t*)t)[idx]) * sc[(b * a->KVN + g) * a->nks + j / a->kvblk];
+    }
     if (!a->kv_i8)
         return elem((const uint16_t*)t, idx, a->dtype);
     const double x = (double)((const int8_t*)t)[idx];
@@ -238,8 +273,12 @@ static int one_row(const oracle_args* a, const uint16_t* q, const void* k,
             continue;
         const int64_t ko = kv_off(a, b, g, j, a->Dqk);
         double acc = 0.0;
-        for (d = 0; d < a->Dqk; ++d)
-            acc += elem(q, qo + d, a->dtype) * kv_elem(a, k, ko + d, 0, b, g, j, d, a->Dqk);
+        for (d = 0; d < a->Dqk; ++d) {
+            const double qv = a->fp8 ? e4m3fn_to_double(((const uint8_t*)q)[qo + d]) *
+                                           a->q_bscale[(b * a->QN + h) * a->nqs + i / a->qblk]
+                                     : elem(q, qo + d, a->dtype);
+            acc += qv * kv_elem(a, k, ko + d, 0, b, g, j, d, a->Dqk);
+        }
         s[j] = a->scale * acc;
         if (s[j] > m)
             m = s[j];
@@ -328,6 +367,8 @@ int oracle_block_sparse(const oracle_args* a, const uint16_t* q, const uint16_t*
 {
     if (!a || !q || !k || !v || !out || !lse || !a->block_mask || a->X <= 0 || a->Y <= 0 ||
         a->KVN <= 0 || a->QN % a->KVN || a->kv_i8)
+        return -2;
+    if (a->fp8 && (!a->q_bscale || !a->k_bscale || !a->v_bscale || a->qblk <= 0 || a->kvblk <= 0))
         return -2;
     return run(a, q, k, v, 1, out, lse);
 }

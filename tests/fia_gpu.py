@@ -22,11 +22,12 @@ def to_dev(case, device="cuda"):
         t = getattr(case, name, None)
         if t is not None and t.device.type != "cuda":
             setattr(case, name, t.to(device))
-    quant = getattr(case, "quant", None)
-    if quant:
-        for key, t in quant.items():
-            if isinstance(t, torch.Tensor) and t.device.type != "cuda":
-                quant[key] = t.to(device)
+    for extra in ("quant", "fp8"):
+        d = getattr(case, extra, None)
+        if d:
+            for key, t in d.items():
+                if isinstance(t, torch.Tensor) and t.device.type != "cuda":
+                    d[key] = t.to(device)
     return case
 
 
@@ -58,6 +59,8 @@ def bsa_plan(case, **over):
     if ql is not None:
         kw["actual_seq_lengths"] = ql
         kw["actual_seq_lengths_kv"] = kl
+    if getattr(case, "fp8", None):
+        kw.update(case.fp8)
     kw.update(over)
     return fia.BsaPlan(case.q, case.k, case.v, case.block_mask, **kw)
 
@@ -86,6 +89,8 @@ def compare(case, out, lse, ref_out, ref_lse, dtype=None):
     """Element-wise comparison; +inf LSE and exact-zero rows must match
     exactly.  Returns (max out err, max lse err)."""
     dtype = dtype or case.dtype
+    if dtype == torch.float8_e4m3fn:
+        dtype = torch.bfloat16               # FP8 inputs give a bf16 output
     o = out_as_oracle_layout(case, out)
     assert o.shape == ref_out.shape, (o.shape, ref_out.shape)
     assert np.all(np.isfinite(o)), "non-finite output"

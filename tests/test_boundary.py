@@ -293,6 +293,48 @@ def test_int8_kv_validation():
     assert code(k=kb) == _abi.FIA_ERR_PARAM
 
 
+def test_bsa_fp8_validation():
+    B, N1, N2, S, D = 1, 4, 2, 512, 128
+    f8 = torch.float8_e4m3fn
+    q = torch.zeros(B, N1, S, D, dtype=f8)
+    k = torch.zeros(B, N2, S, D, dtype=f8)
+    out = torch.zeros(B, N1, S, D, dtype=torch.bfloat16)
+
+    def code(Y=256, X=128, qs=None, ks=None, vs=None, out=out, k=k, scales=True):
+        nqb, nkb = -(-S // X), -(-S // Y)
+        mask = torch.ones(B, N1, nqb, nkb, dtype=torch.uint8)
+        qs = torch.ones(B, N1, nqb, 1) if qs is None else qs
+        ks = torch.ones(B, N2, nkb, 1) if ks is None else ks
+        vs = torch.ones(B, N2, nkb, 1) if vs is None else vs
+        p = fia.bsa_params()
+        fia.bsa_params_init(p)
+        p.num_heads, p.num_key_value_heads = N1, N2
+        p.block_shape[0], p.block_shape[1] = X, Y
+        keep = []
+        if scales:
+            for fld, t in (("dequant_scale_query", qs), ("dequant_scale_key", ks),
+                           ("dequant_scale_value", vs)):
+                if t is not None:
+                    d = fia.describe(t)
+                    keep.append((t, d))
+                    setattr(p, fld, ctypes.pointer(d))
+        st, ws, plan = fia.bsa_get_workspace_size(fia.describe(q), fia.describe(k), fia.describe(k),
+                                                  fia.describe(mask), None, None, p,
+                                                  fia.describe(out), None)
+        fia.fia_plan_destroy(plan)
+        return st
+
+    assert code() == _abi.FIA_OK
+    assert code(Y=512) == _abi.FIA_OK
+    assert code(Y=128) == _abi.FIA_ERR_PARAM              # kv quant blocks of 256 or 512
+    assert code(X=256, Y=256) == _abi.FIA_ERR_PARAM
+    assert code(scales=False) == _abi.FIA_ERR_NULLPTR
+    assert code(qs=torch.ones(B, N1, 4, 1, dtype=torch.float16)) == _abi.FIA_ERR_DTYPE
+    assert code(ks=torch.ones(B, N2, 3, 1)) == _abi.FIA_ERR_SHAPE
+    assert code(out=out.half()) == _abi.FIA_ERR_DTYPE        # bf16 output
+    assert code(k=k.to(torch.bfloat16)) == _abi.FIA_ERR_DTYPE  # all three E4M3FN
+
+
 def test_tnd_requires_cumulative_lengths():
     q = torch.zeros(30, 4, 128, dtype=torch.bfloat16)
     k = torch.zeros(30, 4, 128, dtype=torch.bfloat16)

@@ -685,3 +685,52 @@ def test_int8_kv_multi_token_causal():
     ro, rl = oracle.attention(_dequantized(case))
     np.testing.assert_array_equal(out, ro)
     np.testing.assert_array_equal(lse, rl)
+
+
+# ---------------------------------------------------------------------------
+# block-sparse FP8 (E4M3FN values times per-block fp32 scales)
+# ---------------------------------------------------------------------------
+
+def test_e4m3fn_reader_matches_library_cast():
+    bits = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    ref = bits.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = np.array([oracle.read_e4m3fn(int(b)) for b in range(256)])
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan) and nan.sum() == 2
+    np.testing.assert_array_equal(got[~nan], ref[~nan])
+
+
+def _bsa_fp8_as_bf16(case):
+    """The same case with bf16 inputs holding the dequantized values (exact
+    when the per-block scales are powers of two)."""
+    def deq(x, sc, blk):
+        xb = x.to(torch.float64)
+        if case.layout != "BNSD":
+            xb = xb.permute(0, 2, 1, 3)
+        S = xb.shape[2]
+        rep = sc.to(torch.float64)[..., 0].repeat_interleave(blk, dim=2)[:, :, :S]
+        y = xb * rep[..., None]
+        if case.layout != "BNSD":
+            y = y.permute(0, 2, 1, 3)
+        yb = y.to(torch.bfloat16)
+        assert torch.equal(yb.to(torch.float64), y)
+        return yb.contiguous()
+
+    f = case.fp8
+    ref = W.make_bsa(layout=case.layout, B=case.B, QN=case.QN, KVN=case.KVN, Sq=case.Sq,
+                     Skv=case.Skv, D=case.D, X=case.X, Y=case.Y, lq=case.lq, lkv=case.lkv,
+                     scale=case.scale, mask_kind=case.block_mask.numpy(), seed=0)
+    ref.q = deq(case.q, f["dequant_scale_query"], case.X)
+    ref.k = deq(case.k, f["dequant_scale_key"], case.Y)
+    ref.v = deq(case.v, f["dequant_scale_value"], case.Y)
+    return ref
+
+
+@pytest.mark.parametrize("layout, Y", [("BNSD", 256), ("BSND", 512)])
+def test_bsa_fp8_equals_bf16_on_the_dequantized_inputs(layout, Y):
+    case = W.make_bsa_fp8(layout=layout, B=2, QN=4, KVN=2, Sq=300, Skv=700, D=16, Y=Y, p=0.5,
+                          lq=[300, 129], lkv=[700, 260], pow2=True, seed=80)
+    out, lse = oracle.block_sparse(case)
+    ro, rl = oracle.block_sparse(_bsa_fp8_as_bf16(case))
+    np.testing.assert_array_equal(out, ro)
+    np.testing.assert_array_equal(lse, rl)

@@ -136,6 +136,9 @@ class BsaCase:
     block_mask: Optional[torch.Tensor] = None   # uint8 [B, QN, nqb, nkb], nonzero = selected
     return_lse: bool = True
     meta: dict = field(default_factory=dict)
+    # FP8 (E4M3FN) q/k/v: {"dequant_scale_query": [B, QN, nqb, 1],
+    # "dequant_scale_key": [B, KVN, nkb, 1], "dequant_scale_value": ...} fp32
+    fp8: Optional[dict] = None
 
     def seq_qlen_arg(self):
         if self.lq is None:
@@ -424,6 +427,67 @@ def make_bsa(name="custom", *, layout="BNSD", dtype=torch.bfloat16, B=1, QN=2, K
                    return_lse=return_lse)
 
 
+def _quantize_blocks(x: torch.Tensor, layout: str, blk: int, pow2: bool):
+    """Per-(batch, head, row block) E4M3FN quantization of a BNSD/BSND tensor:
+    scale = amax / 448 of the block (a power of two at or above it with
+    ``pow2``), values x / scale rounded to E4M3FN.  Returns (fp8 tensor,
+    fp32 scales [B, N, nblk, 1])."""
+    xb = x if layout == "BNSD" else x.permute(0, 2, 1, 3)
+    B, N, S, D = xb.shape
+    nb = -(-S // blk)
+    pad = torch.zeros(B, N, nb * blk, D, dtype=torch.float32, device=x.device)
+    pad[:, :, :S] = xb
+    amax = pad.reshape(B, N, nb, blk * D).abs().amax(dim=-1).clamp(min=1e-6)
+    sc = amax / 448.0
+    if pow2:
+        sc = torch.exp2(torch.ceil(torch.log2(sc)))
+    q = (pad.reshape(B, N, nb, blk, D) / sc[..., None, None]).reshape(B, N, nb * blk, D)[:, :, :S]
+    q = q.to(torch.float8_e4m3fn)
+    if layout != "BNSD":
+        q = q.permute(0, 2, 1, 3)
+    return q.contiguous(), sc[..., None].contiguous()
+
+
+def make_bsa_fp8(name="custom", *, layout="BNSD", B=1, QN=2, KVN=1, Sq=256, Skv=None, D=128,
+                 Y=256, p=0.25, lq=None, lkv=None, scale=None, seed=0, device="cpu",
+                 mask_kind="bernoulli", pow2=False, return_lse=True) -> BsaCase:
+    """Block-sparse case with FP8 (E4M3FN) query / key / value: fp32 N(0,1)
+    draws quantized per block (query 128-row blocks, key / value Y-token
+    blocks, Y = 256 or 512) with scale = block amax / 448.  Mask iid
+    Bernoulli(p) per (q block, kv block) with the kv block holding the q
+    block's diagonal forced on ("ones": all selected)."""
+    X = 128
+    Skv = Sq if Skv is None else Skv
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    ss = _streams(seed)
+    if lq is not None:
+        lq = np.asarray(lq, dtype=np.int64)
+    if lkv is not None:
+        lkv = np.asarray(lkv, dtype=np.int64)
+    nqb, nkb = -(-Sq // X), -(-Skv // Y)
+    qf = normal_tensor(_shape(layout, B, QN, Sq, D), torch.float32, ss[STREAM_Q], device)
+    kf = normal_tensor(_shape(layout, B, KVN, Skv, D), torch.float32, ss[STREAM_K], device)
+    vf = normal_tensor(_shape(layout, B, KVN, Skv, D), torch.float32, ss[STREAM_V], device)
+    q, qs = _quantize_blocks(qf, layout, X, pow2)
+    k, ks = _quantize_blocks(kf, layout, Y, pow2)
+    v, vs = _quantize_blocks(vf, layout, Y, pow2)
+    del qf, kf, vf
+    if mask_kind == "ones":
+        m = np.ones((B, QN, nqb, nkb), dtype=np.uint8)
+    else:
+        rng = np.random.default_rng(ss[STREAM_MASK])
+        m = (rng.random((B, QN, nqb, nkb)) < p).astype(np.uint8)
+        for i in range(nqb):
+            if (i * X) // Y < nkb:
+                m[:, :, i, (i * X) // Y] = 1
+    return BsaCase(name=name, layout=layout, dtype=torch.float8_e4m3fn, B=B, QN=QN, KVN=KVN,
+                   Sq=Sq, Skv=Skv, D=D, X=X, Y=Y, scale=scale, lq=lq, lkv=lkv, q=q, k=k, v=v,
+                   block_mask=torch.from_numpy(np.ascontiguousarray(m)).to(device),
+                   return_lse=return_lse,
+                   fp8={"dequant_scale_query": qs, "dequant_scale_key": ks,
+                        "dequant_scale_value": vs})
+
+
 # ---------------------------------------------------------------------------
 # The five named workloads.
 # ---------------------------------------------------------------------------
@@ -532,6 +596,16 @@ def int8_kv_decode_bf16(device="cpu") -> FiaCase:
                              seed=1008, device=device)
 
 
+def fp8_block_sparse(device="cpu") -> BsaCase:
+    """Block-sparse prefill with FP8 (E4M3FN) inputs: B=1, Q_N=32, KV_N=8,
+    S=32768, D=128, BNSD, block [128, 256] (the quantization blocks), mask
+    Bernoulli(0.25) with the diagonal's kv block forced on, per-block amax
+    scales, bf16 output, LSE on."""
+    return make_bsa_fp8("fp8_block_sparse_prefill_b1_n32_kv8_s32768_d128_y256", layout="BNSD",
+                        B=1, QN=32, KVN=8, Sq=32768, D=128, Y=256, p=0.25, seed=1009,
+                        device=device)
+
+
 WORKLOADS = {
     "c1": c1_dense_causal_fp16,
     "c2": c2_gqa_causal_bf16,
@@ -541,4 +615,5 @@ WORKLOADS = {
     "paged_prefill": paged_chunked_prefill_bf16,
     "mtp_decode": paged_mtp_decode_bf16,
     "int8_decode": int8_kv_decode_bf16,
+    "fp8_bsa": fp8_block_sparse,
 }
