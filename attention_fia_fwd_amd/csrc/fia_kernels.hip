@@ -907,11 +907,19 @@ __global__ __launch_bounds__(256, 2) void bsa_fp8(AttnArgs a)
                 s0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ka0, bq, s0, 0, 0, 0, 0, 0, 0);
                 s1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ka1, bq, s1, 0, 0, 0, 0, 0, 0);
             }
+            // scores in dequantized units: raw * f.  For f > 0 (dequant scales
+            // are positive factors) the factor rides in the exp2 FMA below and
+            // the row max is taken on the raw scores; otherwise it is applied
+            // here.
+            const bool fpos = f > 0.f;
+            if (!fpos) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                s0[r] *= f;
-                s1[r] *= f;
+                for (int r = 0; r < 16; ++r) {
+                    s0[r] *= f;
+                    s1[r] *= f;
+                }
             }
+            const float fm = fpos ? f : 1.f;
             // keys past the length and rows past the query length
             if (c0 + BN > Lkv || wend - wr0 < 32) {
                 const int base = c0 + 4 * hh;
@@ -932,7 +940,7 @@ __global__ __launch_bounds__(256, 2) void bsa_fp8(AttnArgs a)
                 mq[q] = vmax(mq[q], s1[4 * q + 3]);
             }
             float mt = vmax(vmax(mq[0], vmax(mq[1], mq[2])), mq[3]);
-            mt = other_half_max(mt);
+            mt = other_half_max(mt) * fm;   // -inf stays -inf (fm > 0)
             const float mn = fmaxf(m, mt);
             const bool grow = (m == -INFINITY) ? (mn > -INFINITY) : (mn > m + lazy_real);
             if (__ballot(grow)) {
@@ -946,24 +954,38 @@ __global__ __launch_bounds__(256, 2) void bsa_fp8(AttnArgs a)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) acc[o][r] *= alpha;
             }
+            // p = exp2(raw f c - m c); the P fed to the P V MFMAs also carries
+            // the tile's value scale: exp2(... + log2 vs) when vs > 0
+            const bool vpos = vsc > 0.f;
             const float mc = (m == -INFINITY) ? 0.f : m * c;
+            const float cf = c * fm;
+            const float lv = vpos ? __log2f(vsc) : 0.f;
+            const float pm = vpos ? 1.f : vsc;  // P multiplier left for the pack
+            const float ls = vpos ? 1.f / vsc : 1.f;
             float ps = 0.f;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                s0[r] = fast_exp2(__builtin_fmaf(s0[r], c, -mc));
-                s1[r] = fast_exp2(__builtin_fmaf(s1[r], c, -mc));
+                s0[r] = fast_exp2(__builtin_fmaf(s0[r], cf, lv - mc));
+                s1[r] = fast_exp2(__builtin_fmaf(s1[r], cf, lv - mc));
                 ps += s0[r] + s1[r];
             }
-            l += ps;
+            l += ps * ls;
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
                 const f32x16& src = (k < 2) ? s0 : s1;
                 const int b8 = 8 * (k & 1);
                 uint4 pb;
-                pb.x = O::pack2(src[b8 + 0] * vsc, src[b8 + 1] * vsc);
-                pb.y = O::pack2(src[b8 + 2] * vsc, src[b8 + 3] * vsc);
-                pb.z = O::pack2(src[b8 + 4] * vsc, src[b8 + 5] * vsc);
-                pb.w = O::pack2(src[b8 + 6] * vsc, src[b8 + 7] * vsc);
+                if (vpos) {
+                    pb.x = O::pack2(src[b8 + 0], src[b8 + 1]);
+                    pb.y = O::pack2(src[b8 + 2], src[b8 + 3]);
+                    pb.z = O::pack2(src[b8 + 4], src[b8 + 5]);
+                    pb.w = O::pack2(src[b8 + 6], src[b8 + 7]);
+                } else {
+                    pb.x = O::pack2(src[b8 + 0] * pm, src[b8 + 1] * pm);
+                    pb.y = O::pack2(src[b8 + 2] * pm, src[b8 + 3] * pm);
+                    pb.z = O::pack2(src[b8 + 4] * pm, src[b8 + 5] * pm);
+                    pb.w = O::pack2(src[b8 + 6] * pm, src[b8 + 7] * pm);
+                }
                 const uint16_t* vk = vs + (16 * k + vrow) * D + vsub;
 #pragma unroll
                 for (int o = 0; o < NO; ++o) {
