@@ -1001,6 +1001,10 @@ fia_status bsa_get_workspace_size(const fia_tensor* query, const fia_tensor* key
         }
     }
     if (tiles.size() > (size_t)INT32_MAX) return FIA_ERR_UNSUPPORTED;
+    // The workgroups of one kv head go to launch positions on one XCD (the
+    // tiles of a kv head's GQA group then share that XCD's L2).
+    tiles = xcd_order(tiles.size(), [&](size_t i) { return tiles[i]; },
+                      [&](size_t i) { return (int)((tiles[i].h / (N1 / N2)) % kNumXcds); });
     p->n_tiles = (int64_t)tiles.size();
     a.n_tiles = (int32_t)tiles.size();
     p->off_batch = 0;
