@@ -239,13 +239,14 @@ void bsa_params_init(bsa_params* p);
 /*
  * Phase 1 of block-sparse attention ("aclnnBlockSparseAttentionV2").
  *
- *   query, key, value  same layout (BNSD / BSND / TND) and dtype (fp16 / bf16),
- *                      D of 64 or 128, equal for q, k and v.
+ *   query, key, value  same layout (BNSD / BSND / TND) and dtype (fp16 / bf16,
+ *                      or FLOAT8_E4M3FN with the dequant scales of bsa_params),
+ *                      D of 64 or 128 (FP8: 128), equal for q, k and v.
  *   block_sparse_mask  required, uint8 or bool [B, N1, ceil(maxQS / X),
  *                      ceil(maxKVS / Y)]; nonzero = the kv block is selected for
  *                      that query head and q block.  Device tensor.
  *   atten_mask, block_table  must be NULL.
- *   attention_out      same shape and dtype as query.
+ *   attention_out      same shape as query; its dtype (bf16 for FP8 inputs).
  *   softmax_lse        fp32 [B, N1, Sq, 1] (TND [T, N1, 1]) when softmax_lse_flag.
  *
  * Attention inside the selected blocks is full (no causal mask); rows past
