@@ -49,7 +49,6 @@ def test_bsa_fp8_all_selected_and_negative_scale():
 
 def test_bsa_fp8_tnd():
     L = np.array([500, 64, 1000])
-    case = W.make_bsa_fp8("fp8_tnd", layout="BNSD", B=1, QN=2, KVN=1, Sq=1, D=128, seed=0)
     # TND: a [T, N, D] layout built from per-sequence BNSD draws
     seqs = [W.make_bsa_fp8("s", layout="BNSD", B=1, QN=4, KVN=2, Sq=int(n), D=128, Y=256, p=0.6,
                            seed=620 + i) for i, n in enumerate(L)]
