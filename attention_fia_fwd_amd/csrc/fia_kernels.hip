@@ -582,6 +582,11 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd(AttnArgs a)
         };
 #pragma unroll
         for (int s = 0; s < KPD; ++s) read_k(s);
+        // D_qk = 192: the wave in a matrix phase wins issue over the other
+        // wave's softmax (measured 3 % faster there; slower for the
+        // block-sparse D = 128 kernel, neutral for dense D = 128)
+        constexpr bool PRIO = DQK == 192;
+        if constexpr (PRIO) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int s = 0; s < NQ; ++s) {
             if (s + KPD < NQ) read_k(s + KPD);
@@ -589,6 +594,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd(AttnArgs a)
             s1 = O::mma32(ka1[s], qf[s], s1);
             __builtin_amdgcn_sched_barrier(0);
         }
+        if constexpr (PRIO) __builtin_amdgcn_s_setprio(0);
 
         // element mask (boundary tiles only): accumulator r holds kv index
         // c0 + 4 hh + kofs(r), kofs(r) = 32 (r/16) + 8 ((r%16)/4) + r%4; the
@@ -651,6 +657,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd(AttnArgs a)
 
         // P^T as the B operand: k-step k holds accumulators 8k..8k+7 of the
         // 32 (s0 then s1); the matching V rows come from two transposed reads.
+        if constexpr (PRIO) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             const f32x16& src = (k < 2) ? s0 : s1;
@@ -670,6 +677,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd(AttnArgs a)
                 acc[o] = O::mma32(va, pb, acc[o]);
             }
         }
+        if constexpr (PRIO) __builtin_amdgcn_s_setprio(0);
     }
 
     // epilogue: rows < q1 are written; rows in [qend, q1) and rows with no
