@@ -721,8 +721,11 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd(AttnArgs a)
 //     V widened exactly from E4M3FN to bf16 in LDS (E4M3FN values are bf16
 //     values), into the swizzled layout of the 16-bit kernel's V tiles.
 // K and V bytes of tile it + 1 go direct-to-LDS at the top of iteration it;
-// its V bytes are widened at the end of iteration it by the lanes whose
-// loads brought them, so the next per-tile barrier also publishes them.
+// its V bytes are widened at the end of iteration it, after a barrier that
+// frees the one bf16 V tile, by the lanes whose loads brought them, so the
+// next per-tile barrier also publishes them.  48 KB of LDS and at most 168
+// VGPRs give three workgroups per CU (14 % faster than two with a second bf16
+// V tile and one barrier per tile).
 // ---------------------------------------------------------------------------
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
@@ -734,12 +737,12 @@ __device__ __forceinline__ i32x4 rows_rsrc8(const uint8_t* base, int64_t row0, i
     return make_rsrc(base + row0 * stride, bytes);
 }
 
-__global__ __launch_bounds__(256, 2) void bsa_fp8(AttnArgs a)
+__global__ __launch_bounds__(256, 3) void bsa_fp8(AttnArgs a)
 {
     constexpr int NW = 4, BN = kBlockN, D = 128;
     constexpr int K8 = BN * D;               // K tile bytes
-    constexpr int VS8 = 2 * K8;              // offset of the bf16 V tile in a stage
-    constexpr int STAGE = K8 + K8 + 2 * BN * D;   // K bytes, V bytes, V bf16
+    constexpr int STAGE = K8 + K8;           // K bytes, V bytes
+    constexpr int VBF = 2 * STAGE;           // offset of the one bf16 V tile
     constexpr int NO = D / 32;
     using O = Ops<FIA_BF16>;
 
@@ -842,7 +845,7 @@ __global__ __launch_bounds__(256, 2) void bsa_fp8(AttnArgs a)
     // widen the V bytes this lane's loads brought into the bf16 tile
     auto widen = [&](int st) {
         uint8_t* base = smem8 + st * STAGE;
-        uint16_t* vbf = (uint16_t*)(base + VS8);
+        uint16_t* vbf = (uint16_t*)(smem8 + VBF);
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             const int sl = 64 * (NW * u + w) + lane;
@@ -893,7 +896,7 @@ __global__ __launch_bounds__(256, 2) void bsa_fp8(AttnArgs a)
 
         if (wend > wr0) {
             const uint8_t* kt = smem8 + st * STAGE;
-            const uint16_t* vs = (const uint16_t*)(kt + VS8);
+            const uint16_t* vs = (const uint16_t*)(smem8 + VBF);
             f32x16 s0, s1;
 #pragma unroll
             for (int r = 0; r < 16; ++r) s0[r] = s1[r] = 0.f;
@@ -1006,6 +1009,7 @@ __global__ __launch_bounds__(256, 2) void bsa_fp8(AttnArgs a)
         }
         if (it + 1 < ntiles) {
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();               // every wave is done with the bf16 V tile
             widen(st ^ 1);
         }
     }
@@ -1816,7 +1820,7 @@ int launch_bsa(const fia_plan& p, const AttnArgs& a, void* stream)
         if (e != hipSuccess) return (int)e;
     }
     if (a.fp8) {
-        const size_t lds = 2u * (2u * kBlockN * 128u + 2u * kBlockN * 128u);   // 2 stages of 32 KB
+        const size_t lds = 2u * (2u * kBlockN * 128u) + 2u * kBlockN * 128u;   // 2 x 16 KB + 16 KB
         static bool configured = false;
         raise_lds_limit(bsa_fp8, lds, configured);
         if (p.n_tiles == 0) return 0;
