@@ -61,6 +61,7 @@ class _Args(ctypes.Structure):
         ("q_bscale", ctypes.c_void_p), ("k_bscale", ctypes.c_void_p), ("v_bscale", ctypes.c_void_p),
         ("nqs", ctypes.c_int64), ("nks", ctypes.c_int64), ("qblk", ctypes.c_int64),
         ("kvblk", ctypes.c_int64),
+        ("q_rope", ctypes.c_void_p), ("k_rope", ctypes.c_void_p), ("Dr", ctypes.c_int64),
     ]
 
 
@@ -206,6 +207,13 @@ def attention(case, rows=None):
                 setattr(a, fld, _ptr(arr))
                 if (fld[0] == "k" and a.kmode == 1) or (fld[0] == "v" and a.vmode == 1):
                     a.tok_stride = t.shape[-1]
+    rope = getattr(case, "rope", None)
+    if rope is not None:
+        qr, kr = _bits(rope["query_rope"]), _bits(rope["key_rope"])
+        keep += [qr, kr]
+        qd = int(rope["query_rope"].shape[-1])
+        a.q_rope, a.k_rope = _ptr(qr), _ptr(kr)
+        a.Dr = qd // case.QN if case.layout == "BSH" else qd     # BSH: H = N * Dr
     r, n = _rows_arg(rows)
     if r is not None:
         keep.append(r)

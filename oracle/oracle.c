@@ -62,6 +62,13 @@
  * the fp32 scale of its block: query row i of (b, h) uses
  * qscale[b][h][i / qblk], key / value token j of (b, g) uses
  * kscale[b][g][j / kvblk] (vscale likewise).
+ *
+ * MLA (v2 page, query_rope / key_rope parameters and their constraints):
+ * with both rope inputs given, the query and key vectors are extended by
+ * their rope parts (width Dr, laid out like query and key with D = Dr), so
+ *   s_j = scale * (sum_d q[b,h,i,d] k[b,g,j,d] + sum_r qr[b,h,i,r] kr[b,g,j,r]);
+ * value and output keep D = Dv.  (The pages state the inputs and their
+ * shapes, not a formula for the rope parts; concatenation is the reading.)
  */
 #include <math.h>
 #include <stdint.h>
@@ -163,6 +170,11 @@ typedef struct {
     const double* k_bscale;          /* [B, KVN, nks] */
     const double* v_bscale;
     int64_t nqs, nks, qblk, kvblk;
+    /* MLA (query_rope / key_rope given): the score adds q_rope . k_rope, both
+     * of width Dr, laid out as the query and the key with D = Dr */
+    const uint16_t* q_rope;
+    const uint16_t* k_rope;
+    int64_t Dr;
 } oracle_args;
 
 static int64_t q_off(const oracle_args* a, int64_t b, int64_t h, int64_t i, int64_t D)
@@ -278,6 +290,12 @@ static int one_row(const oracle_args* a, const uint16_t* q, const void* k,
                                            a->q_bscale[(b * a->QN + h) * a->nqs + i / a->qblk]
                                      : elem(q, qo + d, a->dtype);
             acc += qv * kv_elem(a, k, ko + d, 0, b, g, j, d, a->Dqk);
+        }
+        if (a->Dr > 0) {
+            /* MLA: the rope parts extend the query and key vectors */
+            const int64_t qro = q_off(a, b, h, i, a->Dr), kro = kv_off(a, b, g, j, a->Dr);
+            for (d = 0; d < a->Dr; ++d)
+                acc += elem(a->q_rope, qro + d, a->dtype) * elem(a->k_rope, kro + d, a->dtype);
         }
         s[j] = a->scale * acc;
         if (s[j] > m)

@@ -734,3 +734,60 @@ def test_bsa_fp8_equals_bf16_on_the_dequantized_inputs(layout, Y):
     ro, rl = oracle.block_sparse(_bsa_fp8_as_bf16(case))
     np.testing.assert_array_equal(out, ro)
     np.testing.assert_array_equal(lse, rl)
+
+
+def _gather_rows(pool, bt, bs, pool_layout):
+    """[B, cols * bs, d] float64 copy of a single-kv-head paged pool."""
+    p = pool.to(torch.float64).numpy()
+    if pool_layout == 0:
+        p = p[:, 0]
+    out = np.zeros((bt.shape[0], bt.shape[1] * bs, p.shape[-1]))
+    for b in range(bt.shape[0]):
+        for c in range(bt.shape[1]):
+            if bt[b, c] >= 0:
+                out[b, c * bs:(c + 1) * bs] = p[bt[b, c]]
+    return out
+
+
+@pytest.mark.parametrize("pool_layout", [0, 1])
+@pytest.mark.parametrize("layout,S", [("BSND", 1), ("BNSD", 3), ("BSH", 2)])
+def test_mla_equals_brute_force_on_concatenated_vectors(pool_layout, layout, S):
+    # MLA (query_rope / key_rope): the score is scale * (q.k + q_rope.k_rope),
+    # i.e. attention over the concatenated [q, q_rope] and [k, k_rope] vectors,
+    # with value and output keeping D; query S > 1 is bottom-right causal
+    case = W.make_mla_decode(layout=layout, B=3, QN=4, Sq=S, lkv=[37, 5, 64], block_size=16,
+                             D=24, Dr=8, pool_layout=pool_layout, seed=61, extra_blocks=2)
+    out, lse = oracle.attention(case)
+    bt = case.block_table.numpy()
+    K = _gather_rows(case.k, bt, 16, pool_layout)
+    KR = _gather_rows(case.rope["key_rope"], bt, 16, pool_layout)
+    V = _gather_rows(case.v, bt, 16, pool_layout)
+
+    def bnsd(t, d):
+        x = t.to(torch.float64)
+        if layout == "BSH":
+            x = x.reshape(case.B, S, case.QN, d)
+        if layout != "BNSD":
+            x = x.permute(0, 2, 1, 3)
+        return x.numpy()
+
+    q, qr = bnsd(case.q, 24), bnsd(case.rope["query_rope"], 8)
+    o = out if layout == "BNSD" else np.transpose(out, (0, 2, 1, 3))
+    for b in range(case.B):
+        L = int(case.lkv[b])
+        for h in range(case.QN):
+            for t in range(S):
+                n = L - S + t + 1 if S > 1 else L       # keys j <= L - S + t
+                s = case.scale * (K[b, :n] @ q[b, h, t] + KR[b, :n] @ qr[b, h, t])
+                w = np.exp(s - s.max())
+                assert np.max(np.abs(o[b, h, t] - w @ V[b, :n] / w.sum())) < 1e-12
+                assert abs(lse[b, h, t] - (s.max() + math.log(w.sum()))) < 1e-12
+
+
+def test_mla_zero_key_rope_equals_plain_attention():
+    case = W.make_mla_decode(B=2, QN=8, Sq=1, lkv=[50, 17], block_size=16, D=32, Dr=8, seed=62)
+    case.rope["key_rope"] = torch.zeros_like(case.rope["key_rope"])
+    out, lse = oracle.attention(case)
+    case.rope = None
+    out0, lse0 = oracle.attention(case)
+    assert np.array_equal(out, out0) and np.array_equal(lse, lse0)

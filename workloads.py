@@ -92,6 +92,8 @@ class FiaCase:
     # "dequant_offset_key": t|None, "dequant_offset_value": t|None,
     # "key_quant_mode": 0|1, "value_quant_mode": 0|1}
     quant: Optional[dict] = None
+    # MLA: {"query_rope": t, "key_rope": t}, laid out like query / key with D = 64
+    rope: Optional[dict] = None
 
     @property
     def decode(self) -> bool:
@@ -335,6 +337,67 @@ def make_paged_prefill(name="custom", *, layout="BNSD", dtype=torch.bfloat16, B=
                    next_tokens=next_tokens, lq=lq, lkv=lkv, q=q, k=k, v=v, atten_mask=mask,
                    block_table=torch.from_numpy(table).to(device), block_size=block_size,
                    pool_layout=pool_layout, return_lse=return_lse, meta={"NB": NB})
+
+
+def make_mla_decode(name="custom", *, layout="BSND", dtype=torch.bfloat16, B=2, QN=16, Sq=1,
+                    lq=None, lkv=(100, 37), block_size=16, D=512, Dr=64, pool_layout=1,
+                    scale=None, seed=0, device="cpu", extra_blocks=0, nan_pool=False,
+                    return_lse=True) -> FiaCase:
+    """MLA decode: query (``layout``, Q_N = QN, S = Sq <= 16, D = 512) with its
+    64-wide rope part, one kv head; key and value (D = 512) and key_rope
+    (D = 64) in a shared paged pool, (NB, bs, D) (``pool_layout`` 1) or
+    (NB, 1, bs, D) (0), addressed through a block table holding a seeded
+    permutation of the pool's block ids.  Query S > 1 uses bottom-right causal
+    masking (sparse_mode 3 with the 2048 template).  iid N(0,1) inputs; scale
+    1/sqrt(D + Dr) unless given.  ``nan_pool`` fills the unreferenced blocks
+    and the tail rows of each batch's last block with NaN."""
+    scale = 1.0 / math.sqrt(D + Dr) if scale is None else scale
+    ss = _streams(seed)
+    lkv = np.asarray(lkv, dtype=np.int64)
+    if lq is not None:
+        lq = np.asarray(lq, dtype=np.int64)
+    nblk = [(int(L) + block_size - 1) // block_size for L in lkv]
+    NB = sum(nblk) + extra_blocks
+    cols = max(max(nblk), 1)
+    rng = np.random.default_rng(ss[STREAM_TABLE])
+    perm = rng.permutation(NB).astype(np.int32)
+    table = np.full((B, cols), -1, dtype=np.int32)
+    pos = 0
+    for b in range(B):
+        table[b, :nblk[b]] = perm[pos:pos + nblk[b]]
+        pos += nblk[b]
+    sq, sqr = ss[STREAM_Q].spawn(2)
+    sk, skr = ss[STREAM_K].spawn(2)
+    q = normal_tensor(_shape(layout, B, QN, Sq, D), dtype, sq, device)
+    qr = normal_tensor(_shape(layout, B, QN, Sq, Dr), dtype, sqr, device)
+    def pool(d):
+        return (NB, 1, block_size, d) if pool_layout == 0 else (NB, block_size, d)
+    k = normal_tensor(pool(D), dtype, sk, device)
+    kr = normal_tensor(pool(Dr), dtype, skr, device)
+    v = normal_tensor(pool(D), dtype, ss[STREAM_V], device)
+    if nan_pool:
+        used = set(int(x) for x in table.reshape(-1) if x >= 0)
+        for t in (k, kr, v):
+            for blk in range(NB):
+                if blk not in used:
+                    t[blk] = float("nan")
+            for b in range(B):
+                if nblk[b] == 0:
+                    continue
+                last, tail = int(table[b, nblk[b] - 1]), int(lkv[b]) - (nblk[b] - 1) * block_size
+                if pool_layout == 0:
+                    t[last, :, tail:] = float("nan")
+                else:
+                    t[last, tail:] = float("nan")
+    mask = None
+    if Sq > 1:
+        mask = torch.triu(torch.ones(2048, 2048, dtype=torch.uint8), diagonal=1).to(device)
+    return FiaCase(name=name, layout=layout, dtype=dtype, B=B, QN=QN, KVN=1, Sq=Sq,
+                   Skv=cols * block_size, Dqk=D, Dv=D, scale=scale, sparse_mode=3 if Sq > 1 else 0,
+                   lq=lq, lkv=lkv, q=q, k=k, v=v, atten_mask=mask,
+                   block_table=torch.from_numpy(table).to(device), block_size=block_size,
+                   pool_layout=pool_layout, return_lse=return_lse, meta={"NB": NB},
+                   rope={"query_rope": qr, "key_rope": kr})
 
 
 def make_quant_decode(name="custom", *, layout="BNSD", B=2, QN=4, KVN=2, D=64, Sq=1, Skv=None,
@@ -606,6 +669,17 @@ def fp8_block_sparse(device="cpu") -> BsaCase:
                         device=device)
 
 
+def mla_decode_bf16(device="cpu") -> FiaCase:
+    """MLA decode: B=64, Q_S=1, Q_N=128, one kv head, D=512 + rope 64, bf16,
+    BSND query, KV lengths ~ U{512..16384}, page 128 tokens, pools
+    (NB, 128, 512) for key and value and (NB, 128, 64) for key_rope, LSE on."""
+    rng = np.random.default_rng(_streams(1010)[STREAM_LENGTHS])
+    lkv = rng.integers(512, 16384, size=64, endpoint=True).astype(np.int64)
+    return make_mla_decode("mla_decode_bf16_b64_n128_d512_rope64_bs128", layout="BSND",
+                           dtype=torch.bfloat16, B=64, QN=128, Sq=1, lkv=lkv, block_size=128,
+                           pool_layout=1, seed=1010, device=device)
+
+
 WORKLOADS = {
     "c1": c1_dense_causal_fp16,
     "c2": c2_gqa_causal_bf16,
@@ -616,4 +690,5 @@ WORKLOADS = {
     "mtp_decode": paged_mtp_decode_bf16,
     "int8_decode": int8_kv_decode_bf16,
     "fp8_bsa": fp8_block_sparse,
+    "mla_decode": mla_decode_bf16,
 }
