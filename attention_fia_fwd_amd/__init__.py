@@ -98,6 +98,7 @@ class FiaPlan:
                  inner_precise: int = 0, return_softmax_lse: bool = False,
                  dequant_scale_key=None, dequant_scale_value=None, dequant_offset_key=None,
                  dequant_offset_value=None, key_quant_mode: int = 0, value_quant_mode: int = 0,
+                 query_rope=None, key_rope=None,
                  out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None):
         self.plan = None
         kvn = num_key_value_heads or num_heads
@@ -123,7 +124,7 @@ class FiaPlan:
                                   device=query.device)
         self.out, self.lse = out, (lse if return_softmax_lse else None)
         quant = (dequant_scale_key, dequant_scale_value, dequant_offset_key, dequant_offset_value)
-        self._keep = (query, key, value, atten_mask, block_table, out, lse) + quant
+        self._keep = (query, key, value, atten_mask, block_table, out, lse, query_rope, key_rope) + quant
         p = fia_params()
         fia_params_init(p)
         self._layout = input_layout.encode()
@@ -144,6 +145,8 @@ class FiaPlan:
         (p.dequant_scale_key, p.dequant_scale_value, p.dequant_offset_key,
          p.dequant_offset_value) = [ctypes.pointer(d) if d is not None else None for d in self._qdesc]
         p.key_quant_mode, p.value_quant_mode = key_quant_mode, value_quant_mode
+        self._rdesc = [describe(t) for t in (query_rope, key_rope)]
+        p.query_rope, p.key_rope = [ctypes.pointer(d) if d is not None else None for d in self._rdesc]
         st, ws, plan = fia_get_workspace_size(describe(query), describe(key), describe(value),
                                               describe(atten_mask), describe(block_table), p,
                                               describe(out),

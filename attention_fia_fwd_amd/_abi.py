@@ -51,6 +51,8 @@ class fia_params(ctypes.Structure):
         ("dequant_offset_value", ctypes.POINTER(fia_tensor)),
         ("key_quant_mode", ctypes.c_int64),
         ("value_quant_mode", ctypes.c_int64),
+        ("query_rope", ctypes.POINTER(fia_tensor)),
+        ("key_rope", ctypes.POINTER(fia_tensor)),
     ]
 
 

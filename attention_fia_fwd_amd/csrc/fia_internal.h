@@ -29,6 +29,8 @@ constexpr int kDecodeHeads = 16;
 // size the decode schedule.
 constexpr int kNumCUs = 256;
 constexpr int kDecodeWavesPerCU = 8;
+// Largest MLA decode workgroup (waves of 16 query rows each).
+constexpr int kMlaMaxWaves = 8;
 
 // Per-batch addressing, 24 bytes.  row0 is the first row of batch b on the
 // tensor's row axis: b * S for BNSD/BSND, the cumulative start for TND.
@@ -154,6 +156,14 @@ struct DecodeArgs {
     int32_t n_waves, n_pieces;
     float scale_log2;
     int32_t return_lse;
+    // MLA: query_rope (the query's layout, D 64; element strides batch, head,
+    // token), the key_rope pool (block stride pr_blk, token stride 64) and
+    // the waves per workgroup (0 = not MLA)
+    const void* qr;
+    const void* kr;
+    int64_t qr_sB, qr_sH, qr_sS;
+    int64_t pr_blk;
+    int32_t mla_nw;
 };
 
 }  // namespace fia

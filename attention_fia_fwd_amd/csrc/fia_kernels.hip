@@ -1650,6 +1650,264 @@ __global__ __launch_bounds__(64) void decode_split_i8(DecodeArgs a)
     }
 }
 
+// ---------------------------------------------------------------------------
+// MLA decode (query D 512 + rope 64, one kv head, paged K / V / K-rope pools).
+//
+// The Q_N x S (head, token) rows of a batch share every K/V byte, so a
+// workgroup of NW waves serves Gc <= 16 NW rows, wave w the 16 columns
+// 16 w .. 16 w + 15 of v_mfma_f32_16x16x32 (the decode kernel's layout):
+//   S^T (32 tokens x 16 rows) = [K | K_rope] [Q | Q_rope]^T, 18 k-steps,
+//       Q and Q_rope in registers (B operand), K rows read from LDS;
+//   O^T (512 x 16) += V^T P^T, 32 tiles, V through transposed LDS reads.
+// Per 32-token step the workgroup moves K (32 x 512), K_rope (32 x 64) and
+// V (32 x 512) straight into LDS (two stages, 2 x 68 KB): each K / V row is
+// one 1 KB direct-to-LDS load, spread over the waves.  One barrier per step:
+// wait for the own loads of step st, barrier (all of step st has landed and
+// every wave is done with step st - 1), issue step st + 1 into the other
+// stage, compute step st.  16-byte chunks are XOR-swizzled per row so the
+// 16 rows a quarter-wave reads hit distinct banks.
+// ---------------------------------------------------------------------------
+constexpr int kMlaD = 512, kMlaDR = 64;
+constexpr int kMlaStageHalves = kDecodeStep * (2 * kMlaD + kMlaDR);
+
+template <int DT, int NW>
+__global__ __launch_bounds__(NW * 64, 1) void mla_decode(DecodeArgs a)
+{
+    constexpr int D = kMlaD, DR = kMlaDR;
+    constexpr int ST = kDecodeStep;                 // 32 tokens per step
+    constexpr int NKM = D / 32, NKR = DR / 32;      // k-steps: latent, rope
+    constexpr int NO = D / 16;                      // O^T tiles
+    constexpr int KR_OFF = ST * D;                  // stage layout (halves): K | K_rope | V
+    constexpr int V_OFF = ST * (D + DR);
+    using O = Ops<DT>;
+    extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
+    const uint32_t smem_lds = (uint32_t)(uintptr_t)(lds_void*)smem;
+
+    const int lane = threadIdx.x & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int n = lane & 15, qd = lane >> 4;
+    const int R = a.G * a.S;                        // rows of the (single) kv head
+    const int p_end = a.wave_first[blockIdx.x + 1];
+    for (int item = a.wave_first[blockIdx.x]; item < p_end; ++item) {
+        const DecPiece pc_ = a.pieces[item];
+        const DecSeg db = a.segs[pc_.seg];
+        const int b = db.b;
+        const int hc = pc_.seg % a.nhc;
+        const int t0 = pc_.t0, t1 = pc_.t1;
+        const int S = a.S;
+        const int c0 = a.Gc * hc + 16 * wid;        // first row of this wave
+        const int nh = max(0, min(16, min(a.Gc * (hc + 1), R) - c0));
+        const int rq = c0 + n;
+        const int tq = rq % S, hq = rq / S;
+        const float c = fmaxf(fabsf(a.scale_log2), kMinScale);
+        const uint32_t qflip = a.scale_log2 < 0.f ? 0x80008000u : 0u;
+        const int jbase = db.lkv - db.lq;
+        const int tq_min = (c0 % S) + nh > S ? 0 : c0 % S;
+        const int jmax = a.causal ? jbase + tq : INT32_MAX;
+        const int jmin = a.causal ? jbase + tq_min : INT32_MAX;
+
+        // [Q | Q_rope]^T as the B operand: column n, d = 32 s + 8 qd
+        uint4 qf[NKM + NKR];
+        if (n < nh) {
+            const uint16_t* src = (const uint16_t*)a.q + (int64_t)b * a.q_sB + (int64_t)hq * a.q_sH +
+                                  (int64_t)tq * a.q_sS + 8 * qd;
+            const uint16_t* srr = (const uint16_t*)a.qr + (int64_t)b * a.qr_sB + (int64_t)hq * a.qr_sH +
+                                  (int64_t)tq * a.qr_sS + 8 * qd;
+#pragma unroll
+            for (int s = 0; s < NKM + NKR; ++s) {
+                uint4 v = s < NKM ? *(const uint4*)(src + 32 * s) : *(const uint4*)(srr + 32 * (s - NKM));
+                v.x ^= qflip; v.y ^= qflip; v.z ^= qflip; v.w ^= qflip;
+                qf[s] = v;
+            }
+        } else {
+#pragma unroll
+            for (int s = 0; s < NKM + NKR; ++s) qf[s] = make_uint4(0, 0, 0, 0);
+        }
+
+        // pages of the piece: lane i holds the id of page pg_first + i
+        const int bs = a.block_size;
+        const int32_t* bt = a.block_table + (int64_t)b * a.bt_stride;
+        const int pg_first = t0 / bs;
+        const int pg_last = t1 > t0 ? (t1 - 1) / bs : pg_first;
+        const int my_page = pg_first + lane <= pg_last ? bt[pg_first + lane] : 0;
+        const uint16_t* kbase = (const uint16_t*)a.k;
+        const uint16_t* vbase = (const uint16_t*)a.v;
+        const uint16_t* rbase = (const uint16_t*)a.kr;
+
+        // one step's loads: rows [tt0, tt0 + 32) as two 16-row sub-tiles
+        // (page pg0 offset off0, page pg1 offset off1); rows past t1 read 0
+        auto issue = [&](int tt0, int pg0, int off0, int pg1, int off1, uint32_t stage) {
+            // the per-lane offsets are recomputed at every step (a few VALU
+            // ops) instead of being held in registers across the loop
+            int ln = lane;
+            asm volatile("" : "+v"(ln));
+            i32x4 rk[2], rv[2], rr[2];
+#pragma unroll
+            for (int cc = 0; cc < 2; ++cc) {
+                const int pg = cc ? pg1 : pg0, off = cc ? off1 : off0;
+                const int nvalid = max(0, min(16, t1 - (tt0 + 16 * cc)));
+                const int64_t page =
+                    nvalid > 0 ? (int64_t)__builtin_amdgcn_readlane(my_page, pg - pg_first) : 0;
+                rk[cc] = make_rsrc(kbase + page * a.p_blk + (int64_t)off * D, (int64_t)nvalid * D * 2);
+                rv[cc] = make_rsrc(vbase + page * a.p_blk + (int64_t)off * D, (int64_t)nvalid * D * 2);
+                rr[cc] = make_rsrc(rbase + page * a.pr_blk + (int64_t)off * DR, (int64_t)nvalid * DR * 2);
+            }
+#pragma unroll
+            for (int i = 0; i < ST / NW; ++i) {
+                const int r = NW * i + wid;          // row of the step
+                const i32x4 k_rs = r < 16 ? rk[0] : rk[1];
+                const i32x4 v_rs = r < 16 ? rv[0] : rv[1];
+                const uint32_t row = (uint32_t)((r & 15) * D);
+                dma16(k_rs, stage + 2u * (uint32_t)(r * D), (row + 8u * (uint32_t)(ln ^ (r & 15))) * 2u);
+                dma16(v_rs, stage + 2u * (uint32_t)(V_OFF + r * D),
+                      (row + 8u * (uint32_t)(ln ^ (2 * (r & 7)))) * 2u);
+            }
+            // K_rope: 8 rows of 128 bytes per load, four loads per step
+            for (int u = wid; u < 4; u += NW) {
+                const int r = 8 * u + (ln >> 3);
+                const uint32_t chunk = (uint32_t)((ln & 7) ^ ((r >> 1) & 7));
+                dma16(u < 2 ? rr[0] : rr[1], stage + 2u * (uint32_t)(KR_OFF + 8 * u * DR),
+                      ((uint32_t)((r & 15) * DR) + 8u * chunk) * 2u);
+            }
+        };
+
+        // LDS read offsets (halves) as per-lane bases plus constants:
+        // K row n, chunk (4 s + qd) ^ n = 16 (s / 4) + 4 ((s % 4) ^ (n / 4)) + (qd ^ n % 4);
+        // K_rope row n, chunk (4 s + qd) ^ ((n / 2) % 8) (the same for row 16 + n);
+        // V^T (transposed reads as in the decode kernel): tile o = 8 og + oi
+        // reads chunk pair 2 (o ^ (trow % 8)) = 16 og + 2 (oi ^ (trow % 8)).
+        int koff[4], roff[NKR], voffs[8];
+#pragma unroll
+        for (int si = 0; si < 4; ++si) koff[si] = n * D + 8 * (4 * (si ^ (n >> 2)) + (qd ^ (n & 3)));
+#pragma unroll
+        for (int sr = 0; sr < NKR; ++sr) roff[sr] = n * DR + 8 * ((4 * sr + qd) ^ ((n >> 1) & 7));
+        {
+            const int vi = lane & 15;
+            const int trow = 4 * qd + (vi >> 2);
+            const int tcol_lo = (vi & 3) >> 1, tsub = 4 * (vi & 1);
+#pragma unroll
+            for (int oi = 0; oi < 8; ++oi) voffs[oi] = trow * D + 8 * (2 * (oi ^ (trow & 7)) + tcol_lo) + tsub;
+        }
+
+        f32x4 acc[NO];
+#pragma unroll
+        for (int o = 0; o < NO; ++o) acc[o] = f32x4{0.f, 0.f, 0.f, 0.f};
+        float m = -INFINITY, l = 0.f;
+        const float lazy_raw = kLazy / c;
+
+        const int nsteps = (t1 - t0 + ST - 1) / ST;
+        int pg = t0 / bs, off = t0 % bs;
+        auto advance16 = [&](int& p, int& o) {
+            o += 16;
+            if (o >= bs) { o -= bs; ++p; }
+        };
+        if (nsteps > 0) {
+            int pg1 = pg, off1 = off;
+            advance16(pg1, off1);
+            issue(t0, pg, off, pg1, off1, smem_lds);
+            pg = pg1; off = off1;
+            advance16(pg, off);
+        }
+        for (int st = 0; st < nsteps; ++st) {
+            const int tt0 = t0 + ST * st;
+            __builtin_amdgcn_s_waitcnt(FIA_VMCNT(0));
+            __syncthreads();
+            if (st + 1 < nsteps) {
+                int pg1 = pg, off1 = off;
+                advance16(pg1, off1);
+                issue(tt0 + ST, pg, off, pg1, off1, smem_lds + 2u * kMlaStageHalves * (uint32_t)((st + 1) & 1));
+                pg = pg1; off = off1;
+                advance16(pg, off);
+            }
+            if (nh == 0) continue;
+            const uint16_t* kb = smem + kMlaStageHalves * (st & 1);
+            const uint16_t* krb = kb + KR_OFF;
+            const uint16_t* vb = kb + V_OFF;
+
+            f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < NKM; ++s) {
+                const uint16_t* kp = kb + koff[s & 3] + 128 * (s >> 2);
+                const uint4 a0 = *(const uint4*)(kp);
+                const uint4 a1 = *(const uint4*)(kp + 16 * D);
+                s0 = O::mma16(a0, qf[s], s0);
+                s1 = O::mma16(a1, qf[s], s1);
+            }
+#pragma unroll
+            for (int s = 0; s < NKR; ++s) {
+                const uint4 a0 = *(const uint4*)(krb + roff[s]);
+                const uint4 a1 = *(const uint4*)(krb + roff[s] + 16 * DR);
+                s0 = O::mma16(a0, qf[NKM + s], s0);
+                s1 = O::mma16(a1, qf[NKM + s], s1);
+            }
+            float x[8];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                x[i] = s0[i];
+                x[4 + i] = s1[i];
+            }
+            if (tt0 + ST > t1 || tt0 + ST - 1 > jmin) {
+#pragma unroll
+                for (int r = 0; r < 8; ++r) {
+                    const int tk = tt0 + 16 * (r >> 2) + 4 * qd + (r & 3);
+                    if (tk >= t1 || tk > jmax) x[r] = -INFINITY;
+                }
+            }
+            float mt = x[0];
+#pragma unroll
+            for (int r = 1; r < 8; ++r) mt = fmaxf(mt, x[r]);
+            mt = quad_max(mt);
+            const float mn = fmaxf(m, mt);
+            const bool grow = (m == -INFINITY) ? (mn > -INFINITY) : (mn > m + lazy_raw);
+            if (__ballot(grow)) {
+                float alpha = 1.f;
+                if (m == -INFINITY) alpha = 0.f;
+                else if (mn != -INFINITY) alpha = fast_exp2((m - mn) * c);
+                m = mn;
+                l *= alpha;
+#pragma unroll
+                for (int o = 0; o < NO; ++o) acc[o] *= alpha;
+            }
+            const float mc = (m == -INFINITY) ? 0.f : m * c;
+            float ps = 0.f;
+#pragma unroll
+            for (int r = 0; r < 8; ++r) {
+                x[r] = fast_exp2(__builtin_fmaf(x[r], c, -mc));
+                ps += x[r];
+            }
+            l += ps;
+            uint4 pb;
+            pb.x = O::pack2(x[0], x[1]);
+            pb.y = O::pack2(x[2], x[3]);
+            pb.z = O::pack2(x[4], x[5]);
+            pb.w = O::pack2(x[6], x[7]);
+#pragma unroll
+            for (int o = 0; o < NO; ++o) {
+                const uint16_t* vp = vb + voffs[o & 7] + 128 * (o >> 3);
+                const uint2 lo = lds_read_tr16(vp);
+                const uint2 hi = lds_read_tr16(vp + 16 * D);
+                acc[o] = O::mma16(make_uint4(lo.x, lo.y, hi.x, hi.y), pb, acc[o]);
+            }
+        }
+
+        // partial: normalised O and natural-log LSE of this split
+        const float lt = quad_sum(l);
+        if (n < nh) {
+            const float inv = lt > 0.f ? 1.f / lt : 0.f;
+            float* po = a.part_o + ((int64_t)item * a.Gc + 16 * wid + n) * D;
+#pragma unroll
+            for (int o = 0; o < NO; ++o) {
+                f32x4 v = acc[o] * inv;
+                *(f32x4*)(po + 16 * o + 4 * qd) = v;
+            }
+            if (qd == 0)
+                a.part_lse[(int64_t)item * a.Gc + 16 * wid + n] =
+                    lt > 0.f ? (m * c + __log2f(lt)) * kLn2 : -INFINITY;
+        }
+        __syncthreads();     // the stages are reused by the next piece
+    }
+}
+
 // Merge the kv splits of one (batch, head, query token): weights
 // exp(lse_s - max lse).  Tokens at or past the batch's query length are
 // written as out = 0, lse = +inf.
@@ -1662,7 +1920,7 @@ __global__ __launch_bounds__(64) void decode_combine(DecodeArgs a)
     const int t = bht % S;
     const int b = bht / (a.QN * S), h = (bht / S) % a.QN;
     const int kvh = h / a.G, r = (h % a.G) * S + t;
-    const int hc = r / kDecodeHeads, n = r % kDecodeHeads;
+    const int hc = r / a.Gc, n = r % a.Gc;
     const DecSeg sg = a.segs[((int64_t)b * a.KVN + kvh) * a.nhc + hc];
     const int ns = t < sg.lq ? sg.count : 0;
     const int64_t slot0 = sg.first;
@@ -1835,9 +2093,36 @@ int launch_bsa(const fia_plan& p, const AttnArgs& a, void* stream)
     return (int)hipErrorInvalidValue;
 }
 
+template <int DT, int NW>
+int launch_mla_nw(const fia_plan& p, const DecodeArgs& a, hipStream_t stream)
+{
+    const size_t lds = 2u * kMlaStageHalves * sizeof(uint16_t);    // 2 x 68 KB
+    static bool configured = false;
+    raise_lds_limit(mla_decode<DT, NW>, lds, configured);
+    if (p.n_waves > 0)
+        hipLaunchKernelGGL((mla_decode<DT, NW>), dim3((unsigned)p.n_waves), dim3(NW * 64), lds, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return (int)e;
+    hipLaunchKernelGGL((decode_combine<DT, kMlaD>), dim3((unsigned)(p.B * p.QN * a.S)), dim3(64), 0, stream, a);
+    return (int)hipGetLastError();
+}
+
+template <int DT>
+int launch_mla(const fia_plan& p, const DecodeArgs& a, hipStream_t s)
+{
+    switch (a.mla_nw) {
+    case 1: return launch_mla_nw<DT, 1>(p, a, s);
+    case 2: return launch_mla_nw<DT, 2>(p, a, s);
+    case 4: return launch_mla_nw<DT, 4>(p, a, s);
+    case 8: return launch_mla_nw<DT, 8>(p, a, s);
+    }
+    return (int)hipErrorInvalidValue;
+}
+
 int launch_decode(const fia_plan& p, const DecodeArgs& a, void* stream)
 {
     hipStream_t s = (hipStream_t)stream;
+    if (a.mla_nw) return p.dtype == FIA_BF16 ? launch_mla<FIA_BF16>(p, a, s) : launch_mla<FIA_F16>(p, a, s);
     const bool bf = p.dtype == FIA_BF16;
     if (p.Dqk == 64) return bf ? launch_dec<FIA_BF16, 64>(p, a, s) : launch_dec<FIA_F16, 64>(p, a, s);
     if (p.Dqk == 128) return bf ? launch_dec<FIA_BF16, 128>(p, a, s) : launch_dec<FIA_F16, 128>(p, a, s);

@@ -294,6 +294,18 @@ fia_status fia_get_workspace_size(const fia_tensor* query, const fia_tensor* key
         if (any_quant) return FIA_ERR_PARAM;
     }
 
+    // MLA: query_rope and key_rope both given or both absent (v2 page,
+    // query_rope / key_rope constraints), in the query's dtype
+    const bool mla = prm->query_rope || prm->key_rope;
+    if (mla) {
+        if (!prm->query_rope || !prm->key_rope) return FIA_ERR_PARAM;
+        if (!prm->query_rope->data || !prm->key_rope->data) return FIA_ERR_NULLPTR;
+        if (kv_i8) return FIA_ERR_UNSUPPORTED;
+        if (prm->query_rope->dtype != query->dtype || prm->key_rope->dtype != query->dtype)
+            return FIA_ERR_DTYPE;
+        if (!valid_rank(prm->query_rope) || !valid_rank(prm->key_rope)) return FIA_ERR_SHAPE;
+    }
+
     int32_t layout;
     bool bsh;
     fia_status st = parse_layout(prm->input_layout, &layout, &bsh);
@@ -302,7 +314,8 @@ fia_status fia_get_workspace_size(const fia_tensor* query, const fia_tensor* key
     const int64_t QN = prm->num_heads;
     if (QN <= 0 || QN > 256) return FIA_ERR_PARAM;
     const int64_t KVN = prm->num_key_value_heads == 0 ? QN : prm->num_key_value_heads;
-    if (KVN <= 0 || QN % KVN != 0 || QN / KVN > 64) return FIA_ERR_PARAM;
+    // GQA ratio <= 64; MLA allows 128 query heads on its single kv head
+    if (KVN <= 0 || QN % KVN != 0 || QN / KVN > (mla ? 128 : 64)) return FIA_ERR_PARAM;
     if (prm->sparse_mode < 0 || prm->sparse_mode > 4) return FIA_ERR_PARAM;
     if (prm->inner_precise < 0 || prm->inner_precise > 3) return FIA_ERR_PARAM;
     if (!(std::isfinite(prm->scale_value))) return FIA_ERR_PARAM;
@@ -335,7 +348,12 @@ fia_status fia_get_workspace_size(const fia_tensor* query, const fia_tensor* key
         if (block_table->dtype != FIA_I32) return FIA_ERR_DTYPE;
         if (block_table->ndim != 2 || block_table->dims[0] != gq.B) return FIA_ERR_SHAPE;
         if (prm->block_size <= 0 || prm->block_size % 16 != 0) return FIA_ERR_PARAM;
-        if (!decode && (prm->block_size % 128 != 0 || prm->block_size > 512)) return FIA_ERR_PARAM;
+        if (mla) {
+            // MLA with a query D of 512: block_size 16 or 128
+            if (prm->block_size != 16 && prm->block_size != 128) return FIA_ERR_PARAM;
+        } else if (!decode && (prm->block_size % 128 != 0 || prm->block_size > 512)) {
+            return FIA_ERR_PARAM;
+        }
         if (!prm->actual_seq_kvlen) return FIA_ERR_PARAM;
         if (key->ndim != value->ndim) return FIA_ERR_SHAPE;
         for (int i = 0; i < key->ndim; ++i)
@@ -484,8 +502,36 @@ fia_status fia_get_workspace_size(const fia_tensor* query, const fia_tensor* key
         }
     }
 
+    // ----- MLA (query D 512, rope D 64, one kv head, paged) -----
+    const void* qr_data = nullptr;
+    int64_t qr_sB = 0, qr_sH = 0, qr_sS = 0;
+    if (mla) {
+        if (layout == LAYOUT_TND || !paged) return FIA_ERR_UNSUPPORTED;
+        if (gq.D != 512 || Dv != 512) return FIA_ERR_UNSUPPORTED;
+        if (KVN != 1 || QN > 128 || (QN & (QN - 1)) != 0) return FIA_ERR_UNSUPPORTED;
+        if (gq.S > kDecodeHeads) return FIA_ERR_UNSUPPORTED;
+        // S == 1: sparse_mode 0 without a mask; S > 1: sparse_mode 3
+        if (mask || (gq.S == 1 && atten_mask) || (gq.S > 1 && mode != 3)) return FIA_ERR_UNSUPPORTED;
+        Geo gr;
+        if ((st = geometry(prm->query_rope, layout, bsh, QN, &gr)) != FIA_OK) return st;
+        if (gr.N != QN || gr.B != gq.B || gr.S != gq.S || gr.D != 64) return FIA_ERR_SHAPE;
+        const fia_tensor* kr = prm->key_rope;
+        const int64_t bs = prm->block_size;
+        const bool ok = (kr->ndim == 4 && kr->dims[1] == 1 && kr->dims[2] == bs && kr->dims[3] == 64) ||
+                        (kr->ndim == 3 && kr->dims[1] == bs && kr->dims[2] == 64);
+        if (!ok || kr->dims[0] != pool_blocks) return FIA_ERR_SHAPE;
+        qr_data = prm->query_rope->data;
+        if (layout == LAYOUT_BNSD) {
+            qr_sB = QN * gq.S * 64; qr_sH = gq.S * 64; qr_sS = 64;
+        } else {
+            qr_sB = gq.S * QN * 64; qr_sH = 64; qr_sS = QN * 64;
+        }
+    }
+
     // ----- supported head dims -----
-    if (decode) {
+    if (mla) {
+        // checked above
+    } else if (decode) {
         if (!((gq.D == 64 || gq.D == 128) && Dv == gq.D)) return FIA_ERR_UNSUPPORTED;
     } else {
         const bool ok = (gq.D == 64 && Dv == 64) || (gq.D == 128 && Dv == 128) ||
@@ -501,7 +547,7 @@ fia_status fia_get_workspace_size(const fia_tensor* query, const fia_tensor* key
     // byte is read once for all those rows and the kv range is spread over
     // the whole GPU.  Everything else runs on the prefill kernel.
     const bool dec_kernel =
-        decode || (layout != LAYOUT_TND && gq.S <= kDecodeHeads && p->G * gq.S <= kDecodeHeads &&
+        mla || decode || (layout != LAYOUT_TND && gq.S <= kDecodeHeads && p->G * gq.S <= kDecodeHeads &&
                    mask == nullptr && (mode == 3 || mode == 0) && Dv == gq.D &&
                    (gq.D == 64 || gq.D == 128));
 
@@ -596,8 +642,17 @@ fia_status fia_get_workspace_size(const fia_tensor* query, const fia_tensor* key
         }
         const int64_t G = QN / KVN;
         const int64_t R = G * S;       // (head, token) rows of one kv head
-        const int64_t Gc = std::min<int64_t>(R, kDecodeHeads);
-        const int64_t nhc = (R + kDecodeHeads - 1) / kDecodeHeads;
+        // rows per chunk: 16 (one wave), or for MLA up to 16 x 8 (one
+        // workgroup of nw waves)
+        int64_t nw = 0;
+        if (mla) {
+            const int64_t need = (std::min<int64_t>(R, 16 * kMlaMaxWaves) + 15) / 16;
+            nw = 1;
+            while (nw < need) nw *= 2;
+        }
+        const int64_t rows_per_chunk = mla ? 16 * nw : kDecodeHeads;
+        const int64_t Gc = std::min<int64_t>(R, rows_per_chunk);
+        const int64_t nhc = (R + rows_per_chunk - 1) / rows_per_chunk;
         // Balanced schedule: one wave per resident slot, each with an equal
         // quota of the concatenated token stream (a multiple of 16 tokens, so
         // a 16-token sub-tile never crosses a page).
@@ -605,7 +660,8 @@ fia_status fia_get_workspace_size(const fia_tensor* query, const fia_tensor* key
         int64_t total = 0;
         for (int64_t b = 0; b < B; ++b) total += lkv[(size_t)b] * KVN * nhc;
         const int64_t steps = (total + kDecodeStep - 1) / kDecodeStep;
-        const int64_t W = std::min<int64_t>((int64_t)kNumCUs * kDecodeWavesPerCU, steps);
+        // one MLA workgroup per CU (its two stages fill most of the LDS)
+        const int64_t W = std::min<int64_t>((int64_t)kNumCUs * (mla ? 1 : kDecodeWavesPerCU), steps);
         int64_t quota = W > 0 ? (total + W - 1) / W : 0;
         quota = (quota + kDecodeStep - 1) / kDecodeStep * kDecodeStep;
         // a piece touches at most 64 pages (one block-table entry per lane)
@@ -650,6 +706,13 @@ fia_status fia_get_workspace_size(const fia_tensor* query, const fia_tensor* key
         d.n_waves = (int32_t)(wave_first.size() - 1);
         d.n_pieces = (int32_t)pieces.size();
         d.scale_log2 = (float)scale_log2;
+        d.mla_nw = (int32_t)nw;
+        if (mla) {
+            d.qr = qr_data;
+            d.kr = prm->key_rope->data;
+            d.qr_sB = qr_sB; d.qr_sH = qr_sH; d.qr_sS = qr_sS;
+            d.pr_blk = prm->block_size * 64;
+        }
         p->n_waves = d.n_waves;
         p->n_pieces = d.n_pieces;
         p->off_batch = 0;

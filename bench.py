@@ -2,7 +2,7 @@
 """Benchmark of the MI355X fused inference attention forward.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2]
-                    [--secondary c1,c3,c4,c5,paged_prefill,mtp_decode,int8_decode,fp8_bsa]
+                    [--secondary c1,c3,c4,c5,paged_prefill,mtp_decode,int8_decode,fp8_bsa,mla_decode]
 
 One step is one fia_run (phase 2) of the headline workload: the GQA causal
 prefill, bf16, B=4, Q_N=32, KV_N=8, max S=4096, D=128, BSND, per-batch
@@ -101,6 +101,11 @@ def decode_bytes(case) -> int:
                 kv += t.numel() * t.element_size() if mode == 0 else int(L.sum()) * 4
     rows = case.B * case.QN * case.Sq          # query rows (decode: S = 1)
     qo = rows * (case.Dqk + case.Dv) * 2
+    if getattr(case, "rope", None):
+        # MLA: the key_rope pool rows read and the query_rope rows
+        dr = case.rope["key_rope"].shape[-1]
+        kv += int(L.sum()) * dr * 2
+        qo += rows * dr * 2
     lse = rows * 4 if case.return_lse else 0
     bt = 4 * int(((L + case.block_size - 1) // case.block_size).sum()) if case.block_table is not None else 0
     return kv + qo + lse + bt
@@ -166,11 +171,15 @@ def measure(name, steps, warmup):
     wall, ev = time_plan(plan, steps, warmup)
     res = {"workload": case.name, "steps": steps, "ms_per_step": wall * 1e3,
            "kernel_ms": ev * 1e3, "phase1_us": round(phase1_us, 1)}
-    if name in ("c3", "mtp_decode", "int8_decode"):
+    if name in ("c3", "mtp_decode", "int8_decode", "mla_decode"):
         nbytes = decode_bytes(case)
         res.update(value=nbytes / wall / 1e9, unit="GB/s", algorithmic_bytes=nbytes,
                    roofline={"bound": "hbm", "achieved": nbytes / ev / 1e9, "peak": PEAK_HBM_GBS,
                              "unit": "GB/s", "frac": nbytes / ev / 1e9 / PEAK_HBM_GBS})
+        if name == "mla_decode":
+            # MFMA work beside the bytes: 2 (576 + 512) flops per (query row, kv token)
+            flops = 2 * (case.Dqk + case.rope["query_rope"].shape[-1] + case.Dv) * case.QN * int(case.lkv.sum())
+            res.update(algorithmic_flops=flops, mfma_tflops=flops / ev / 1e12)
     else:
         if name in ("c5", "fp8_bsa"):
             pairs = allowed_pairs_bsa(case)
@@ -233,7 +242,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="c2")
-    ap.add_argument("--secondary", default="c1,c3,c4,c5,paged_prefill,mtp_decode,int8_decode,fp8_bsa",
+    ap.add_argument("--secondary", default="c1,c3,c4,c5,paged_prefill,mtp_decode,int8_decode,fp8_bsa,mla_decode",
                     help="comma list of other workloads to time ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",

@@ -142,6 +142,21 @@ typedef struct fia_params {
     const fia_tensor* dequant_offset_value;
     int64_t key_quant_mode;
     int64_t value_quant_mode;
+    /* MLA (query_rope / key_rope parameters of the v2 page and their
+     * constraints for a query D of 512): both given or both NULL
+     * (FIA_ERR_PARAM for one alone).  The score of query row i and key j
+     * becomes scale * (q_i . k_j + q_rope_i . k_rope_j); value and output
+     * keep D = 512.  Provided here: query D 512 and rope D 64, fp16 or bf16
+     * (the rope inputs take the query's dtype), layouts BSH / BSND / BNSD
+     * (query_rope the query's layout with D = 64), query S 1..16 (S > 1:
+     * sparse_mode 3, S == 1: sparse_mode 0 without a mask), Q_N in
+     * {1, 2, 4, ..., 128}, KV_N 1, a paged cache (block_table required) with
+     * block_size 16 or 128 and key_rope a pool of the key's layout with D 64.
+     * value is its own pool of the key's shape (it may be the key itself).
+     * softmax_lse is computed as for any other call.  Anything else with rope
+     * inputs returns FIA_ERR_UNSUPPORTED. */
+    const fia_tensor* query_rope;
+    const fia_tensor* key_rope;
 } fia_params;
 
 /* Fill `p` with the defaults listed above (layout "BSH", scale 1.0,

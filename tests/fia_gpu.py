@@ -22,7 +22,7 @@ def to_dev(case, device="cuda"):
         t = getattr(case, name, None)
         if t is not None and t.device.type != "cuda":
             setattr(case, name, t.to(device))
-    for extra in ("quant", "fp8"):
+    for extra in ("quant", "fp8", "rope"):
         d = getattr(case, extra, None)
         if d:
             for key, t in d.items():
@@ -47,6 +47,8 @@ def fia_plan(case, **over):
         kw["actual_seq_kvlen"] = kl
     if getattr(case, "quant", None):
         kw.update(case.quant)
+    if getattr(case, "rope", None):
+        kw.update(case.rope)
     kw.update(over)
     return fia.FiaPlan(case.q, case.k, case.v, **kw)
 

@@ -413,3 +413,56 @@ def test_bsa_validation():
     q2 = torch.zeros(1, 4, 300, 96, dtype=torch.bfloat16)
     k2 = torch.zeros(1, 2, 260, 96, dtype=torch.bfloat16)
     assert _bsa_phase1(q2, k2, k2, m, **p_shape)[0] == _abi.FIA_ERR_UNSUPPORTED
+
+
+def test_mla_validation():
+    # MLA (query_rope / key_rope): query D 512 + rope 64, one kv head, paged
+    # pool with block_size 16 or 128, query S <= 16, Q_N a power of two <= 128
+    B, QN, bs, D = 2, 16, 128, 512
+    pool = torch.zeros(4, bs, D, dtype=torch.bfloat16)
+    kr = torch.zeros(4, bs, 64, dtype=torch.bfloat16)
+    bt = torch.zeros(B, 2, dtype=torch.int32)
+
+    def code(S=1, qn=QN, q=None, qr=None, k=pool, krope=kr, block_size=bs, mode=0, layout="BNSD",
+             table=bt, mask=None, kvn=1, give=(True, True)):
+        if q is None:
+            q = torch.zeros(B, qn, S, D, dtype=torch.bfloat16)
+        if qr is None:
+            qr = torch.zeros(*q.shape[:-1], 64, dtype=q.dtype)
+        p = _params(num_heads=qn, num_key_value_heads=kvn, input_layout=layout,
+                    block_size=block_size, sparse_mode=mode)
+        keep = [qr, krope]
+        dq, dk = fia.describe(qr), fia.describe(krope)
+        keep += [dq, dk]
+        if give[0]:
+            p.query_rope = ctypes.pointer(dq)
+        if give[1]:
+            p.key_rope = ctypes.pointer(dk)
+        lk = np.array([200, 7], dtype=np.int64)
+        keep.append(lk)
+        p.actual_seq_kvlen, p.n_actual_seq_kvlen = lk.ctypes.data, 2
+        out = torch.zeros(*q.shape[:-1], D, dtype=q.dtype)
+        return _phase1(q, k, k, p, out=out, bt=table, mask=mask)[0]
+
+    assert code() == _abi.FIA_OK
+    assert code(qn=128) == _abi.FIA_OK
+    tmpl = torch.triu(torch.ones(2048, 2048, dtype=torch.uint8), diagonal=1)
+    assert code(S=4, mode=3, mask=tmpl) == _abi.FIA_OK
+    assert code(k=torch.zeros(4, 1, bs, D, dtype=torch.bfloat16),
+                krope=torch.zeros(4, 1, bs, 64, dtype=torch.bfloat16)) == _abi.FIA_OK
+    assert code(give=(True, False)) == _abi.FIA_ERR_PARAM           # both or neither
+    assert code(give=(False, True)) == _abi.FIA_ERR_PARAM
+    assert code(qr=torch.zeros(B, QN, 1, 64, dtype=torch.float16)) == _abi.FIA_ERR_DTYPE
+    assert code(qr=torch.zeros(B, QN, 1, 32, dtype=torch.bfloat16)) == _abi.FIA_ERR_SHAPE
+    assert code(krope=torch.zeros(4, bs, 32, dtype=torch.bfloat16)) == _abi.FIA_ERR_SHAPE
+    assert code(krope=torch.zeros(3, bs, 64, dtype=torch.bfloat16)) == _abi.FIA_ERR_SHAPE
+    assert code(block_size=64, k=torch.zeros(8, 64, D, dtype=torch.bfloat16),
+                krope=torch.zeros(8, 64, 64, dtype=torch.bfloat16)) == _abi.FIA_ERR_PARAM
+    assert code(table=None, block_size=0, k=torch.zeros(B, 1, 200, D, dtype=torch.bfloat16),
+                krope=torch.zeros(B, 1, 200, 64, dtype=torch.bfloat16)) == _abi.FIA_ERR_UNSUPPORTED
+    assert code(qn=12) == _abi.FIA_ERR_UNSUPPORTED                  # Q_N a power of two
+    assert code(qn=256) == _abi.FIA_ERR_PARAM                        # above the pages' 128
+    assert code(S=17, mode=3) == _abi.FIA_ERR_UNSUPPORTED
+    assert code(S=2, mode=0) == _abi.FIA_ERR_UNSUPPORTED            # S > 1: sparse_mode 3
+    assert code(mask=torch.zeros(B, 256, dtype=torch.uint8)) == _abi.FIA_ERR_UNSUPPORTED
+    assert code(kvn=2, k=torch.zeros(4, bs, 2 * D, dtype=torch.bfloat16)) == _abi.FIA_ERR_UNSUPPORTED
