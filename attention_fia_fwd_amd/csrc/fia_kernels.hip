@@ -199,6 +199,17 @@ __device__ __forceinline__ void dma16_burst(i32x4 rs, uint32_t lds_base, const u
                      : "s"(m0v), "v"(voff[0]), "v"(voff[1]), "v"(voff[2]), "v"(voff[3]), "s"(rs) : "memory");
 }
 
+// 4 bytes per lane from a buffer resource straight into LDS: lane i writes
+// lds_wave + 4 i (the same ordering contract as dma16).
+__device__ __forceinline__ void dma4(i32x4 rs, uint32_t lds_wave, uint32_t voff)
+{
+    const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_wave);
+    uint32_t keep;
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
+                 "buffer_load_dword %2, %3, 0 offen lds\n\ts_mov_b32 m0, %0"
+                 : "=&s"(keep) : "s"(m0v), "v"(voff), "s"(rs) : "memory");
+}
+
 // The same resource moved `d` bytes further (fewer valid bytes, never < 0);
 // offsets past the valid range still read as zero.
 __device__ __forceinline__ i32x4 rsrc_advance(i32x4 r, uint32_t d)
@@ -1654,34 +1665,43 @@ __global__ __launch_bounds__(64) void decode_split_i8(DecodeArgs a)
 // MLA decode (query D 512 + rope 64, one kv head, paged K / V / K-rope pools).
 //
 // The Q_N x S (head, token) rows of a batch share every K/V byte, so a
-// workgroup of NW waves serves Gc <= 16 NW rows, wave w the 16 columns
-// 16 w .. 16 w + 15 of v_mfma_f32_16x16x32 (the decode kernel's layout):
+// workgroup of NW (2..8) waves serves Gc <= 16 NW rows, wave w the 16
+// columns 16 w .. 16 w + 15 of v_mfma_f32_16x16x32 (the decode kernel's
+// layout):
 //   S^T (32 tokens x 16 rows) = [K | K_rope] [Q | Q_rope]^T, 18 k-steps,
 //       Q and Q_rope in registers (B operand), K rows read from LDS;
 //   O^T (512 x 16) += V^T P^T, 32 tiles, V through transposed LDS reads.
-// Per 32-token step the workgroup moves K (32 x 512), K_rope (32 x 64) and
-// V (32 x 512) straight into LDS (two stages, 2 x 68 KB): each K / V row is
-// one 1 KB direct-to-LDS load, spread over the waves.  One barrier per step:
-// wait for the own loads of step st, barrier (all of step st has landed and
-// every wave is done with step st - 1), issue step st + 1 into the other
-// stage, compute step st.  16-byte chunks are XOR-swizzled per row so the
-// 16 rows a quarter-wave reads hit distinct banks.
+// Per 32-token step the workgroup moves K (32 x 512) and K_rope (32 x 64)
+// into one of two K slots and V (32 x 512) into one of two V slots, straight
+// from the pools into LDS (K / V rows as 1 KB loads, K_rope rows as 4-byte
+// loads so every wave issues the same number of loads).  The rings are
+// decoupled so K runs two steps ahead: at the top of step st (after its K
+// landed and every wave left P V of step st - 1) V of step st + 1 goes out;
+// after S of step st (its V landed, every wave done with its K slot) K of
+// step st + 2 goes out into that slot.  16-byte chunks are XOR-swizzled per
+// row so the 16 rows a quarter-wave reads hit distinct banks.
 // ---------------------------------------------------------------------------
 constexpr int kMlaD = 512, kMlaDR = 64;
-constexpr int kMlaStageHalves = kDecodeStep * (2 * kMlaD + kMlaDR);
+constexpr int kMlaKSlot = kDecodeStep * (kMlaD + kMlaDR);   // halves
+constexpr int kMlaVSlot = kDecodeStep * kMlaD;
+constexpr int kMlaLdsBytes = 2 * 2 * (kMlaKSlot + kMlaVSlot);
 
 template <int DT, int NW>
 __global__ __launch_bounds__(NW * 64, 1) void mla_decode(DecodeArgs a)
 {
+    static_assert(NW == 2 || NW == 4 || NW == 8, "2, 4 or 8 waves");
     constexpr int D = kMlaD, DR = kMlaDR;
     constexpr int ST = kDecodeStep;                 // 32 tokens per step
     constexpr int NKM = D / 32, NKR = DR / 32;      // k-steps: latent, rope
     constexpr int NO = D / 16;                      // O^T tiles
-    constexpr int KR_OFF = ST * D;                  // stage layout (halves): K | K_rope | V
-    constexpr int V_OFF = ST * (D + DR);
+    constexpr int NLK = ST / NW + 16 / NW;          // loads per wave: K + K_rope of a step
+    constexpr int NLV = ST / NW;                    // V of a step
     using O = Ops<DT>;
     extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
     const uint32_t smem_lds = (uint32_t)(uintptr_t)(lds_void*)smem;
+    // byte addresses: K slots (K rows, then K_rope rows), then V slots
+    auto kslot = [&](int st) { return smem_lds + 2u * (uint32_t)(kMlaKSlot * (st & 1)); };
+    auto vslot = [&](int st) { return smem_lds + 2u * (uint32_t)(2 * kMlaKSlot + kMlaVSlot * (st & 1)); };
 
     const int lane = threadIdx.x & 63;
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1733,41 +1753,61 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_decode(DecodeArgs a)
         const uint16_t* kbase = (const uint16_t*)a.k;
         const uint16_t* vbase = (const uint16_t*)a.v;
         const uint16_t* rbase = (const uint16_t*)a.kr;
+        // settle the query and page-table loads: the step loop counts only
+        // its own loads
+        __builtin_amdgcn_s_waitcnt(FIA_VMCNT(0));
 
-        // one step's loads: rows [tt0, tt0 + 32) as two 16-row sub-tiles
-        // (page pg0 offset off0, page pg1 offset off1); rows past t1 read 0
-        auto issue = [&](int tt0, int pg0, int off0, int pg1, int off1, uint32_t stage) {
-            // the per-lane offsets are recomputed at every step (a few VALU
-            // ops) instead of being held in registers across the loop
+        auto advance16 = [&](int& p, int& o) {
+            o += 16;
+            if (o >= bs) { o -= bs; ++p; }
+        };
+        // resource over rows [off, off + nvalid) of page pg of a pool; rows
+        // of the sub-tile starting at token tb past t1 read as zero
+        auto sub_rsrc = [&](const uint16_t* base, int64_t blk, int rowlen, int pg, int off, int tb) {
+            const int nvalid = max(0, min(16, t1 - tb));
+            const int64_t page = nvalid > 0 ? (int64_t)__builtin_amdgcn_readlane(my_page, pg - pg_first) : 0;
+            return make_rsrc(base + page * blk + (int64_t)off * rowlen, (int64_t)nvalid * rowlen * 2);
+        };
+        // K and K_rope of the step starting at token tt0 (first sub-tile at
+        // page pg, offset off) into K slot `dst`
+        auto issue_k = [&](int tt0, int pg, int off, uint32_t dst) {
             int ln = lane;
-            asm volatile("" : "+v"(ln));
-            i32x4 rk[2], rv[2], rr[2];
-#pragma unroll
-            for (int cc = 0; cc < 2; ++cc) {
-                const int pg = cc ? pg1 : pg0, off = cc ? off1 : off0;
-                const int nvalid = max(0, min(16, t1 - (tt0 + 16 * cc)));
-                const int64_t page =
-                    nvalid > 0 ? (int64_t)__builtin_amdgcn_readlane(my_page, pg - pg_first) : 0;
-                rk[cc] = make_rsrc(kbase + page * a.p_blk + (int64_t)off * D, (int64_t)nvalid * D * 2);
-                rv[cc] = make_rsrc(vbase + page * a.p_blk + (int64_t)off * D, (int64_t)nvalid * D * 2);
-                rr[cc] = make_rsrc(rbase + page * a.pr_blk + (int64_t)off * DR, (int64_t)nvalid * DR * 2);
-            }
+            asm volatile("" : "+v"(ln));              // per-step offsets, not held in registers
+            int pg1 = pg, off1 = off;
+            advance16(pg1, off1);
+            const i32x4 rk0 = sub_rsrc(kbase, a.p_blk, D, pg, off, tt0);
+            const i32x4 rk1 = sub_rsrc(kbase, a.p_blk, D, pg1, off1, tt0 + 16);
+            const i32x4 rr0 = sub_rsrc(rbase, a.pr_blk, DR, pg, off, tt0);
+            const i32x4 rr1 = sub_rsrc(rbase, a.pr_blk, DR, pg1, off1, tt0 + 16);
 #pragma unroll
             for (int i = 0; i < ST / NW; ++i) {
-                const int r = NW * i + wid;          // row of the step
-                const i32x4 k_rs = r < 16 ? rk[0] : rk[1];
-                const i32x4 v_rs = r < 16 ? rv[0] : rv[1];
-                const uint32_t row = (uint32_t)((r & 15) * D);
-                dma16(k_rs, stage + 2u * (uint32_t)(r * D), (row + 8u * (uint32_t)(ln ^ (r & 15))) * 2u);
-                dma16(v_rs, stage + 2u * (uint32_t)(V_OFF + r * D),
-                      (row + 8u * (uint32_t)(ln ^ (2 * (r & 7)))) * 2u);
+                const int r = NW * i + wid;
+                dma16(r < 16 ? rk0 : rk1, dst + 2u * (uint32_t)(r * D),
+                      ((uint32_t)((r & 15) * D) + 8u * (uint32_t)(ln ^ (r & 15))) * 2u);
             }
-            // K_rope: 8 rows of 128 bytes per load, four loads per step
-            for (int u = wid; u < 4; u += NW) {
-                const int r = 8 * u + (ln >> 3);
-                const uint32_t chunk = (uint32_t)((ln & 7) ^ ((r >> 1) & 7));
-                dma16(u < 2 ? rr[0] : rr[1], stage + 2u * (uint32_t)(KR_OFF + 8 * u * DR),
-                      ((uint32_t)((r & 15) * DR) + 8u * chunk) * 2u);
+            // K_rope: 16 loads of 4 bytes per lane, two 128-byte rows each
+#pragma unroll
+            for (int i = 0; i < 16 / NW; ++i) {
+                const int u = NW * i + wid;
+                const int r = 2 * u + (ln >> 5);
+                const int pch = (ln & 31) >> 2;      // 16-byte position in the row
+                const uint32_t e = (uint32_t)(8 * (pch ^ ((r >> 1) & 7)) + 2 * (ln & 3));
+                dma4(u < 8 ? rr0 : rr1, dst + 2u * (uint32_t)(ST * D) + 256u * (uint32_t)u,
+                     ((uint32_t)((r & 15) * DR) + e) * 2u);
+            }
+        };
+        auto issue_v = [&](int tt0, int pg, int off, uint32_t dst) {
+            int ln = lane;
+            asm volatile("" : "+v"(ln));
+            int pg1 = pg, off1 = off;
+            advance16(pg1, off1);
+            const i32x4 rv0 = sub_rsrc(vbase, a.p_blk, D, pg, off, tt0);
+            const i32x4 rv1 = sub_rsrc(vbase, a.p_blk, D, pg1, off1, tt0 + 16);
+#pragma unroll
+            for (int i = 0; i < ST / NW; ++i) {
+                const int r = NW * i + wid;
+                dma16(r < 16 ? rv0 : rv1, dst + 2u * (uint32_t)(r * D),
+                      ((uint32_t)((r & 15) * D) + 8u * (uint32_t)(ln ^ (2 * (r & 7)))) * 2u);
             }
         };
 
@@ -1780,7 +1820,7 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_decode(DecodeArgs a)
 #pragma unroll
         for (int si = 0; si < 4; ++si) koff[si] = n * D + 8 * (4 * (si ^ (n >> 2)) + (qd ^ (n & 3)));
 #pragma unroll
-        for (int sr = 0; sr < NKR; ++sr) roff[sr] = n * DR + 8 * ((4 * sr + qd) ^ ((n >> 1) & 7));
+        for (int sr = 0; sr < NKR; ++sr) roff[sr] = ST * D + n * DR + 8 * ((4 * sr + qd) ^ ((n >> 1) & 7));
         {
             const int vi = lane & 15;
             const int trow = 4 * qd + (vi >> 2);
@@ -1796,97 +1836,108 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_decode(DecodeArgs a)
         const float lazy_raw = kLazy / c;
 
         const int nsteps = (t1 - t0 + ST - 1) / ST;
-        int pg = t0 / bs, off = t0 % bs;
-        auto advance16 = [&](int& p, int& o) {
-            o += 16;
-            if (o >= bs) { o -= bs; ++p; }
-        };
+        // next K step to issue and next V step to issue: first sub-tile's page / offset
+        int kpg = t0 / bs, koffs = t0 % bs;
+        int vpg = kpg, voffp = koffs;
+        auto skip32 = [&](int& p, int& o) { advance16(p, o); advance16(p, o); };
         if (nsteps > 0) {
-            int pg1 = pg, off1 = off;
-            advance16(pg1, off1);
-            issue(t0, pg, off, pg1, off1, smem_lds);
-            pg = pg1; off = off1;
-            advance16(pg, off);
+            issue_k(t0, kpg, koffs, kslot(0));
+            skip32(kpg, koffs);
+            issue_v(t0, vpg, voffp, vslot(0));
+            skip32(vpg, voffp);
+            if (nsteps > 1) {
+                issue_k(t0 + ST, kpg, koffs, kslot(1));
+                skip32(kpg, koffs);
+            }
         }
         for (int st = 0; st < nsteps; ++st) {
             const int tt0 = t0 + ST * st;
-            __builtin_amdgcn_s_waitcnt(FIA_VMCNT(0));
+            const bool more = st + 1 < nsteps;
+            // K of step st landed (V of st and K of st + 1 may still fly)
+            if (more) __builtin_amdgcn_s_waitcnt(FIA_VMCNT(NLV + NLK));
+            else __builtin_amdgcn_s_waitcnt(FIA_VMCNT(NLV));
             __syncthreads();
-            if (st + 1 < nsteps) {
-                int pg1 = pg, off1 = off;
-                advance16(pg1, off1);
-                issue(tt0 + ST, pg, off, pg1, off1, smem_lds + 2u * kMlaStageHalves * (uint32_t)((st + 1) & 1));
-                pg = pg1; off = off1;
-                advance16(pg, off);
+            if (more) {
+                issue_v(tt0 + ST, vpg, voffp, vslot(st + 1));
+                skip32(vpg, voffp);
             }
-            if (nh == 0) continue;
-            const uint16_t* kb = smem + kMlaStageHalves * (st & 1);
-            const uint16_t* krb = kb + KR_OFF;
-            const uint16_t* vb = kb + V_OFF;
-
-            f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+            uint4 pb = make_uint4(0, 0, 0, 0);
+            if (nh > 0) {
+                const uint16_t* kb = smem + kMlaKSlot * (st & 1);
+                f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int s = 0; s < NKM; ++s) {
-                const uint16_t* kp = kb + koff[s & 3] + 128 * (s >> 2);
-                const uint4 a0 = *(const uint4*)(kp);
-                const uint4 a1 = *(const uint4*)(kp + 16 * D);
-                s0 = O::mma16(a0, qf[s], s0);
-                s1 = O::mma16(a1, qf[s], s1);
-            }
+                for (int s = 0; s < NKM; ++s) {
+                    const uint16_t* kp = kb + koff[s & 3] + 128 * (s >> 2);
+                    const uint4 a0 = *(const uint4*)(kp);
+                    const uint4 a1 = *(const uint4*)(kp + 16 * D);
+                    s0 = O::mma16(a0, qf[s], s0);
+                    s1 = O::mma16(a1, qf[s], s1);
+                }
 #pragma unroll
-            for (int s = 0; s < NKR; ++s) {
-                const uint4 a0 = *(const uint4*)(krb + roff[s]);
-                const uint4 a1 = *(const uint4*)(krb + roff[s] + 16 * DR);
-                s0 = O::mma16(a0, qf[NKM + s], s0);
-                s1 = O::mma16(a1, qf[NKM + s], s1);
-            }
-            float x[8];
+                for (int s = 0; s < NKR; ++s) {
+                    const uint4 a0 = *(const uint4*)(kb + roff[s]);
+                    const uint4 a1 = *(const uint4*)(kb + roff[s] + 16 * DR);
+                    s0 = O::mma16(a0, qf[NKM + s], s0);
+                    s1 = O::mma16(a1, qf[NKM + s], s1);
+                }
+                float x[8];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                x[i] = s0[i];
-                x[4 + i] = s1[i];
-            }
-            if (tt0 + ST > t1 || tt0 + ST - 1 > jmin) {
+                for (int i = 0; i < 4; ++i) {
+                    x[i] = s0[i];
+                    x[4 + i] = s1[i];
+                }
+                if (tt0 + ST > t1 || tt0 + ST - 1 > jmin) {
+#pragma unroll
+                    for (int r = 0; r < 8; ++r) {
+                        const int tk = tt0 + 16 * (r >> 2) + 4 * qd + (r & 3);
+                        if (tk >= t1 || tk > jmax) x[r] = -INFINITY;
+                    }
+                }
+                float mt = x[0];
+#pragma unroll
+                for (int r = 1; r < 8; ++r) mt = fmaxf(mt, x[r]);
+                mt = quad_max(mt);
+                const float mn = fmaxf(m, mt);
+                const bool grow = (m == -INFINITY) ? (mn > -INFINITY) : (mn > m + lazy_raw);
+                if (__ballot(grow)) {
+                    float alpha = 1.f;
+                    if (m == -INFINITY) alpha = 0.f;
+                    else if (mn != -INFINITY) alpha = fast_exp2((m - mn) * c);
+                    m = mn;
+                    l *= alpha;
+#pragma unroll
+                    for (int o = 0; o < NO; ++o) acc[o] *= alpha;
+                }
+                const float mc = (m == -INFINITY) ? 0.f : m * c;
+                float ps = 0.f;
 #pragma unroll
                 for (int r = 0; r < 8; ++r) {
-                    const int tk = tt0 + 16 * (r >> 2) + 4 * qd + (r & 3);
-                    if (tk >= t1 || tk > jmax) x[r] = -INFINITY;
+                    x[r] = fast_exp2(__builtin_fmaf(x[r], c, -mc));
+                    ps += x[r];
                 }
+                l += ps;
+                pb.x = O::pack2(x[0], x[1]);
+                pb.y = O::pack2(x[2], x[3]);
+                pb.z = O::pack2(x[4], x[5]);
+                pb.w = O::pack2(x[6], x[7]);
             }
-            float mt = x[0];
-#pragma unroll
-            for (int r = 1; r < 8; ++r) mt = fmaxf(mt, x[r]);
-            mt = quad_max(mt);
-            const float mn = fmaxf(m, mt);
-            const bool grow = (m == -INFINITY) ? (mn > -INFINITY) : (mn > m + lazy_raw);
-            if (__ballot(grow)) {
-                float alpha = 1.f;
-                if (m == -INFINITY) alpha = 0.f;
-                else if (mn != -INFINITY) alpha = fast_exp2((m - mn) * c);
-                m = mn;
-                l *= alpha;
-#pragma unroll
-                for (int o = 0; o < NO; ++o) acc[o] *= alpha;
+            // V of step st landed (K of st + 1 and V of st + 1 may still fly)
+            if (more) __builtin_amdgcn_s_waitcnt(FIA_VMCNT(NLK + NLV));
+            else __builtin_amdgcn_s_waitcnt(FIA_VMCNT(0));
+            __syncthreads();
+            if (st + 2 < nsteps) {
+                issue_k(tt0 + 2 * ST, kpg, koffs, kslot(st));
+                skip32(kpg, koffs);
             }
-            const float mc = (m == -INFINITY) ? 0.f : m * c;
-            float ps = 0.f;
+            if (nh > 0) {
+                const uint16_t* vb = smem + 2 * kMlaKSlot + kMlaVSlot * (st & 1);
 #pragma unroll
-            for (int r = 0; r < 8; ++r) {
-                x[r] = fast_exp2(__builtin_fmaf(x[r], c, -mc));
-                ps += x[r];
-            }
-            l += ps;
-            uint4 pb;
-            pb.x = O::pack2(x[0], x[1]);
-            pb.y = O::pack2(x[2], x[3]);
-            pb.z = O::pack2(x[4], x[5]);
-            pb.w = O::pack2(x[6], x[7]);
-#pragma unroll
-            for (int o = 0; o < NO; ++o) {
-                const uint16_t* vp = vb + voffs[o & 7] + 128 * (o >> 3);
-                const uint2 lo = lds_read_tr16(vp);
-                const uint2 hi = lds_read_tr16(vp + 16 * D);
-                acc[o] = O::mma16(make_uint4(lo.x, lo.y, hi.x, hi.y), pb, acc[o]);
+                for (int o = 0; o < NO; ++o) {
+                    const uint16_t* vp = vb + voffs[o & 7] + 128 * (o >> 3);
+                    const uint2 lo = lds_read_tr16(vp);
+                    const uint2 hi = lds_read_tr16(vp + 16 * D);
+                    acc[o] = O::mma16(make_uint4(lo.x, lo.y, hi.x, hi.y), pb, acc[o]);
+                }
             }
         }
 
@@ -1904,7 +1955,7 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_decode(DecodeArgs a)
                 a.part_lse[(int64_t)item * a.Gc + 16 * wid + n] =
                     lt > 0.f ? (m * c + __log2f(lt)) * kLn2 : -INFINITY;
         }
-        __syncthreads();     // the stages are reused by the next piece
+        __syncthreads();     // the slots are reused by the next piece
     }
 }
 
@@ -2096,7 +2147,7 @@ int launch_bsa(const fia_plan& p, const AttnArgs& a, void* stream)
 template <int DT, int NW>
 int launch_mla_nw(const fia_plan& p, const DecodeArgs& a, hipStream_t stream)
 {
-    const size_t lds = 2u * kMlaStageHalves * sizeof(uint16_t);    // 2 x 68 KB
+    const size_t lds = kMlaLdsBytes;    // 2 K slots of 36 KB, 2 V slots of 32 KB
     static bool configured = false;
     raise_lds_limit(mla_decode<DT, NW>, lds, configured);
     if (p.n_waves > 0)
@@ -2111,7 +2162,6 @@ template <int DT>
 int launch_mla(const fia_plan& p, const DecodeArgs& a, hipStream_t s)
 {
     switch (a.mla_nw) {
-    case 1: return launch_mla_nw<DT, 1>(p, a, s);
     case 2: return launch_mla_nw<DT, 2>(p, a, s);
     case 4: return launch_mla_nw<DT, 4>(p, a, s);
     case 8: return launch_mla_nw<DT, 8>(p, a, s);

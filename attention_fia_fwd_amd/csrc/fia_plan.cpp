@@ -647,7 +647,7 @@ fia_status fia_get_workspace_size(const fia_tensor* query, const fia_tensor* key
         int64_t nw = 0;
         if (mla) {
             const int64_t need = (std::min<int64_t>(R, 16 * kMlaMaxWaves) + 15) / 16;
-            nw = 1;
+            nw = 2;                    // the MLA kernel runs 2, 4 or 8 waves
             while (nw < need) nw *= 2;
         }
         const int64_t rows_per_chunk = mla ? 16 * nw : kDecodeHeads;
