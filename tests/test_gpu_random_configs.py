@@ -154,3 +154,20 @@ def test_random_block_sparse(seed):
     out, lse = run(p)
     compare(case, out, lse, *ref)
     p.close()
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_random_mla_decode(seed):
+    rng = np.random.default_rng(1100 + seed)
+    S = int(rng.choice([1, 1, 2, 3, 8, 16]))
+    QN = int(rng.choice([1, 2, 4, 8, 16, 32, 64, 128]))
+    B = int(rng.integers(1, 4))
+    bs = int(rng.choice([16, 128]))
+    lkv = rng.integers(0, 2500, size=B)
+    lkv[rng.integers(B)] = int(rng.integers(1, 40))
+    lq = rng.integers(1, S + 1, size=B) if S > 1 and rng.random() < 0.5 else None
+    case = W.make_mla_decode(f"rand_mla_{seed}", layout=str(rng.choice(["BSND", "BNSD", "BSH"])),
+                             dtype=torch.bfloat16 if rng.random() < 0.6 else torch.float16, B=B, QN=QN,
+                             Sq=S, lq=lq, lkv=lkv, block_size=bs, pool_layout=int(rng.integers(2)),
+                             seed=1110 + seed, extra_blocks=1, nan_pool=True)
+    _check_fia(case)
