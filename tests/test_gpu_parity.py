@@ -363,6 +363,25 @@ def test_workload_c1_full():
     check_fia(W.c1_dense_causal_fp16())
 
 
+def test_workload_c1_mode1_explicit_causal_mask():
+    # the smallest workload with sparse_mode 1 and an explicit 128 x 128
+    # causal mask (nonzero above the diagonal): the oracle's result, and the
+    # mode-3 run's result
+    case = W.c1_dense_causal_fp16()
+    case.sparse_mode = 1
+    case.atten_mask = torch.triu(torch.ones(128, 128, dtype=torch.uint8), diagonal=1)
+    check_fia(case)
+    p = fia_plan(case)
+    out1, lse1 = run(p)
+    p.close()
+    c3 = to_dev(W.c1_dense_causal_fp16())
+    p = fia_plan(c3)
+    out3, lse3 = run(p)
+    p.close()
+    assert (out1.float() - out3.float()).abs().max().item() <= 1e-3
+    assert (lse1 - lse3).abs().max().item() <= 1e-5
+
+
 def _full_sampled(case, n_rows, seed):
     say(f"[full] {case.name}")
     rows = sample_rows(case, n_rows, seed=seed, decode=case.decode)
