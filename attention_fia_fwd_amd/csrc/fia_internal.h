@@ -164,6 +164,7 @@ struct DecodeArgs {
     int64_t qr_sB, qr_sH, qr_sS;
     int64_t pr_blk;
     int32_t mla_nw;
+    int32_t v_is_k;                // value is the key tensor itself (V read from the K tile)
 };
 
 }  // namespace fia

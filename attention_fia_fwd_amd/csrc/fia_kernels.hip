@@ -1680,13 +1680,17 @@ __global__ __launch_bounds__(64) void decode_split_i8(DecodeArgs a)
 // after S of step st (its V landed, every wave done with its K slot) K of
 // step st + 2 goes out into that slot.  16-byte chunks are XOR-swizzled per
 // row so the 16 rows a quarter-wave reads hit distinct banks.
+// VK (value is the key tensor itself): V^T is read from the K slot, nothing
+// else is loaded, and three K slots keep two steps in flight with one
+// barrier per step.
 // ---------------------------------------------------------------------------
 constexpr int kMlaD = 512, kMlaDR = 64;
 constexpr int kMlaKSlot = kDecodeStep * (kMlaD + kMlaDR);   // halves
 constexpr int kMlaVSlot = kDecodeStep * kMlaD;
 constexpr int kMlaLdsBytes = 2 * 2 * (kMlaKSlot + kMlaVSlot);
+constexpr int kMlaLdsBytesVK = 3 * 2 * kMlaKSlot;
 
-template <int DT, int NW>
+template <int DT, int NW, bool VK>
 __global__ __launch_bounds__(NW * 64, 1) void mla_decode(DecodeArgs a)
 {
     static_assert(NW == 2 || NW == 4 || NW == 8, "2, 4 or 8 waves");
@@ -1696,11 +1700,12 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_decode(DecodeArgs a)
     constexpr int NO = D / 16;                      // O^T tiles
     constexpr int NLK = ST / NW + 16 / NW;          // loads per wave: K + K_rope of a step
     constexpr int NLV = ST / NW;                    // V of a step
+    constexpr int NSLOT = VK ? 3 : 2;               // K slots
     using O = Ops<DT>;
     extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
     const uint32_t smem_lds = (uint32_t)(uintptr_t)(lds_void*)smem;
     // byte addresses: K slots (K rows, then K_rope rows), then V slots
-    auto kslot = [&](int st) { return smem_lds + 2u * (uint32_t)(kMlaKSlot * (st & 1)); };
+    auto kslot = [&](int st) { return smem_lds + 2u * (uint32_t)(kMlaKSlot * (st % NSLOT)); };
     auto vslot = [&](int st) { return smem_lds + 2u * (uint32_t)(2 * kMlaKSlot + kMlaVSlot * (st & 1)); };
 
     const int lane = threadIdx.x & 63;
@@ -1826,7 +1831,9 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_decode(DecodeArgs a)
             const int trow = 4 * qd + (vi >> 2);
             const int tcol_lo = (vi & 3) >> 1, tsub = 4 * (vi & 1);
 #pragma unroll
-            for (int oi = 0; oi < 8; ++oi) voffs[oi] = trow * D + 8 * (2 * (oi ^ (trow & 7)) + tcol_lo) + tsub;
+            for (int oi = 0; oi < 8; ++oi)
+                voffs[oi] = VK ? trow * D + 8 * ((2 * oi + tcol_lo) ^ (trow & 15)) + tsub   // K's swizzle
+                               : trow * D + 8 * (2 * (oi ^ (trow & 7)) + tcol_lo) + tsub;
         }
 
         f32x4 acc[NO];
@@ -1843,8 +1850,10 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_decode(DecodeArgs a)
         if (nsteps > 0) {
             issue_k(t0, kpg, koffs, kslot(0));
             skip32(kpg, koffs);
-            issue_v(t0, vpg, voffp, vslot(0));
-            skip32(vpg, voffp);
+            if constexpr (!VK) {
+                issue_v(t0, vpg, voffp, vslot(0));
+                skip32(vpg, voffp);
+            }
             if (nsteps > 1) {
                 issue_k(t0 + ST, kpg, koffs, kslot(1));
                 skip32(kpg, koffs);
@@ -1853,17 +1862,29 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_decode(DecodeArgs a)
         for (int st = 0; st < nsteps; ++st) {
             const int tt0 = t0 + ST * st;
             const bool more = st + 1 < nsteps;
-            // K of step st landed (V of st and K of st + 1 may still fly)
-            if (more) __builtin_amdgcn_s_waitcnt(FIA_VMCNT(NLV + NLK));
-            else __builtin_amdgcn_s_waitcnt(FIA_VMCNT(NLV));
-            __syncthreads();
-            if (more) {
-                issue_v(tt0 + ST, vpg, voffp, vslot(st + 1));
-                skip32(vpg, voffp);
+            if constexpr (VK) {
+                // K of step st landed (K of st + 1 may still fly); every wave
+                // is done with step st - 1, whose slot takes K of st + 2
+                if (more) __builtin_amdgcn_s_waitcnt(FIA_VMCNT(NLK));
+                else __builtin_amdgcn_s_waitcnt(FIA_VMCNT(0));
+                __syncthreads();
+                if (st + 2 < nsteps) {
+                    issue_k(tt0 + 2 * ST, kpg, koffs, kslot(st + 2));
+                    skip32(kpg, koffs);
+                }
+            } else {
+                // K of step st landed (V of st and K of st + 1 may still fly)
+                if (more) __builtin_amdgcn_s_waitcnt(FIA_VMCNT(NLV + NLK));
+                else __builtin_amdgcn_s_waitcnt(FIA_VMCNT(NLV));
+                __syncthreads();
+                if (more) {
+                    issue_v(tt0 + ST, vpg, voffp, vslot(st + 1));
+                    skip32(vpg, voffp);
+                }
             }
             uint4 pb = make_uint4(0, 0, 0, 0);
             if (nh > 0) {
-                const uint16_t* kb = smem + kMlaKSlot * (st & 1);
+                const uint16_t* kb = smem + kMlaKSlot * (st % NSLOT);
                 f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int s = 0; s < NKM; ++s) {
@@ -1921,16 +1942,18 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_decode(DecodeArgs a)
                 pb.z = O::pack2(x[4], x[5]);
                 pb.w = O::pack2(x[6], x[7]);
             }
-            // V of step st landed (K of st + 1 and V of st + 1 may still fly)
-            if (more) __builtin_amdgcn_s_waitcnt(FIA_VMCNT(NLK + NLV));
-            else __builtin_amdgcn_s_waitcnt(FIA_VMCNT(0));
-            __syncthreads();
-            if (st + 2 < nsteps) {
-                issue_k(tt0 + 2 * ST, kpg, koffs, kslot(st));
-                skip32(kpg, koffs);
+            if constexpr (!VK) {
+                // V of step st landed (K of st + 1 and V of st + 1 may still fly)
+                if (more) __builtin_amdgcn_s_waitcnt(FIA_VMCNT(NLK + NLV));
+                else __builtin_amdgcn_s_waitcnt(FIA_VMCNT(0));
+                __syncthreads();
+                if (st + 2 < nsteps) {
+                    issue_k(tt0 + 2 * ST, kpg, koffs, kslot(st));
+                    skip32(kpg, koffs);
+                }
             }
             if (nh > 0) {
-                const uint16_t* vb = smem + 2 * kMlaKSlot + kMlaVSlot * (st & 1);
+                const uint16_t* vb = VK ? smem + kMlaKSlot * (st % NSLOT) : smem + 2 * kMlaKSlot + kMlaVSlot * (st & 1);
 #pragma unroll
                 for (int o = 0; o < NO; ++o) {
                     const uint16_t* vp = vb + voffs[o & 7] + 128 * (o >> 3);
@@ -2144,14 +2167,15 @@ int launch_bsa(const fia_plan& p, const AttnArgs& a, void* stream)
     return (int)hipErrorInvalidValue;
 }
 
-template <int DT, int NW>
+template <int DT, int NW, bool VK>
 int launch_mla_nw(const fia_plan& p, const DecodeArgs& a, hipStream_t stream)
 {
-    const size_t lds = kMlaLdsBytes;    // 2 K slots of 36 KB, 2 V slots of 32 KB
+    // 2 K slots of 36 KB and 2 V slots of 32 KB, or 3 K slots when V is K
+    const size_t lds = VK ? kMlaLdsBytesVK : kMlaLdsBytes;
     static bool configured = false;
-    raise_lds_limit(mla_decode<DT, NW>, lds, configured);
+    raise_lds_limit(mla_decode<DT, NW, VK>, lds, configured);
     if (p.n_waves > 0)
-        hipLaunchKernelGGL((mla_decode<DT, NW>), dim3((unsigned)p.n_waves), dim3(NW * 64), lds, stream, a);
+        hipLaunchKernelGGL((mla_decode<DT, NW, VK>), dim3((unsigned)p.n_waves), dim3(NW * 64), lds, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return (int)e;
     hipLaunchKernelGGL((decode_combine<DT, kMlaD>), dim3((unsigned)(p.B * p.QN * a.S)), dim3(64), 0, stream, a);
@@ -2161,10 +2185,18 @@ int launch_mla_nw(const fia_plan& p, const DecodeArgs& a, hipStream_t stream)
 template <int DT>
 int launch_mla(const fia_plan& p, const DecodeArgs& a, hipStream_t s)
 {
-    switch (a.mla_nw) {
-    case 2: return launch_mla_nw<DT, 2>(p, a, s);
-    case 4: return launch_mla_nw<DT, 4>(p, a, s);
-    case 8: return launch_mla_nw<DT, 8>(p, a, s);
+    if (a.v_is_k) {
+        switch (a.mla_nw) {
+        case 2: return launch_mla_nw<DT, 2, true>(p, a, s);
+        case 4: return launch_mla_nw<DT, 4, true>(p, a, s);
+        case 8: return launch_mla_nw<DT, 8, true>(p, a, s);
+        }
+    } else {
+        switch (a.mla_nw) {
+        case 2: return launch_mla_nw<DT, 2, false>(p, a, s);
+        case 4: return launch_mla_nw<DT, 4, false>(p, a, s);
+        case 8: return launch_mla_nw<DT, 8, false>(p, a, s);
+        }
     }
     return (int)hipErrorInvalidValue;
 }

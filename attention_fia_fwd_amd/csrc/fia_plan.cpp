@@ -712,6 +712,9 @@ fia_status fia_get_workspace_size(const fia_tensor* query, const fia_tensor* key
             d.kr = prm->key_rope->data;
             d.qr_sB = qr_sB; d.qr_sH = qr_sH; d.qr_sS = qr_sS;
             d.pr_blk = prm->block_size * 64;
+            // value passed as the key tensor itself (same pointer; the shapes
+            // are equal): V is read from the K tiles
+            d.v_is_k = value->data == key->data;
         }
         p->n_waves = d.n_waves;
         p->n_pieces = d.n_pieces;

@@ -2,7 +2,7 @@
 """Benchmark of the MI355X fused inference attention forward.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2]
-                    [--secondary c1,c3,c4,c5,paged_prefill,mtp_decode,int8_decode,fp8_bsa,mla_decode]
+                    [--secondary c1,c3,c4,c5,paged_prefill,mtp_decode,int8_decode,fp8_bsa,mla_decode,mla_shared_kv]
 
 One step is one fia_run (phase 2) of the headline workload: the GQA causal
 prefill, bf16, B=4, Q_N=32, KV_N=8, max S=4096, D=128, BSND, per-batch
@@ -90,7 +90,8 @@ def allowed_pairs_bsa(case) -> int:
 def decode_bytes(case) -> int:
     import numpy as np
     L = case.lkv.astype(np.int64)
-    kv = int(L.sum()) * case.KVN * (case.Dqk + case.Dv) * case.k.element_size()
+    dv = 0 if case.meta.get("v_is_k") else case.Dv     # value read from the key's bytes
+    kv = int(L.sum()) * case.KVN * (case.Dqk + dv) * case.k.element_size()
     if getattr(case, "quant", None):
         # dequant scales/offsets: per channel whole, per token the tokens read
         for key in ("dequant_scale_key", "dequant_offset_key", "dequant_scale_value",
@@ -171,12 +172,12 @@ def measure(name, steps, warmup):
     wall, ev = time_plan(plan, steps, warmup)
     res = {"workload": case.name, "steps": steps, "ms_per_step": wall * 1e3,
            "kernel_ms": ev * 1e3, "phase1_us": round(phase1_us, 1)}
-    if name in ("c3", "mtp_decode", "int8_decode", "mla_decode"):
+    if name in ("c3", "mtp_decode", "int8_decode", "mla_decode", "mla_shared_kv"):
         nbytes = decode_bytes(case)
         res.update(value=nbytes / wall / 1e9, unit="GB/s", algorithmic_bytes=nbytes,
                    roofline={"bound": "hbm", "achieved": nbytes / ev / 1e9, "peak": PEAK_HBM_GBS,
                              "unit": "GB/s", "frac": nbytes / ev / 1e9 / PEAK_HBM_GBS})
-        if name == "mla_decode":
+        if name in ("mla_decode", "mla_shared_kv"):
             # MFMA work beside the bytes: 2 (576 + 512) flops per (query row, kv token)
             flops = 2 * (case.Dqk + case.rope["query_rope"].shape[-1] + case.Dv) * case.QN * int(case.lkv.sum())
             res.update(algorithmic_flops=flops, mfma_tflops=flops / ev / 1e12)
@@ -242,7 +243,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="c2")
-    ap.add_argument("--secondary", default="c1,c3,c4,c5,paged_prefill,mtp_decode,int8_decode,fp8_bsa,mla_decode",
+    ap.add_argument("--secondary", default="c1,c3,c4,c5,paged_prefill,mtp_decode,int8_decode,fp8_bsa,mla_decode,mla_shared_kv",
                     help="comma list of other workloads to time ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",

@@ -152,7 +152,8 @@ typedef struct fia_params {
      * sparse_mode 3, S == 1: sparse_mode 0 without a mask), Q_N in
      * {1, 2, 4, ..., 128}, KV_N 1, a paged cache (block_table required) with
      * block_size 16 or 128 and key_rope a pool of the key's layout with D 64.
-     * value is its own pool of the key's shape (it may be the key itself).
+     * value is its own pool of the key's shape, or the key tensor itself
+     * (same pointer: then the value bytes are not read a second time).
      * softmax_lse is computed as for any other call.  Anything else with rope
      * inputs returns FIA_ERR_UNSUPPORTED. */
     const fia_tensor* query_rope;

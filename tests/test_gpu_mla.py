@@ -82,3 +82,30 @@ def test_mla_full_size_workload_sampled():
     assert err <= TOL_OUT[case.dtype] and lerr <= TOL_LSE
     assert torch.isfinite(out).all()
     p.close()
+
+
+VK_CASES = [
+    # name, layout, QN, S, block_size, pool_layout, lkv
+    ("vk_n128_s1", "BSND", 128, 1, 128, 1, [900, 33, 0]),
+    ("vk_n16_s4", "BNSD", 16, 4, 16, 0, [400, 5]),
+    ("vk_n2_s1", "BSH", 2, 1, 16, 1, [97, 64, 1]),
+    ("vk_n64_s2", "BSND", 64, 2, 128, 0, [2100, 130]),
+]
+
+
+@pytest.mark.parametrize("case_args", VK_CASES, ids=[c[0] for c in VK_CASES])
+def test_mla_value_is_key(case_args):
+    # value passed as the key tensor itself (the latent cache read as both):
+    # V comes from the K tiles
+    name, layout, QN, S, bs, pl, lkv = case_args
+    case = W.make_mla_decode(f"mla_{name}", layout=layout, B=len(lkv), QN=QN, Sq=S, lkv=lkv,
+                             block_size=bs, pool_layout=pl, seed=1250 + QN, extra_blocks=2, nan_pool=True)
+    case.v = case.k
+    say(f"[mla] {case.name} value=key layout={layout} QN={QN} S={S} bs={bs} pool={pl} lkv={lkv}")
+    ref = oracle.attention(case)
+    to_dev(case)
+    case.v = case.k                      # one device tensor for both
+    p = fia_plan(case)
+    out, lse = run(p)
+    compare(case, out, lse, *ref)
+    p.close()

@@ -680,6 +680,17 @@ def mla_decode_bf16(device="cpu") -> FiaCase:
                            pool_layout=1, seed=1010, device=device)
 
 
+def mla_decode_shared_kv_bf16(device="cpu") -> FiaCase:
+    """The MLA decode workload with value passed as the key tensor itself (the
+    latent cache read as both key and value): key pool (NB, 128, 512) and
+    key_rope pool (NB, 128, 64) only."""
+    case = mla_decode_bf16(device)
+    case.name = "mla_decode_shared_kv_bf16_b64_n128_d512_rope64_bs128"
+    case.v = case.k
+    case.meta["v_is_k"] = True
+    return case
+
+
 WORKLOADS = {
     "c1": c1_dense_causal_fp16,
     "c2": c2_gqa_causal_bf16,
@@ -691,4 +702,5 @@ WORKLOADS = {
     "int8_decode": int8_kv_decode_bf16,
     "fp8_bsa": fp8_block_sparse,
     "mla_decode": mla_decode_bf16,
+    "mla_shared_kv": mla_decode_shared_kv_bf16,
 }
