@@ -1821,19 +1821,22 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_decode(DecodeArgs a)
         // K_rope row n, chunk (4 s + qd) ^ ((n / 2) % 8) (the same for row 16 + n);
         // V^T (transposed reads as in the decode kernel): tile o = 8 og + oi
         // reads chunk pair 2 (o ^ (trow % 8)) = 16 og + 2 (oi ^ (trow % 8)).
-        int koff[4], roff[NKR], voffs[8];
+        int koff[4], roff[NKR], voffs[VK ? 8 : 1];
 #pragma unroll
         for (int si = 0; si < 4; ++si) koff[si] = n * D + 8 * (4 * (si ^ (n >> 2)) + (qd ^ (n & 3)));
 #pragma unroll
         for (int sr = 0; sr < NKR; ++sr) roff[sr] = ST * D + n * DR + 8 * ((4 * sr + qd) ^ ((n >> 1) & 7));
-        {
-            const int vi = lane & 15;
-            const int trow = 4 * qd + (vi >> 2);
-            const int tcol_lo = (vi & 3) >> 1, tsub = 4 * (vi & 1);
+        // V^T reads: with V in its own slot the offsets are computed per read
+        // (fewer registers held for the read-ahead), with V in the K slot
+        // (K's swizzle) they are held
+        const int vi = lane & 15;
+        const int trow = 4 * qd + (vi >> 2);
+        const int tcol_lo = (vi & 3) >> 1, tsub = 4 * (vi & 1);
+        const int vrb = trow * D + tsub + 8 * tcol_lo, vsw = trow & 7;
+        auto vofs = [&](int o) { return vrb + 16 * ((o & 7) ^ vsw) + 128 * (o >> 3); };
+        if constexpr (VK) {
 #pragma unroll
-            for (int oi = 0; oi < 8; ++oi)
-                voffs[oi] = VK ? trow * D + 8 * ((2 * oi + tcol_lo) ^ (trow & 15)) + tsub   // K's swizzle
-                               : trow * D + 8 * (2 * (oi ^ (trow & 7)) + tcol_lo) + tsub;
+            for (int oi = 0; oi < 8; ++oi) voffs[oi] = trow * D + 8 * ((2 * oi + tcol_lo) ^ (trow & 15)) + tsub;
         }
 
         f32x4 acc[NO];
@@ -1886,20 +1889,43 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_decode(DecodeArgs a)
             if (nh > 0) {
                 const uint16_t* kb = smem + kMlaKSlot * (st % NSLOT);
                 f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+                if constexpr (!VK) {
+                    // K operands one k-step ahead of their MFMAs (the scheduling
+                    // barrier keeps each read ahead of the previous step's
+                    // MFMAs; measured 3 % faster; with V read from the K slot
+                    // the extra registers spill, so that path reads in place)
+                    auto rdk = [&](int s, uint4& x0, uint4& x1) {
+                        const uint16_t* kp = s < NKM ? kb + koff[s & 3] + 128 * (s >> 2) : kb + roff[s - NKM];
+                        const int r16 = s < NKM ? 16 * D : 16 * DR;
+                        x0 = *(const uint4*)(kp);
+                        x1 = *(const uint4*)(kp + r16);
+                    };
+                    uint4 c0, c1, n0, n1;
+                    rdk(0, c0, c1);
 #pragma unroll
-                for (int s = 0; s < NKM; ++s) {
-                    const uint16_t* kp = kb + koff[s & 3] + 128 * (s >> 2);
-                    const uint4 a0 = *(const uint4*)(kp);
-                    const uint4 a1 = *(const uint4*)(kp + 16 * D);
-                    s0 = O::mma16(a0, qf[s], s0);
-                    s1 = O::mma16(a1, qf[s], s1);
-                }
+                    for (int s = 0; s < NKM + NKR; ++s) {
+                        if (s + 1 < NKM + NKR) rdk(s + 1, n0, n1);
+                        s0 = O::mma16(c0, qf[s], s0);
+                        s1 = O::mma16(c1, qf[s], s1);
+                        __builtin_amdgcn_sched_barrier(0);
+                        c0 = n0; c1 = n1;
+                    }
+                } else {
 #pragma unroll
-                for (int s = 0; s < NKR; ++s) {
-                    const uint4 a0 = *(const uint4*)(kb + roff[s]);
-                    const uint4 a1 = *(const uint4*)(kb + roff[s] + 16 * DR);
-                    s0 = O::mma16(a0, qf[NKM + s], s0);
-                    s1 = O::mma16(a1, qf[NKM + s], s1);
+                    for (int s = 0; s < NKM; ++s) {
+                        const uint16_t* kp = kb + koff[s & 3] + 128 * (s >> 2);
+                        const uint4 a0 = *(const uint4*)(kp);
+                        const uint4 a1 = *(const uint4*)(kp + 16 * D);
+                        s0 = O::mma16(a0, qf[s], s0);
+                        s1 = O::mma16(a1, qf[s], s1);
+                    }
+#pragma unroll
+                    for (int s = 0; s < NKR; ++s) {
+                        const uint4 a0 = *(const uint4*)(kb + roff[s]);
+                        const uint4 a1 = *(const uint4*)(kb + roff[s] + 16 * DR);
+                        s0 = O::mma16(a0, qf[NKM + s], s0);
+                        s1 = O::mma16(a1, qf[NKM + s], s1);
+                    }
                 }
                 float x[8];
 #pragma unroll
@@ -1954,12 +1980,30 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_decode(DecodeArgs a)
             }
             if (nh > 0) {
                 const uint16_t* vb = VK ? smem + kMlaKSlot * (st % NSLOT) : smem + 2 * kMlaKSlot + kMlaVSlot * (st & 1);
+                if constexpr (!VK) {
+                    // V^T operands one tile ahead of their MFMAs
+                    uint2 cl, ch, nl, nh2;
+                    cl = lds_read_tr16(vb + vofs(0));
+                    ch = lds_read_tr16(vb + vofs(0) + 16 * D);
 #pragma unroll
-                for (int o = 0; o < NO; ++o) {
-                    const uint16_t* vp = vb + voffs[o & 7] + 128 * (o >> 3);
-                    const uint2 lo = lds_read_tr16(vp);
-                    const uint2 hi = lds_read_tr16(vp + 16 * D);
-                    acc[o] = O::mma16(make_uint4(lo.x, lo.y, hi.x, hi.y), pb, acc[o]);
+                    for (int o = 0; o < NO; ++o) {
+                        if (o + 1 < NO) {
+                            const uint16_t* vp = vb + vofs(o + 1);
+                            nl = lds_read_tr16(vp);
+                            nh2 = lds_read_tr16(vp + 16 * D);
+                        }
+                        acc[o] = O::mma16(make_uint4(cl.x, cl.y, ch.x, ch.y), pb, acc[o]);
+                        __builtin_amdgcn_sched_barrier(0);
+                        cl = nl; ch = nh2;
+                    }
+                } else {
+#pragma unroll
+                    for (int o = 0; o < NO; ++o) {
+                        const uint16_t* vp = vb + voffs[o & 7] + 128 * (o >> 3);
+                        const uint2 lo = lds_read_tr16(vp);
+                        const uint2 hi = lds_read_tr16(vp + 16 * D);
+                        acc[o] = O::mma16(make_uint4(lo.x, lo.y, hi.x, hi.y), pb, acc[o]);
+                    }
                 }
             }
         }
