@@ -1821,23 +1821,22 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_decode(DecodeArgs a)
         // K_rope row n, chunk (4 s + qd) ^ ((n / 2) % 8) (the same for row 16 + n);
         // V^T (transposed reads as in the decode kernel): tile o = 8 og + oi
         // reads chunk pair 2 (o ^ (trow % 8)) = 16 og + 2 (oi ^ (trow % 8)).
-        int koff[4], roff[NKR], voffs[VK ? 8 : 1];
+        int koff[4], roff[NKR];
 #pragma unroll
         for (int si = 0; si < 4; ++si) koff[si] = n * D + 8 * (4 * (si ^ (n >> 2)) + (qd ^ (n & 3)));
 #pragma unroll
         for (int sr = 0; sr < NKR; ++sr) roff[sr] = ST * D + n * DR + 8 * ((4 * sr + qd) ^ ((n >> 1) & 7));
-        // V^T reads: with V in its own slot the offsets are computed per read
-        // (fewer registers held for the read-ahead), with V in the K slot
-        // (K's swizzle) they are held
+        // V^T reads (offsets computed per read: fewer registers held for the
+        // read-ahead); V in the K slot uses K's swizzle
         const int vi = lane & 15;
         const int trow = 4 * qd + (vi >> 2);
         const int tcol_lo = (vi & 3) >> 1, tsub = 4 * (vi & 1);
         const int vrb = trow * D + tsub + 8 * tcol_lo, vsw = trow & 7;
-        auto vofs = [&](int o) { return vrb + 16 * ((o & 7) ^ vsw) + 128 * (o >> 3); };
-        if constexpr (VK) {
-#pragma unroll
-            for (int oi = 0; oi < 8; ++oi) voffs[oi] = trow * D + 8 * ((2 * oi + tcol_lo) ^ (trow & 15)) + tsub;
-        }
+        auto vofs = [&](int o) {
+            if (VK) return trow * D + tsub + 8 * ((2 * (o & 7) + tcol_lo) ^ (trow & 15)) + 128 * (o >> 3);
+            return vrb + 16 * ((o & 7) ^ vsw) + 128 * (o >> 3);
+        };
+
 
         f32x4 acc[NO];
 #pragma unroll
@@ -1980,7 +1979,7 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_decode(DecodeArgs a)
             }
             if (nh > 0) {
                 const uint16_t* vb = VK ? smem + kMlaKSlot * (st % NSLOT) : smem + 2 * kMlaKSlot + kMlaVSlot * (st & 1);
-                if constexpr (!VK) {
+                {
                     // V^T operands one tile ahead of their MFMAs
                     uint2 cl, ch, nl, nh2;
                     cl = lds_read_tr16(vb + vofs(0));
@@ -1995,14 +1994,6 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_decode(DecodeArgs a)
                         acc[o] = O::mma16(make_uint4(cl.x, cl.y, ch.x, ch.y), pb, acc[o]);
                         __builtin_amdgcn_sched_barrier(0);
                         cl = nl; ch = nh2;
-                    }
-                } else {
-#pragma unroll
-                    for (int o = 0; o < NO; ++o) {
-                        const uint16_t* vp = vb + voffs[o & 7] + 128 * (o >> 3);
-                        const uint2 lo = lds_read_tr16(vp);
-                        const uint2 hi = lds_read_tr16(vp + 16 * D);
-                        acc[o] = O::mma16(make_uint4(lo.x, lo.y, hi.x, hi.y), pb, acc[o]);
                     }
                 }
             }
