@@ -466,3 +466,36 @@ def test_mla_validation():
     assert code(S=2, mode=0) == _abi.FIA_ERR_UNSUPPORTED            # S > 1: sparse_mode 3
     assert code(mask=torch.zeros(B, 256, dtype=torch.uint8)) == _abi.FIA_ERR_UNSUPPORTED
     assert code(kvn=2, k=torch.zeros(4, bs, 2 * D, dtype=torch.bfloat16)) == _abi.FIA_ERR_UNSUPPORTED
+
+
+def test_mla_tnd_validation():
+    # TND MLA: cumulative actual_seq_qlen (each batch 1..16 tokens), per-batch
+    # actual_seq_kvlen, paged cache; sparse_mode 0 without a mask or 3
+    QN, bs, D = 8, 16, 512
+    pool = torch.zeros(8, bs, D, dtype=torch.bfloat16)
+    kr = torch.zeros(8, bs, 64, dtype=torch.bfloat16)
+
+    def code(lq=(1, 3), lkv=(40, 20), mode=3, mask="tmpl", table_rows=2):
+        T = int(sum(lq))
+        q = torch.zeros(T, QN, D, dtype=torch.bfloat16)
+        qr = torch.zeros(T, QN, 64, dtype=torch.bfloat16)
+        p = _params(num_heads=QN, num_key_value_heads=1, input_layout="TND", block_size=bs,
+                    sparse_mode=mode)
+        dq, dk = fia.describe(qr), fia.describe(kr)
+        p.query_rope, p.key_rope = ctypes.pointer(dq), ctypes.pointer(dk)
+        ql = np.cumsum(np.array(lq, dtype=np.int64))
+        kl = np.array(lkv, dtype=np.int64)
+        p.actual_seq_qlen, p.n_actual_seq_qlen = ql.ctypes.data, len(ql)
+        p.actual_seq_kvlen, p.n_actual_seq_kvlen = kl.ctypes.data, len(kl)
+        m = torch.triu(torch.ones(2048, 2048, dtype=torch.uint8), diagonal=1) if mask == "tmpl" else mask
+        bt = torch.zeros(table_rows, 4, dtype=torch.int32)
+        out = torch.zeros(T, QN, D, dtype=torch.bfloat16)
+        return _phase1(q, pool, pool, p, out=out, bt=bt, mask=m)[0]
+
+    assert code() == _abi.FIA_OK
+    assert code(lq=(1, 1), mode=0, mask=None) == _abi.FIA_OK
+    assert code(lq=(16, 2)) == _abi.FIA_OK
+    assert code(lq=(17, 2)) == _abi.FIA_ERR_UNSUPPORTED              # 1..16 tokens per batch
+    assert code(mode=4) == _abi.FIA_ERR_UNSUPPORTED
+    assert code(table_rows=3) == _abi.FIA_ERR_SHAPE                  # one table row per batch
+    assert code(lkv=(40, 70)) == _abi.FIA_ERR_SHAPE                  # past the table's 4 pages

@@ -791,3 +791,34 @@ def test_mla_zero_key_rope_equals_plain_attention():
     case.rope = None
     out0, lse0 = oracle.attention(case)
     assert np.array_equal(out, out0) and np.array_equal(lse, lse0)
+
+
+@pytest.mark.parametrize("mode_causal", [True, False])
+def test_mla_tnd_equals_brute_force(mode_causal):
+    # TND MLA decode: batch b's lq_b query tokens are rows q_start_b .. of
+    # the (T, N, D) query; kv lengths are per batch with the paged cache
+    lq = [1, 3, 4] if mode_causal else [1, 1, 1]
+    case = W.make_mla_decode(layout="TND", B=3, QN=4, lq=lq, lkv=[37, 2, 64], block_size=16,
+                             D=24, Dr=8, pool_layout=1, seed=63, extra_blocks=1)
+    assert case.sparse_mode == (3 if mode_causal else 0)
+    out, lse = oracle.attention(case)
+    bt = case.block_table.numpy()
+    K = _gather_rows(case.k, bt, 16, 1)
+    KR = _gather_rows(case.rope["key_rope"], bt, 16, 1)
+    V = _gather_rows(case.v, bt, 16, 1)
+    q = case.q.to(torch.float64).numpy()
+    qr = case.rope["query_rope"].to(torch.float64).numpy()
+    row = 0
+    for b in range(3):
+        L = int(case.lkv[b])
+        for t in range(lq[b]):
+            n = L - lq[b] + t + 1 if mode_causal else L
+            for h in range(4):
+                if n <= 0:
+                    assert np.all(out[row, h] == 0) and np.isposinf(lse[row, h])
+                    continue
+                s = case.scale * (K[b, :n] @ q[row, h] + KR[b, :n] @ qr[row, h])
+                w = np.exp(s - s.max())
+                assert np.max(np.abs(out[row, h] - w @ V[b, :n] / w.sum())) < 1e-12
+                assert abs(lse[row, h] - (s.max() + math.log(w.sum()))) < 1e-12
+            row += 1

@@ -110,8 +110,9 @@ class FiaCase:
     def seq_kvlen_arg(self):
         if self.lkv is None:
             return None
-        if self.layout == "TND":
+        if self.layout == "TND" and self.block_table is None:
             return np.cumsum(self.lkv).astype(np.int64)
+        # (TND with page attention, the MLA case: each batch's own length)
         return self.lkv.astype(np.int64)
 
 
@@ -343,8 +344,8 @@ def make_mla_decode(name="custom", *, layout="BSND", dtype=torch.bfloat16, B=2, 
                     lq=None, lkv=(100, 37), block_size=16, D=512, Dr=64, pool_layout=1,
                     scale=None, seed=0, device="cpu", extra_blocks=0, nan_pool=False,
                     return_lse=True) -> FiaCase:
-    """MLA decode: query (``layout``, Q_N = QN, S = Sq <= 16, D = 512) with its
-    64-wide rope part, one kv head; key and value (D = 512) and key_rope
+    """MLA decode: query (``layout``, Q_N = QN, S = Sq <= 16, D = 512; TND: the
+    batches' ``lq`` tokens back to back) with its 64-wide rope part, one kv head; key and value (D = 512) and key_rope
     (D = 64) in a shared paged pool, (NB, bs, D) (``pool_layout`` 1) or
     (NB, 1, bs, D) (0), addressed through a block table holding a seeded
     permutation of the pool's block ids.  Query S > 1 uses bottom-right causal
@@ -368,6 +369,9 @@ def make_mla_decode(name="custom", *, layout="BSND", dtype=torch.bfloat16, B=2, 
         pos += nblk[b]
     sq, sqr = ss[STREAM_Q].spawn(2)
     sk, skr = ss[STREAM_K].spawn(2)
+    if layout == "TND":
+        # TND: the batches' query tokens (lq, each 1..16) back to back
+        Sq = int(lq.sum())
     q = normal_tensor(_shape(layout, B, QN, Sq, D), dtype, sq, device)
     qr = normal_tensor(_shape(layout, B, QN, Sq, Dr), dtype, sqr, device)
     def pool(d):
@@ -390,10 +394,11 @@ def make_mla_decode(name="custom", *, layout="BSND", dtype=torch.bfloat16, B=2, 
                 else:
                     t[last, tail:] = float("nan")
     mask = None
-    if Sq > 1:
+    causal = (lq.max() > 1) if layout == "TND" else Sq > 1
+    if causal:
         mask = torch.triu(torch.ones(2048, 2048, dtype=torch.uint8), diagonal=1).to(device)
     return FiaCase(name=name, layout=layout, dtype=dtype, B=B, QN=QN, KVN=1, Sq=Sq,
-                   Skv=cols * block_size, Dqk=D, Dv=D, scale=scale, sparse_mode=3 if Sq > 1 else 0,
+                   Skv=cols * block_size, Dqk=D, Dv=D, scale=scale, sparse_mode=3 if causal else 0,
                    lq=lq, lkv=lkv, q=q, k=k, v=v, atten_mask=mask,
                    block_table=torch.from_numpy(table).to(device), block_size=block_size,
                    pool_layout=pool_layout, return_lse=return_lse, meta={"NB": NB},
