@@ -106,7 +106,7 @@ struct DecSeg {
     int32_t first;       // first piece of this segment
     int32_t count;       // pieces of this segment (0 when lkv == 0)
     int32_t lq;          // valid query tokens of batch b (rows past it: out 0, lse +inf)
-    int32_t pad;
+    int32_t q_row0;      // TND: first query row of batch b (else 0)
 };
 
 struct DecPiece {
@@ -164,6 +164,7 @@ struct DecodeArgs {
     int64_t qr_sB, qr_sH, qr_sS;
     int64_t pr_blk;
     int32_t mla_nw;
+    int32_t tnd;                   // TND query (MLA): rows q_row0 + t; rows t >= Lq do not exist
     int32_t v_is_k;                // value is the key tensor itself (V read from the K tile)
 };
 

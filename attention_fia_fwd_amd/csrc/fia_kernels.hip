@@ -1731,13 +1731,16 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_decode(DecodeArgs a)
         const int jmax = a.causal ? jbase + tq : INT32_MAX;
         const int jmin = a.causal ? jbase + tq_min : INT32_MAX;
 
-        // [Q | Q_rope]^T as the B operand: column n, d = 32 s + 8 qd
+        // [Q | Q_rope]^T as the B operand: column n, d = 32 s + 8 qd (query
+        // tokens at or past the batch's length are not read: in TND they are
+        // the next batch's rows)
         uint4 qf[NKM + NKR];
-        if (n < nh) {
+        if (n < nh && tq < db.lq) {
+            const int64_t qrow = (int64_t)db.q_row0 + tq;
             const uint16_t* src = (const uint16_t*)a.q + (int64_t)b * a.q_sB + (int64_t)hq * a.q_sH +
-                                  (int64_t)tq * a.q_sS + 8 * qd;
+                                  qrow * a.q_sS + 8 * qd;
             const uint16_t* srr = (const uint16_t*)a.qr + (int64_t)b * a.qr_sB + (int64_t)hq * a.qr_sH +
-                                  (int64_t)tq * a.qr_sS + 8 * qd;
+                                  qrow * a.qr_sS + 8 * qd;
 #pragma unroll
             for (int s = 0; s < NKM + NKR; ++s) {
                 uint4 v = s < NKM ? *(const uint4*)(src + 32 * s) : *(const uint4*)(srr + 32 * (s - NKM));
@@ -2031,10 +2034,12 @@ __global__ __launch_bounds__(64) void decode_combine(DecodeArgs a)
     const int kvh = h / a.G, r = (h % a.G) * S + t;
     const int hc = r / a.Gc, n = r % a.Gc;
     const DecSeg sg = a.segs[((int64_t)b * a.KVN + kvh) * a.nhc + hc];
+    if (a.tnd && t >= sg.lq) return;        // TND: the row does not exist
     const int ns = t < sg.lq ? sg.count : 0;
     const int64_t slot0 = sg.first;
     const int lane = threadIdx.x;
-    uint16_t* op = (uint16_t*)a.o + (int64_t)b * a.o_sB + (int64_t)h * a.o_sH + (int64_t)t * a.o_sS;
+    const int64_t orow = (int64_t)sg.q_row0 + t;
+    uint16_t* op = (uint16_t*)a.o + (int64_t)b * a.o_sB + (int64_t)h * a.o_sH + orow * a.o_sS;
 
     float M = -INFINITY;
     for (int s = 0; s < ns; ++s) M = fmaxf(M, a.part_lse[(slot0 + s) * a.Gc + n]);
@@ -2066,8 +2071,10 @@ __global__ __launch_bounds__(64) void decode_combine(DecodeArgs a)
         const uint32_t pk = O::pack2(val, 0.f);
         op[lane + 64 * e] = (uint16_t)(pk & 0xffffu);
     }
-    if (a.return_lse && lane == 0)
-        a.lse[((int64_t)b * a.QN + h) * S + t] = wsum > 0.f ? M + __logf(wsum) : INFINITY;
+    if (a.return_lse && lane == 0) {
+        const int64_t li = a.tnd ? orow * a.QN + h : ((int64_t)b * a.QN + h) * S + t;
+        a.lse[li] = wsum > 0.f ? M + __logf(wsum) : INFINITY;
+    }
 }
 
 // ---------------------------------------------------------------------------

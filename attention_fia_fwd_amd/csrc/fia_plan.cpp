@@ -343,10 +343,13 @@ fia_status fia_get_workspace_size(const fia_tensor* query, const fia_tensor* key
         // PageAttention (constraints, page attention scenario).  Query S == 1:
         // block_size a multiple of 16; query S > 1: a multiple of 128 in
         // [128, 512].  A TND query with a paged cache is not provided.
-        if (layout == LAYOUT_TND) return FIA_ERR_UNSUPPORTED;
+        // (MLA with a query D of 512 allows TND: the batch is the count of
+        // actual_seq_qlen, checked against the table below)
+        if (layout == LAYOUT_TND && !mla) return FIA_ERR_UNSUPPORTED;
         if (!block_table->data) return FIA_ERR_NULLPTR;
         if (block_table->dtype != FIA_I32) return FIA_ERR_DTYPE;
-        if (block_table->ndim != 2 || block_table->dims[0] != gq.B) return FIA_ERR_SHAPE;
+        if (block_table->ndim != 2) return FIA_ERR_SHAPE;
+        if (layout != LAYOUT_TND && block_table->dims[0] != gq.B) return FIA_ERR_SHAPE;
         if (prm->block_size <= 0 || prm->block_size % 16 != 0) return FIA_ERR_PARAM;
         if (mla) {
             // MLA with a query D of 512: block_size 16 or 128
@@ -396,9 +399,17 @@ fia_status fia_get_workspace_size(const fia_tensor* query, const fia_tensor* key
         if ((st = resolve_cumulative(prm->actual_seq_qlen, prm->n_actual_seq_qlen, gq.S, &lq,
                                      &qstart)) != FIA_OK)
             return st;
-        if ((st = resolve_cumulative(prm->actual_seq_kvlen, prm->n_actual_seq_kvlen, Skv, &lkv,
-                                     &kvstart)) != FIA_OK)
+        if (paged) {
+            // MLA TND with page attention: actual_seq_kvlen holds each batch's
+            // own length (D 512 TND constraints), not cumulative sums
+            if ((st = resolve_lengths(prm->actual_seq_kvlen, prm->n_actual_seq_kvlen,
+                                      prm->n_actual_seq_qlen, Skv, &lkv)) != FIA_OK)
+                return st;
+            if (block_table->dims[0] != prm->n_actual_seq_qlen) return FIA_ERR_SHAPE;
+        } else if ((st = resolve_cumulative(prm->actual_seq_kvlen, prm->n_actual_seq_kvlen, Skv, &lkv,
+                                            &kvstart)) != FIA_OK) {
             return st;
+        }
         B = prm->n_actual_seq_qlen;
     } else {
         if (decode)
@@ -505,13 +516,21 @@ fia_status fia_get_workspace_size(const fia_tensor* query, const fia_tensor* key
     // ----- MLA (query D 512, rope D 64, one kv head, paged) -----
     const void* qr_data = nullptr;
     int64_t qr_sB = 0, qr_sH = 0, qr_sS = 0;
+    int64_t mla_S = gq.S;               // query tokens per batch (TND: the largest)
     if (mla) {
-        if (layout == LAYOUT_TND || !paged) return FIA_ERR_UNSUPPORTED;
+        if (!paged) return FIA_ERR_UNSUPPORTED;
         if (gq.D != 512 || Dv != 512) return FIA_ERR_UNSUPPORTED;
         if (KVN != 1 || QN > 128 || (QN & (QN - 1)) != 0) return FIA_ERR_UNSUPPORTED;
-        if (gq.S > kDecodeHeads) return FIA_ERR_UNSUPPORTED;
-        // S == 1: sparse_mode 0 without a mask; S > 1: sparse_mode 3
-        if (mask || (gq.S == 1 && atten_mask) || (gq.S > 1 && mode != 3)) return FIA_ERR_UNSUPPORTED;
+        if (layout == LAYOUT_TND) {
+            mla_S = 1;
+            for (int64_t x : lq) mla_S = std::max(mla_S, x);
+            // TND: sparse_mode 0 without a mask or 3 (checked with the mask above)
+            if (mode != 0 && mode != 3) return FIA_ERR_UNSUPPORTED;
+        } else if (mask || (gq.S == 1 && atten_mask) || (gq.S > 1 && mode != 3)) {
+            // S == 1: sparse_mode 0 without a mask; S > 1: sparse_mode 3
+            return FIA_ERR_UNSUPPORTED;
+        }
+        if (mla_S > kDecodeHeads) return FIA_ERR_UNSUPPORTED;
         Geo gr;
         if ((st = geometry(prm->query_rope, layout, bsh, QN, &gr)) != FIA_OK) return st;
         if (gr.N != QN || gr.B != gq.B || gr.S != gq.S || gr.D != 64) return FIA_ERR_SHAPE;
@@ -523,6 +542,8 @@ fia_status fia_get_workspace_size(const fia_tensor* query, const fia_tensor* key
         qr_data = prm->query_rope->data;
         if (layout == LAYOUT_BNSD) {
             qr_sB = QN * gq.S * 64; qr_sH = gq.S * 64; qr_sS = 64;
+        } else if (layout == LAYOUT_TND) {
+            qr_sB = 0; qr_sH = 64; qr_sS = QN * 64;     // row = first row of the batch + token
         } else {
             qr_sB = gq.S * QN * 64; qr_sH = 64; qr_sS = QN * 64;
         }
@@ -608,8 +629,9 @@ fia_status fia_get_workspace_size(const fia_tensor* query, const fia_tensor* key
         d.return_lse = want_lse;
         d.paged = paged;
         const int64_t D = gq.D;
-        const int64_t S = gq.S;
+        const int64_t S = mla_S;
         d.S = (int32_t)S;
+        d.tnd = layout == LAYOUT_TND;
         d.causal = !decode && mode == 3;
         d.mask = decode ? mask : nullptr;     // S > 1 reaches here only without one
         d.mask_bstride = mask_bstride;
@@ -623,6 +645,8 @@ fia_status fia_get_workspace_size(const fia_tensor* query, const fia_tensor* key
         d.tok_stride = tok_stride;
         if (layout == LAYOUT_BNSD) {
             d.q_sB = QN * S * D; d.q_sH = S * D; d.q_sS = D;
+        } else if (layout == LAYOUT_TND) {
+            d.q_sB = 0; d.q_sH = D; d.q_sS = QN * D;        // row = first row of the batch + token
         } else {
             d.q_sB = S * QN * D; d.q_sH = D; d.q_sS = QN * D;
         }
@@ -681,6 +705,7 @@ fia_status fia_get_workspace_size(const fia_tensor* query, const fia_tensor* key
                 sg.b = (int32_t)b;
                 sg.lkv = (int32_t)L;
                 sg.lq = (int32_t)lq[(size_t)b];
+                sg.q_row0 = layout == LAYOUT_TND ? (int32_t)qstart[(size_t)b] : 0;
                 sg.first = (int32_t)pieces.size();
                 for (int64_t t = 0; t < L;) {
                     if (remaining < 16) {                  // next wave

@@ -109,3 +109,32 @@ def test_mla_value_is_key(case_args):
     out, lse = run(p)
     compare(case, out, lse, *ref)
     p.close()
+
+
+TND_CASES = [
+    # name, QN, lq (tokens per batch), lkv, block_size, value = key
+    ("tnd_n16_mixed", 16, [1, 3, 16, 2], [300, 50, 1000, 2], 16, False),
+    ("tnd_n128_s1", 128, [1, 1, 1], [700, 1, 40], 128, False),
+    ("tnd_n8_short_kv", 8, [4, 1], [3, 200], 16, False),
+    ("tnd_n32_value_is_key", 32, [2, 5, 1], [600, 130, 0], 128, True),
+]
+
+
+@pytest.mark.parametrize("case_args", TND_CASES, ids=[c[0] for c in TND_CASES])
+def test_mla_tnd(case_args):
+    # TND query: batch b's lq_b tokens are consecutive rows; kv lengths per
+    # batch; rows of a batch with fewer allowed keys than tokens are 0 / +inf
+    name, QN, lq, lkv, bs, vk = case_args
+    case = W.make_mla_decode(f"mla_{name}", layout="TND", B=len(lq), QN=QN, lq=lq, lkv=lkv,
+                             block_size=bs, pool_layout=1, seed=1270 + QN, extra_blocks=2, nan_pool=True)
+    if vk:
+        case.v = case.k
+    say(f"[mla] {case.name} TND QN={QN} lq={lq} lkv={lkv} bs={bs} value=key={vk}")
+    ref = oracle.attention(case)
+    to_dev(case)
+    if vk:
+        case.v = case.k
+    p = fia_plan(case)
+    out, lse = run(p)
+    compare(case, out, lse, *ref)
+    p.close()
