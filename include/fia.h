@@ -189,7 +189,8 @@ void fia_params_init(fia_params* p);
  *                block ids (page attention scenario of the v2 page): kv token
  *                j of batch b is row j % block_size of pool block
  *                block_table[b][j / block_size].  Any query S outside TND (a
- *                TND query with a paged cache returns FIA_ERR_UNSUPPORTED).
+ *                TND query with a paged cache returns FIA_ERR_UNSUPPORTED,
+ *                except for MLA: see query_rope in fia_params).
  *                Ids are not checked: each referenced id must be in
  *                [0, blocknum), as the page requires; entries past
  *                ceil(Lkv_b / block_size) are never read.
