@@ -251,8 +251,9 @@ def main():
                          "FETCH_SIZE / WRITE_SIZE counters to bytes) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only: this build runs on a single MI355X "
-              f"(asked for --gpus {args.gpus}); run with --gpus 1.", file=sys.stderr)
+        print(f"bench.py measures one GPU only: the kernels run on a single MI355X and the "
+              f"multi-GPU sharding is a design, not code (asked for --gpus {args.gpus}); "
+              f"run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import torch
