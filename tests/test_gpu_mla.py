@@ -68,8 +68,10 @@ def test_mla_zero_and_negative_scale(scale):
     p.close()
 
 
-def test_mla_full_size_workload_sampled():
-    case = W.mla_decode_bf16(device="cuda")
+@pytest.mark.parametrize("make", [W.mla_decode_bf16, W.mla_decode_shared_kv_bf16],
+                         ids=["separate_value", "value_is_key"])
+def test_mla_full_size_workload_sampled(make):
+    case = make(device="cuda")
     say(f"[mla] {case.name} (sampled rows)")
     rows = sample_rows(case, 48, seed=31, decode=True)
     ref_o, ref_l = oracle.attention(case, rows=rows)
