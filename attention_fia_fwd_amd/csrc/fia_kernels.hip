@@ -10,13 +10,21 @@
 //                   the GQA heads sharing a kv head are the 16 columns of
 //                   v_mfma_f32_16x16x32, so every K/V byte is read once;
 //                   pages are gathered through the block table.
+//   decode_split_i8 decode against an int8 KV cache (per-channel or
+//                   per-token scale and offset), the same column layout.
 //   decode_combine  merges the pieces of one (batch, head) by their LSE.
 //   bsa_compact     compacts the block-sparse mask into ascending kv-block
 //                   lists per (batch, head, q block).
+//   bsa_fp8         block-sparse prefill with E4M3FN inputs and per-block
+//                   scales: S^T on v_mfma_f32_32x32x64_f8f6f4, P V on bf16.
+//   mla_decode      MLA decode (query D 512 + rope 64, one kv head): a
+//                   workgroup of up to 8 waves shares DMA-staged K / K_rope /
+//                   V tiles across up to 128 (head, token) rows.
 //
 // The method: pages "torch_npu.npu_prompt_flash_attention" (formula),
 // "torch_npu.npu_fused_infer_attention_score_v2" (formula, sparse_mode,
-// softmax_lse), "aclnnBlockSparseAttentionV2" (formula, constraints).  The
+// softmax_lse, kv pseudo-quant and query_rope / key_rope parameters),
+// "aclnnBlockSparseAttentionV2" (formula, constraints, FP8 feature).  The
 // online-softmax rescaling and the split-KV merge by LSE rest on the identity
 // the softmax_lse output description gives: a row's log-sum-exp lets partial
 // results over disjoint key sets be merged exactly.
