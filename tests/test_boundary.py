@@ -499,3 +499,39 @@ def test_mla_tnd_validation():
     assert code(mode=4) == _abi.FIA_ERR_UNSUPPORTED
     assert code(table_rows=3) == _abi.FIA_ERR_SHAPE                  # one table row per batch
     assert code(lkv=(40, 70)) == _abi.FIA_ERR_SHAPE                  # past the table's 4 pages
+
+
+def test_product_path_does_not_touch_the_oracle():
+    # the GPU library and its binding share nothing with the fp64 oracle
+    import ast
+    pkg = os.path.join(ROOT, "attention_fia_fwd_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for fn in files:
+            if fn.endswith((".py", ".hip", ".cpp", ".h")):
+                src = open(os.path.join(dirpath, fn), encoding="utf-8").read()
+                assert "import oracle" not in src and "from oracle" not in src, fn
+                assert "oracle.h" not in src and "liboracle" not in src, fn
+    lib = _abi.lib()
+    assert not hasattr(lib, "oracle_attention") and not hasattr(lib, "oracle_block_sparse")
+    # bench.py may use the oracle only in its CPU-baseline leg
+    tree = ast.parse(open(os.path.join(ROOT, "bench.py"), encoding="utf-8").read())
+    for fn in ast.walk(tree):
+        if isinstance(fn, ast.FunctionDef):
+            for node in ast.walk(fn):
+                if isinstance(node, (ast.Import, ast.ImportFrom)):
+                    names = [a.name for a in node.names] + [getattr(node, "module", None) or ""]
+                    if "oracle" in names:
+                        assert fn.name == "cpu_baseline", fn.name
+    top = [n for n in tree.body if isinstance(n, (ast.Import, ast.ImportFrom))]
+    assert not any("oracle" in [a.name for a in n.names] + [getattr(n, "module", None) or ""] for n in top)
+
+
+def test_binding_fails_loudly_without_the_library(tmp_path):
+    saved = (_abi._lib, _abi.LIB_PATH)
+    try:
+        _abi._lib = None
+        _abi.LIB_PATH = str(tmp_path / "missing_libfia.so")
+        with pytest.raises(Exception):
+            _abi.lib()
+    finally:
+        _abi._lib, _abi.LIB_PATH = saved
