@@ -2060,24 +2060,33 @@ __global__ __launch_bounds__(64) void decode_combine(DecodeArgs a)
         for (int s = 0; s < ns; ++s) {
             const float ws = __expf(a.part_lse[(slot0 + s) * a.Gc + n] - M);
             wsum += ws;
-            const float* po = a.part_o + ((slot0 + s) * a.Gc + n) * D;
+            const float* po = a.part_o + ((slot0 + s) * a.Gc + n) * D + PER * lane;
 #pragma unroll
-            for (int e = 0; e < PER; ++e) accv[e] += ws * po[lane + 64 * e];
+            for (int e = 0; e < PER; ++e) accv[e] += ws * po[e];
         }
     }
     const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+    float vals[PER];
 #pragma unroll
     for (int e = 0; e < PER; ++e) {
         float val = accv[e] * inv;
         if (a.kv_i8 && a.vmode == 0 && wsum > 0.f) {
             // int8 V per channel: the partials are in raw int8 units
-            const int64_t ch = (int64_t)kvh * D + lane + 64 * e;
+            const int64_t ch = (int64_t)kvh * D + PER * lane + e;
             const float sv = __uint_as_float((uint32_t)((const uint16_t*)a.v_scale)[ch] << 16);
             const float ov = a.v_off ? __uint_as_float((uint32_t)((const uint16_t*)a.v_off)[ch] << 16) : 0.f;
             val = sv * (val + ov);
         }
-        const uint32_t pk = O::pack2(val, 0.f);
-        op[lane + 64 * e] = (uint16_t)(pk & 0xffffu);
+        vals[e] = val;
+    }
+    if constexpr (PER % 2 == 0) {
+        // lane's PER consecutive outputs as bf16 / fp16 pairs
+        uint32_t* op2 = (uint32_t*)(op + PER * lane);
+#pragma unroll
+        for (int e = 0; e < PER / 2; ++e) op2[e] = O::pack2(vals[2 * e], vals[2 * e + 1]);
+    } else {
+#pragma unroll
+        for (int e = 0; e < PER; ++e) op[PER * lane + e] = (uint16_t)(O::pack2(vals[e], 0.f) & 0xffffu);
     }
     if (a.return_lse && lane == 0) {
         const int64_t li = a.tnd ? orow * a.QN + h : ((int64_t)b * a.QN + h) * S + t;
