@@ -156,8 +156,11 @@ typedef struct fia_params {
      * block_size 16 or 128 and key_rope a pool of the key's layout with D 64.
      * value is its own pool of the key's shape, or the key tensor itself
      * (same pointer: then the value bytes are not read a second time).
-     * softmax_lse is computed as for any other call.  Anything else with rope
-     * inputs returns FIA_ERR_UNSUPPORTED. */
+     * softmax_lse is computed as for any other call.  Errors: a rope dtype
+     * other than the query's FIA_ERR_DTYPE; rope shapes that do not match
+     * FIA_ERR_SHAPE; another block_size, or Q_N / KV_N above 128,
+     * FIA_ERR_PARAM; other head dims, KV_N, Q_N, S, layouts, modes, masks,
+     * int8 key/value or a contiguous cache FIA_ERR_UNSUPPORTED. */
     const fia_tensor* query_rope;
     const fia_tensor* key_rope;
 } fia_params;
