@@ -172,7 +172,8 @@ def attention(case, rows=None):
     a.sparse_mode = int(case.sparse_mode)
     a.decode = 1 if case.decode else 0
     a.pre_tokens, a.next_tokens = int(case.pre_tokens), int(case.next_tokens)
-    if case.atten_mask is not None and case.decode:
+    mla_band = getattr(case, "rope", None) is not None and case.sparse_mode == 4
+    if case.atten_mask is not None and case.decode and not mla_band:
         # query S == 1: one value per (batch, kv token), leading 1 broadcasts
         mn = np.ascontiguousarray(case.atten_mask.detach().to("cpu").to(torch.uint8).numpy())
         keep.append(mn)

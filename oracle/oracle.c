@@ -69,6 +69,8 @@
  *   s_j = scale * (sum_d q[b,h,i,d] k[b,g,j,d] + sum_r qr[b,h,i,r] kr[b,g,j,r]);
  * value and output keep D = Dv.  (The pages state the inputs and their
  * shapes, not a formula for the rope parts; concatenation is the reading.)
+ * With sparse_mode 4 the bottom-right band of the mode list applies at query
+ * S 1 too (the MLA constraints list that mode for S 1).
  */
 #include <math.h>
 #include <stdint.h>
@@ -204,7 +206,11 @@ static int64_t kv_off(const oracle_args* a, int64_t b, int64_t g, int64_t j, int
 
 static int allowed_dense(const oracle_args* a, int64_t b, int64_t i, int64_t j)
 {
-    if (a->decode)
+    /* MLA with a query D of 512 lists sparse_mode 4 (with the mask) at query
+     * S 1 as well (v2 page, query_rope / key_rope constraints): there the
+     * band applies to decode too, through the mode rules below */
+    const int mla_band = a->Dr > 0 && a->sparse_mode == 4;
+    if (a->decode && !mla_band)
         return a->mask ? a->mask[b * a->mask_bstride + j] == 0 : 1;
     int64_t delta = a->lkv[b] - a->lq[b];
     int masked_by_tensor = 0;

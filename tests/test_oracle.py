@@ -822,3 +822,33 @@ def test_mla_tnd_equals_brute_force(mode_causal):
                 assert np.max(np.abs(out[row, h] - w @ V[b, :n] / w.sum())) < 1e-12
                 assert abs(lse[row, h] - (s.max() + math.log(w.sum()))) < 1e-12
             row += 1
+
+
+@pytest.mark.parametrize("S,pre,nxt", [(1, 20, 0), (1, 5, 3), (3, 7, 0), (4, 10, 2), (2, 0, 0)])
+@pytest.mark.parametrize("pool_layout", [0, 1])
+def test_mla_band_equals_brute_force(S, pre, nxt, pool_layout):
+    # MLA with sparse_mode 4: query token t of batch b sees the keys
+    # Lkv - S + t - pre <= j <= Lkv - S + t + next, at query S 1 too
+    case = W.make_mla_decode(layout="BSND", B=3, QN=4, Sq=S, lkv=[37, 2, 64], block_size=16,
+                             D=24, Dr=8, pool_layout=pool_layout, seed=64, extra_blocks=1,
+                             band=(pre, nxt))
+    assert case.sparse_mode == 4
+    out, lse = oracle.attention(case)
+    bt = case.block_table.numpy()
+    K = _gather_rows(case.k, bt, 16, pool_layout)
+    KR = _gather_rows(case.rope["key_rope"], bt, 16, pool_layout)
+    V = _gather_rows(case.v, bt, 16, pool_layout)
+    q = case.q.to(torch.float64).numpy()                        # [B, S, N, D]
+    qr = case.rope["query_rope"].to(torch.float64).numpy()
+    for b in range(3):
+        L = int(case.lkv[b])
+        for t in range(S):
+            lo, hi = max(0, L - S + t - pre), min(L - 1, L - S + t + nxt)
+            for h in range(4):
+                if hi < lo:
+                    assert np.all(out[b, t, h] == 0) and np.isposinf(lse[b, h, t])
+                    continue
+                s = case.scale * (K[b, lo:hi + 1] @ q[b, t, h] + KR[b, lo:hi + 1] @ qr[b, t, h])
+                w = np.exp(s - s.max())
+                assert np.max(np.abs(out[b, t, h] - w @ V[b, lo:hi + 1] / w.sum())) < 1e-12
+                assert abs(lse[b, h, t] - (s.max() + math.log(w.sum()))) < 1e-12

@@ -343,7 +343,7 @@ def make_paged_prefill(name="custom", *, layout="BNSD", dtype=torch.bfloat16, B=
 def make_mla_decode(name="custom", *, layout="BSND", dtype=torch.bfloat16, B=2, QN=16, Sq=1,
                     lq=None, lkv=(100, 37), block_size=16, D=512, Dr=64, pool_layout=1,
                     scale=None, seed=0, device="cpu", extra_blocks=0, nan_pool=False,
-                    return_lse=True) -> FiaCase:
+                    return_lse=True, band=None) -> FiaCase:
     """MLA decode: query (``layout``, Q_N = QN, S = Sq <= 16, D = 512; TND: the
     batches' ``lq`` tokens back to back) with its 64-wide rope part, one kv head; key and value (D = 512) and key_rope
     (D = 64) in a shared paged pool, (NB, bs, D) (``pool_layout`` 1) or
@@ -351,7 +351,9 @@ def make_mla_decode(name="custom", *, layout="BSND", dtype=torch.bfloat16, B=2, 
     permutation of the pool's block ids.  Query S > 1 uses bottom-right causal
     masking (sparse_mode 3 with the 2048 template).  iid N(0,1) inputs; scale
     1/sqrt(D + Dr) unless given.  ``nan_pool`` fills the unreferenced blocks
-    and the tail rows of each batch's last block with NaN."""
+    and the tail rows of each batch's last block with NaN.  ``band`` =
+    (pre_tokens, next_tokens) selects sparse_mode 4 (bottom-right band, the
+    2048 template as mask)."""
     scale = 1.0 / math.sqrt(D + Dr) if scale is None else scale
     ss = _streams(seed)
     lkv = np.asarray(lkv, dtype=np.int64)
@@ -395,10 +397,13 @@ def make_mla_decode(name="custom", *, layout="BSND", dtype=torch.bfloat16, B=2, 
                     t[last, tail:] = float("nan")
     mask = None
     causal = (lq.max() > 1) if layout == "TND" else Sq > 1
-    if causal:
+    if causal or band is not None:
         mask = torch.triu(torch.ones(2048, 2048, dtype=torch.uint8), diagonal=1).to(device)
+    mode = 4 if band is not None else (3 if causal else 0)
+    pre, nxt = band if band is not None else (INT_MAX, INT_MAX)
     return FiaCase(name=name, layout=layout, dtype=dtype, B=B, QN=QN, KVN=1, Sq=Sq,
-                   Skv=cols * block_size, Dqk=D, Dv=D, scale=scale, sparse_mode=3 if causal else 0,
+                   Skv=cols * block_size, Dqk=D, Dv=D, scale=scale, sparse_mode=mode,
+                   pre_tokens=pre, next_tokens=nxt,
                    lq=lq, lkv=lkv, q=q, k=k, v=v, atten_mask=mask,
                    block_table=torch.from_numpy(table).to(device), block_size=block_size,
                    pool_layout=pool_layout, return_lse=return_lse, meta={"NB": NB},
