@@ -165,6 +165,8 @@ struct DecodeArgs {
     int64_t pr_blk;
     int32_t mla_nw;
     int32_t tnd;                   // TND query (MLA): rows q_row0 + t; rows t >= Lq do not exist
+    // MLA: query token t sees keys Lkv - Lq + t + band_lo .. Lkv - Lq + t + band_hi
+    int32_t band_lo, band_hi;
     int32_t v_is_k;                // value is the key tensor itself (V read from the K tile)
 };
 

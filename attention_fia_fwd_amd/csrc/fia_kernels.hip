@@ -1734,10 +1734,15 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_decode(DecodeArgs a)
         const int tq = rq % S, hq = rq / S;
         const float c = fmaxf(fabsf(a.scale_log2), kMinScale);
         const uint32_t qflip = a.scale_log2 < 0.f ? 0x80008000u : 0u;
+        // allowed keys of query token tq: jbase + tq + band_lo <= j <=
+        // jbase + tq + band_hi (sparse_mode 3: (-2^30, 0]; 4: [-pre, next];
+        // 0: open); wave-uniform extremes over the wave's columns decide
+        // which steps evaluate the per-column bounds
         const int jbase = db.lkv - db.lq;
         const int tq_min = (c0 % S) + nh > S ? 0 : c0 % S;
-        const int jmax = a.causal ? jbase + tq : INT32_MAX;
-        const int jmin = a.causal ? jbase + tq_min : INT32_MAX;
+        const int tq_max = (c0 % S) + nh > S ? S - 1 : c0 % S + max(nh, 1) - 1;
+        const int jhi = jbase + tq + a.band_hi, jlo = jbase + tq + a.band_lo;
+        const int jhi_min = jbase + tq_min + a.band_hi, jlo_max = jbase + tq_max + a.band_lo;
 
         // [Q | Q_rope]^T as the B operand: column n, d = 32 s + 8 qd (query
         // tokens at or past the batch's length are not read: in TND they are
@@ -1943,11 +1948,11 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_decode(DecodeArgs a)
                     x[i] = s0[i];
                     x[4 + i] = s1[i];
                 }
-                if (tt0 + ST > t1 || tt0 + ST - 1 > jmin) {
+                if (tt0 + ST > t1 || tt0 + ST - 1 > jhi_min || tt0 < jlo_max) {
 #pragma unroll
                     for (int r = 0; r < 8; ++r) {
                         const int tk = tt0 + 16 * (r >> 2) + 4 * qd + (r & 3);
-                        if (tk >= t1 || tk > jmax) x[r] = -INFINITY;
+                        if (tk >= t1 || tk > jhi || tk < jlo) x[r] = -INFINITY;
                     }
                 }
                 float mt = x[0];

@@ -498,7 +498,12 @@ fia_status fia_get_workspace_size(const fia_tensor* query, const fia_tensor* key
         // (B, 1, KV_S) or (B, 1, 1, KV_S) (atten_mask parameter description;
         // a leading 1 broadcasts); with a paged cache KV_S covers
         // maxBlockNumPerSeq * block_size
-        if (atten_mask) {
+        if (atten_mask && mla && mode == 4) {
+            // MLA sparse_mode 4 at query S 1: the band's 2048 template, not
+            // a per-token mask (its contents are not read)
+            if (!mask_dtype_ok(atten_mask->dtype)) return FIA_ERR_DTYPE;
+            if (!is_template_2048(atten_mask)) return FIA_ERR_SHAPE;
+        } else if (atten_mask) {
             const fia_tensor* m = atten_mask;
             if (!mask_dtype_ok(m->dtype)) return FIA_ERR_DTYPE;
             if (!m->data) return FIA_ERR_NULLPTR;
@@ -526,8 +531,9 @@ fia_status fia_get_workspace_size(const fia_tensor* query, const fia_tensor* key
             for (int64_t x : lq) mla_S = std::max(mla_S, x);
             // TND: sparse_mode 0 without a mask or 3 (checked with the mask above)
             if (mode != 0 && mode != 3) return FIA_ERR_UNSUPPORTED;
-        } else if (mask || (gq.S == 1 && atten_mask) || (gq.S > 1 && mode != 3)) {
-            // S == 1: sparse_mode 0 without a mask; S > 1: sparse_mode 3
+        } else if (mask || (gq.S == 1 && mode != 4 && atten_mask) ||
+                   (gq.S == 1 && mode != 0 && mode != 4) || (gq.S > 1 && mode != 3 && mode != 4)) {
+            // S == 1: sparse_mode 0 without a mask, or 4; S > 1: sparse_mode 3 or 4
             return FIA_ERR_UNSUPPORTED;
         }
         if (mla_S > kDecodeHeads) return FIA_ERR_UNSUPPORTED;
@@ -681,8 +687,15 @@ fia_status fia_get_workspace_size(const fia_tensor* query, const fia_tensor* key
         // quota of the concatenated token stream (a multiple of 16 tokens, so
         // a 16-token sub-tile never crosses a page).
         const int64_t nseg = B * KVN * nhc;
+        // first kv token a batch's rows can see (MLA sparse_mode 4: keys below
+        // Lkv - Lq - pre are outside every row's band), 16-aligned
+        auto first_token = [&](int64_t b) -> int64_t {
+            if (!(mla && mode == 4)) return 0;
+            const int64_t lo = lkv[(size_t)b] - lq[(size_t)b] - std::min<int64_t>(prm->pre_tokens, (int64_t)1 << 40);
+            return std::min(lkv[(size_t)b], std::max<int64_t>(0, lo)) / 16 * 16;
+        };
         int64_t total = 0;
-        for (int64_t b = 0; b < B; ++b) total += lkv[(size_t)b] * KVN * nhc;
+        for (int64_t b = 0; b < B; ++b) total += (lkv[(size_t)b] - first_token(b)) * KVN * nhc;
         const int64_t steps = (total + kDecodeStep - 1) / kDecodeStep;
         // one MLA workgroup per CU (its two stages fill most of the LDS)
         const int64_t W = std::min<int64_t>((int64_t)kNumCUs * (mla ? 1 : kDecodeWavesPerCU), steps);
@@ -707,7 +720,7 @@ fia_status fia_get_workspace_size(const fia_tensor* query, const fia_tensor* key
                 sg.lq = (int32_t)lq[(size_t)b];
                 sg.q_row0 = layout == LAYOUT_TND ? (int32_t)qstart[(size_t)b] : 0;
                 sg.first = (int32_t)pieces.size();
-                for (int64_t t = 0; t < L;) {
+                for (int64_t t = first_token(b); t < L;) {
                     if (remaining < 16) {                  // next wave
                         wave_first.push_back((int32_t)pieces.size());
                         remaining = quota;
@@ -732,6 +745,17 @@ fia_status fia_get_workspace_size(const fia_tensor* query, const fia_tensor* key
         d.n_pieces = (int32_t)pieces.size();
         d.scale_log2 = (float)scale_log2;
         d.mla_nw = (int32_t)nw;
+        // MLA band (bottom-right, relative to Lkv - Lq + t): mode 3 (-2^30, 0],
+        // mode 4 [-pre, next] (clamped to +-2^30), otherwise open
+        const int64_t band_lim = (int64_t)1 << 30;
+        int64_t blo = -band_lim, bhi = band_lim;
+        if (mla && mode == 3) bhi = 0;
+        if (mla && mode == 4) {
+            blo = std::max(-band_lim, std::min(band_lim, -prm->pre_tokens));
+            bhi = std::max(-band_lim, std::min(band_lim, prm->next_tokens));
+        }
+        d.band_lo = (int32_t)blo;
+        d.band_hi = (int32_t)bhi;
         if (mla) {
             d.qr = qr_data;
             d.kr = prm->key_rope->data;

@@ -149,7 +149,9 @@ typedef struct fia_params {
      * keep D = 512.  Provided here: query D 512 and rope D 64, fp16 or bf16
      * (the rope inputs take the query's dtype), layouts BSH / BSND / BNSD
      * (query_rope the query's layout with D = 64), query S 1..16 (S > 1:
-     * sparse_mode 3, S == 1: sparse_mode 0 without a mask), or TND with
+     * sparse_mode 3 or 4, S == 1: sparse_mode 0 without a mask or 4; mode 4
+     * is the bottom-right band pre_tokens / next_tokens, also at S == 1, with
+     * the 2048 template or NULL as atten_mask), or TND with
      * cumulative actual_seq_qlen (1..16 tokens per batch), actual_seq_kvlen
      * holding each batch's own length and sparse_mode 0 (no mask) or 3, Q_N in
      * {1, 2, 4, ..., 128}, KV_N 1, a paged cache (block_table required) with

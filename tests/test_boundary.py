@@ -463,7 +463,11 @@ def test_mla_validation():
     assert code(qn=12) == _abi.FIA_ERR_UNSUPPORTED                  # Q_N a power of two
     assert code(qn=256) == _abi.FIA_ERR_PARAM                        # above the pages' 128
     assert code(S=17, mode=3) == _abi.FIA_ERR_UNSUPPORTED
-    assert code(S=2, mode=0) == _abi.FIA_ERR_UNSUPPORTED            # S > 1: sparse_mode 3
+    assert code(S=2, mode=0) == _abi.FIA_ERR_UNSUPPORTED            # S > 1: sparse_mode 3 or 4
+    assert code(S=1, mode=4, mask=tmpl) == _abi.FIA_OK               # the band, also at S 1
+    assert code(S=4, mode=4, mask=tmpl) == _abi.FIA_OK
+    assert code(S=1, mode=4, mask=torch.zeros(B, 256, dtype=torch.uint8)) == _abi.FIA_ERR_SHAPE
+    assert code(S=1, mode=3) == _abi.FIA_ERR_UNSUPPORTED
     assert code(mask=torch.zeros(B, 256, dtype=torch.uint8)) == _abi.FIA_ERR_UNSUPPORTED
     assert code(kvn=2, k=torch.zeros(4, bs, 2 * D, dtype=torch.bfloat16)) == _abi.FIA_ERR_UNSUPPORTED
 

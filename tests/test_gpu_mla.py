@@ -140,3 +140,34 @@ def test_mla_tnd(case_args):
     out, lse = run(p)
     compare(case, out, lse, *ref)
     p.close()
+
+
+BAND_CASES = [
+    # name, QN, S, block_size, lkv, (pre_tokens, next_tokens), value = key
+    ("band_s1_narrow", 16, 1, 16, [900, 40, 5], (100, 0), False),
+    ("band_s1_n128", 128, 1, 128, [3000, 700], (1000, 0), False),
+    ("band_s4", 16, 4, 16, [600, 3, 70], (50, 0), False),
+    ("band_s2_next", 32, 2, 128, [1500, 200], (300, 1), False),
+    ("band_s1_zero_window", 8, 1, 16, [400, 17], (0, 0), False),
+    ("band_s4_value_is_key", 64, 4, 128, [2500, 90], (700, 0), True),
+]
+
+
+@pytest.mark.parametrize("case_args", BAND_CASES, ids=[c[0] for c in BAND_CASES])
+def test_mla_band(case_args):
+    # sparse_mode 4: token t sees keys Lkv - S + t - pre .. Lkv - S + t + next
+    # (at query S 1 too); keys below every row's window are not loaded
+    name, QN, S, bs, lkv, band, vk = case_args
+    case = W.make_mla_decode(f"mla_{name}", B=len(lkv), QN=QN, Sq=S, lkv=lkv, block_size=bs,
+                             band=band, seed=1290 + QN + S, extra_blocks=2, nan_pool=True)
+    if vk:
+        case.v = case.k
+    say(f"[mla] {case.name} band={band} QN={QN} S={S} bs={bs} lkv={lkv} value=key={vk}")
+    ref = oracle.attention(case)
+    to_dev(case)
+    if vk:
+        case.v = case.k
+    p = fia_plan(case)
+    out, lse = run(p)
+    compare(case, out, lse, *ref)
+    p.close()
