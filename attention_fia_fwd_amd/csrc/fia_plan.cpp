@@ -352,8 +352,10 @@ fia_status fia_get_workspace_size(const fia_tensor* query, const fia_tensor* key
         if (layout != LAYOUT_TND && block_table->dims[0] != gq.B) return FIA_ERR_SHAPE;
         if (prm->block_size <= 0 || prm->block_size % 16 != 0) return FIA_ERR_PARAM;
         if (mla) {
-            // MLA with a query D of 512: block_size 16 or 128
-            if (prm->block_size != 16 && prm->block_size != 128) return FIA_ERR_PARAM;
+            // MLA with a query D of 512: block_size 16 or 128 (64 or 128 with
+            // sparse_mode 4)
+            if (prm->block_size != 16 && prm->block_size != 64 && prm->block_size != 128)
+                return FIA_ERR_PARAM;
         } else if (!decode && (prm->block_size % 128 != 0 || prm->block_size > 512)) {
             return FIA_ERR_PARAM;
         }

@@ -155,7 +155,7 @@ typedef struct fia_params {
      * cumulative actual_seq_qlen (1..16 tokens per batch), actual_seq_kvlen
      * holding each batch's own length and sparse_mode 0 (no mask) or 3, Q_N in
      * {1, 2, 4, ..., 128}, KV_N 1, a paged cache (block_table required) with
-     * block_size 16 or 128 and key_rope a pool of the key's layout with D 64.
+     * block_size 16, 64 or 128 and key_rope a pool of the key's layout with D 64.
      * value is its own pool of the key's shape, or the key tensor itself
      * (same pointer: then the value bytes are not read a second time).
      * softmax_lse is computed as for any other call.  Errors: a rope dtype

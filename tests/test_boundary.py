@@ -456,8 +456,11 @@ def test_mla_validation():
     assert code(qr=torch.zeros(B, QN, 1, 32, dtype=torch.bfloat16)) == _abi.FIA_ERR_SHAPE
     assert code(krope=torch.zeros(4, bs, 32, dtype=torch.bfloat16)) == _abi.FIA_ERR_SHAPE
     assert code(krope=torch.zeros(3, bs, 64, dtype=torch.bfloat16)) == _abi.FIA_ERR_SHAPE
+    assert code(block_size=32, k=torch.zeros(8, 32, D, dtype=torch.bfloat16),
+                krope=torch.zeros(8, 32, 64, dtype=torch.bfloat16)) == _abi.FIA_ERR_PARAM
     assert code(block_size=64, k=torch.zeros(8, 64, D, dtype=torch.bfloat16),
-                krope=torch.zeros(8, 64, 64, dtype=torch.bfloat16)) == _abi.FIA_ERR_PARAM
+                krope=torch.zeros(8, 64, 64, dtype=torch.bfloat16),
+                table=torch.zeros(B, 4, dtype=torch.int32)) == _abi.FIA_OK
     assert code(table=None, block_size=0, k=torch.zeros(B, 1, 200, D, dtype=torch.bfloat16),
                 krope=torch.zeros(B, 1, 200, 64, dtype=torch.bfloat16)) == _abi.FIA_ERR_UNSUPPORTED
     assert code(qn=12) == _abi.FIA_ERR_UNSUPPORTED                  # Q_N a power of two

@@ -150,6 +150,7 @@ BAND_CASES = [
     ("band_s2_next", 32, 2, 128, [1500, 200], (300, 1), False),
     ("band_s1_zero_window", 8, 1, 16, [400, 17], (0, 0), False),
     ("band_s4_value_is_key", 64, 4, 128, [2500, 90], (700, 0), True),
+    ("band_s1_bs64", 128, 1, 64, [2000, 130, 64], (500, 0), False),
 ]
 
 
