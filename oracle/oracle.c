@@ -68,7 +68,8 @@
  * their rope parts (width Dr, laid out like query and key with D = Dr), so
  *   s_j = scale * (sum_d q[b,h,i,d] k[b,g,j,d] + sum_r qr[b,h,i,r] kr[b,g,j,r]);
  * value and output keep D = Dv.  (The pages state the inputs and their
- * shapes, not a formula for the rope parts; concatenation is the reading.)
+ * shapes, not a formula for the rope parts; concatenation is the reading:
+ * parity unpinned against the pages.)
  * With sparse_mode 4 the bottom-right band of the mode list applies at query
  * S 1 too (the MLA constraints list that mode for S 1).
  */
