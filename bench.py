@@ -242,7 +242,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="c2")
+    ap.add_argument("--workload", default="c2",
+                    help="headline workload (c2) or one of: c1, c3, c4, c5, paged_prefill, mtp_decode, "
+                         "int8_decode, fp8_bsa, mla_decode, mla_shared_kv")
     ap.add_argument("--secondary", default="c1,c3,c4,c5,paged_prefill,mtp_decode,int8_decode,fp8_bsa,mla_decode,mla_shared_kv",
                     help="comma list of other workloads to time ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
