@@ -678,6 +678,40 @@ def test_int8_kv_unit_scale_is_the_raw_integers():
     np.testing.assert_array_equal(lse, rl)
 
 
+@pytest.mark.parametrize("pool_layout", [0, 1])
+@pytest.mark.parametrize("kmode, vmode", [(0, 0), (1, 1), (0, 1)])
+def test_paged_int8_kv_equals_contiguous_after_gather(pool_layout, kmode, vmode):
+    # page attention with an int8 cache (v2 page, query S 1 page attention
+    # scenario: int8 key/value allowed): the paged oracle equals the
+    # contiguous int8 oracle on the gathered pool, with the same per-channel
+    # or per-token (logical kv position) scales and offsets, bit for bit
+    case = W.make_quant_decode(layout="BNSD", B=3, QN=4, KVN=2, D=16, lkv=[70, 5, 64],
+                               kmode=kmode, vmode=vmode, block_size=32, pool_layout=pool_layout,
+                               extra_blocks=2, seed=80 + 2 * kmode + vmode + 4 * pool_layout)
+    out, lse = oracle.attention(case)
+    kc, vc = _gather_pool(case)
+    cont = W.make_quant_decode(layout="BNSD", B=3, QN=4, KVN=2, D=16, lkv=[70, 5, 64],
+                               Skv=kc.shape[2], kmode=kmode, vmode=vmode, seed=0)
+    cont.q, cont.k, cont.v = case.q, kc, vc
+    cont.quant = dict(case.quant)
+    oc, lc = oracle.attention(cont)
+    np.testing.assert_array_equal(out, oc)
+    np.testing.assert_array_equal(lse, lc)
+    # and with power-of-two scales, the bf16 oracle on the dequantized pool
+    case2 = W.make_quant_decode(layout="BNSD", B=3, QN=4, KVN=2, D=16, lkv=[70, 5, 64],
+                                kmode=kmode, vmode=vmode, block_size=32, pool_layout=pool_layout,
+                                pow2=True, seed=90 + 2 * kmode + vmode + 4 * pool_layout)
+    kc2, vc2 = _gather_pool(case2)
+    cont2 = W.make_quant_decode(layout="BNSD", B=3, QN=4, KVN=2, D=16, lkv=[70, 5, 64],
+                                Skv=kc2.shape[2], kmode=kmode, vmode=vmode, seed=0)
+    cont2.q, cont2.k, cont2.v = case2.q, kc2, vc2
+    cont2.quant = dict(case2.quant)
+    out2, lse2 = oracle.attention(case2)
+    ro, rl = oracle.attention(_dequantized(cont2))
+    np.testing.assert_array_equal(out2, ro)
+    np.testing.assert_array_equal(lse2, rl)
+
+
 def test_int8_kv_multi_token_causal():
     case = W.make_quant_decode(layout="BNSD", B=2, QN=4, KVN=2, D=16, Sq=3, lkv=[20, 2],
                                kmode=0, vmode=1, pow2=True, sparse_mode=3, seed=76)

@@ -412,19 +412,39 @@ def make_mla_decode(name="custom", *, layout="BSND", dtype=torch.bfloat16, B=2, 
 
 def make_quant_decode(name="custom", *, layout="BNSD", B=2, QN=4, KVN=2, D=64, Sq=1, Skv=None,
                       lkv=(100, 37), kmode=0, vmode=0, offsets=True, sparse_mode=0, scale=None,
-                      seed=0, device="cpu", pow2=False, unit=False, return_lse=True) -> FiaCase:
+                      seed=0, device="cpu", pow2=False, unit=False, return_lse=True,
+                      block_size=0, pool_layout=0, extra_blocks=0) -> FiaCase:
     """Decode (query S <= 16) against an int8 KV cache (kv pseudo-quantization):
     bf16 query, int8 key/value uniform in [-127, 127], each value standing for
     scale * (x + offset).  Mode 0 (per channel): bf16 scale ~ U[0.004, 0.02],
     offset ~ U[-8, 8], shape [KV_N, D]; mode 1 (per token): fp32, shape
     [B, KV_S].  ``pow2``: scales 2^-k (k in 5..7) and integer offsets (the
-    dequantized cache is then exact in bf16); ``unit``: scale 1, offset 0."""
+    dequantized cache is then exact in bf16); ``unit``: scale 1, offset 0.
+    ``block_size`` > 0: K/V are int8 pools (NB, KV_N, bs, D) (``pool_layout``
+    0) or (NB, bs, KV_N * D) (1) addressed through a block table holding a
+    seeded permutation of the pool's block ids (unused entries -1); KV_S of
+    the per-token scales is then cols * bs."""
     scale = 1.0 / math.sqrt(D) if scale is None else scale
     ss = _streams(seed)
     lkv = np.asarray(lkv, dtype=np.int64)
-    Skv = int(lkv.max()) if Skv is None else Skv
     q = normal_tensor(_shape(layout, B, QN, Sq, D), torch.bfloat16, ss[STREAM_Q], device)
-    kshape = _shape(layout, B, KVN, Skv, D)
+    table = None
+    if block_size:
+        nblk = [(int(L) + block_size - 1) // block_size for L in lkv]
+        NB = sum(nblk) + extra_blocks
+        cols = max(max(nblk), 1)
+        rng = np.random.default_rng(ss[STREAM_TABLE])
+        perm = rng.permutation(NB).astype(np.int32)
+        table = np.full((B, cols), -1, dtype=np.int32)
+        pos = 0
+        for b in range(B):
+            table[b, :nblk[b]] = perm[pos:pos + nblk[b]]
+            pos += nblk[b]
+        Skv = cols * block_size
+        kshape = (NB, KVN, block_size, D) if pool_layout == 0 else (NB, block_size, KVN * D)
+    else:
+        Skv = int(lkv.max()) if Skv is None else Skv
+        kshape = _shape(layout, B, KVN, Skv, D)
     k = int8_tensor(kshape, ss[STREAM_K], device)
     v = int8_tensor(kshape, ss[STREAM_V], device)
     prng = np.random.default_rng(ss[STREAM_MASK])
@@ -453,7 +473,9 @@ def make_quant_decode(name="custom", *, layout="BNSD", B=2, QN=4, KVN=2, D=64, S
         mask = torch.triu(torch.ones(2048, 2048, dtype=torch.uint8), diagonal=1).to(device)
     return FiaCase(name=name, layout=layout, dtype=torch.bfloat16, B=B, QN=QN, KVN=KVN, Sq=Sq,
                    Skv=Skv, Dqk=D, Dv=D, scale=scale, sparse_mode=sparse_mode, lq=None, lkv=lkv,
-                   q=q, k=k, v=v, atten_mask=mask, return_lse=return_lse, quant=quant)
+                   q=q, k=k, v=v, atten_mask=mask, return_lse=return_lse, quant=quant,
+                   block_table=None if table is None else torch.from_numpy(table).to(device),
+                   block_size=block_size, pool_layout=pool_layout)
 
 
 def make_bsa(name="custom", *, layout="BNSD", dtype=torch.bfloat16, B=1, QN=2, KVN=1,
