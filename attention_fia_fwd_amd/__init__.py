@@ -17,6 +17,7 @@ Argument names and defaults follow the parameter description of
 from __future__ import annotations
 
 import ctypes
+import time
 from typing import Optional, Sequence
 
 import numpy as np
@@ -73,16 +74,6 @@ def _host_i64(x):
 
 def _stream_handle(device: torch.device) -> int:
     return torch.cuda.current_stream(device).cuda_stream
-
-
-def _out_shapes(query, value, layout, num_heads, block_table):
-    if block_table is not None:
-        Dv = value.shape[-1] if value.dim() == 4 else None
-        if Dv is None:
-            kvn_d = value.shape[-1]
-            return None, kvn_d
-        return None, Dv
-    return None, None
 
 
 class FiaPlan:
@@ -147,10 +138,12 @@ class FiaPlan:
         p.key_quant_mode, p.value_quant_mode = key_quant_mode, value_quant_mode
         self._rdesc = [describe(t) for t in (query_rope, key_rope)]
         p.query_rope, p.key_rope = [ctypes.pointer(d) if d is not None else None for d in self._rdesc]
-        st, ws, plan = fia_get_workspace_size(describe(query), describe(key), describe(value),
-                                              describe(atten_mask), describe(block_table), p,
-                                              describe(out),
-                                              describe(lse) if return_softmax_lse else None)
+        args = (describe(query), describe(key), describe(value), describe(atten_mask),
+                describe(block_table), p, describe(out),
+                describe(lse) if return_softmax_lse else None)
+        t0 = time.perf_counter()
+        st, ws, plan = fia_get_workspace_size(*args)
+        self.phase1_s = time.perf_counter() - t0     # the C call alone (validation, plan, upload)
         del qa, ka
         if st != FIA_OK:
             raise FiaError(st, "fia_get_workspace_size")
@@ -220,10 +213,11 @@ class BsaPlan:
         p.actual_seq_lengths, p.n_actual_seq_lengths = qp, qn
         p.actual_seq_lengths_kv, p.n_actual_seq_lengths_kv = kp, kn
         p.softmax_lse_flag = 1 if softmax_lse_flag else 0
-        st, ws, plan = bsa_get_workspace_size(describe(query), describe(key), describe(value),
-                                              describe(block_sparse_mask), None, None, p,
-                                              describe(out),
-                                              describe(lse) if softmax_lse_flag else None)
+        args = (describe(query), describe(key), describe(value), describe(block_sparse_mask), None,
+                None, p, describe(out), describe(lse) if softmax_lse_flag else None)
+        t0 = time.perf_counter()
+        st, ws, plan = bsa_get_workspace_size(*args)
+        self.phase1_s = time.perf_counter() - t0     # the C call alone (validation, plan, upload)
         del qa, ka
         if st != FIA_OK:
             raise FiaError(st, "bsa_get_workspace_size")
@@ -244,13 +238,11 @@ class BsaPlan:
         st, co, io, nqb, nkb = bsa_schedule_layout(self.plan)
         if st != FIA_OK:
             raise FiaError(st, "bsa_schedule_layout")
-        n = (io - co) // 4
         rows = self.workspace[co:co + 4 * (self._rows(nqb))].view(torch.int32)
         idx = self.workspace[io:io + 4 * self._rows(nqb) * nkb].view(torch.int32)
         return rows, idx.view(-1, nkb), nqb, nkb
 
     def _rows(self, nqb):
-        q = self._keep[0]
         B = self._keep[3].shape[0]
         N = self._keep[3].shape[1]
         return B * N * nqb

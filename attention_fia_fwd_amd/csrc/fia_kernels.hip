@@ -1346,8 +1346,8 @@ __global__ __launch_bounds__(64) void decode_split(DecodeArgs a)
 }
 
 // ---------------------------------------------------------------------------
-// Decode against an int8 KV cache (kv pseudo-quantization; contiguous KV, as
-// the pages allow it only without page attention).  A cached value x stands
+// Decode against an int8 KV cache (kv pseudo-quantization), contiguous or
+// (query S 1) paged through the block table.  A cached value x stands
 // for scale * (x + offset), per channel (bf16 scale/offset [KV_N * D]) or per
 // token (fp32 [B, KV_S]), K and V each with their own mode.  K bytes are read
 // as u = x + 128 (0..255, exact in bf16) for the bf16 QK MFMAs; V bytes as the
@@ -1470,15 +1470,35 @@ __global__ __launch_bounds__(64) void decode_split_i8(DecodeArgs a)
         const float Cn = quad_sum(cpart);     // K per channel: constant of column n
         const float Qs = quad_sum(qpart);     // K per token: sum_d q_d of column n
 
-        const int64_t tokstride = a.c_tok;
-        const int64_t hoff = db.kv_row0 * a.c_rowmul + (int64_t)kvh * a.c_head;
+        // Contiguous cache, or a paged pool (int8 elements are bytes, so the
+        // pool strides are byte strides); a 16-token sub-tile never crosses a
+        // page (block_size % 32 == 0, pieces 16-aligned).
+        const int64_t tokstride = a.paged ? a.p_tok : a.c_tok;
+        const int64_t hoff = a.paged ? (int64_t)kvh * a.p_head
+                                     : db.kv_row0 * a.c_rowmul + (int64_t)kvh * a.c_head;
         const uint8_t* kbase = (const uint8_t*)a.k + hoff;
         const uint8_t* vbase = (const uint8_t*)a.v + hoff;
+        // the piece's block-table entries (at most 64 pages): lane i holds the
+        // id of page pg_first + i; a sub-tile takes its page id by v_readlane
+        const int bs = a.paged ? a.block_size : 0x40000000;
+        const int32_t* bt = a.paged ? a.block_table + (int64_t)b * a.bt_stride : nullptr;
+        const int pg_first = t0 / bs;
+        const int pg_last = t1 > t0 ? (t1 - 1) / bs : pg_first;
+        const int my_page = (a.paged && pg_first + lane <= pg_last) ? bt[pg_first + lane] : 0;
+        // settle the table load here, not inside the prefetching step loop
+        __builtin_amdgcn_s_waitcnt(FIA_VMCNT(0));
         auto sub_rsrc = [&](const uint8_t* base, int tb) {
             // rows [tb, t1) (at most 16) of the piece; rows past t1 read as zero
             const int nvalid = min(16, t1 - tb);
+            const uint8_t* ptr = base + (int64_t)tb * tokstride;
+            if (a.paged) {
+                const int pg = tb / bs;
+                // a sub-tile past the end reads nothing, not even its table entry
+                const int64_t blk = nvalid > 0 ? __builtin_amdgcn_readlane(my_page, pg - pg_first) : 0;
+                ptr = base + blk * a.p_blk + (int64_t)(tb - pg * bs) * tokstride;
+            }
             const int64_t bytes = nvalid > 0 ? (int64_t)(nvalid - 1) * tokstride + D : 0;
-            return __builtin_amdgcn_make_buffer_rsrc((void*)(base + (int64_t)tb * tokstride), (short)0,
+            return __builtin_amdgcn_make_buffer_rsrc((void*)ptr, (short)0,
                                                      (int)min(bytes, (int64_t)0x7fffffff), 0x00020000);
         };
         const float* ksrow = KM == 1 ? (const float*)a.k_scale + (int64_t)b * a.tok_stride : nullptr;
@@ -2160,9 +2180,9 @@ template <int D>
 void launch_split_i8(const fia_plan& p, const DecodeArgs& a, hipStream_t stream)
 {
     const dim3 g((unsigned)p.n_waves), blk(64);
+    // the mode pairs phase 1 accepts: equal, or key per channel with value per token
     if (a.kmode == 0 && a.vmode == 0) hipLaunchKernelGGL((decode_split_i8<D, 0, 0>), g, blk, 0, stream, a);
     else if (a.kmode == 0) hipLaunchKernelGGL((decode_split_i8<D, 0, 1>), g, blk, 0, stream, a);
-    else if (a.vmode == 0) hipLaunchKernelGGL((decode_split_i8<D, 1, 0>), g, blk, 0, stream, a);
     else hipLaunchKernelGGL((decode_split_i8<D, 1, 1>), g, blk, 0, stream, a);
 }
 

@@ -288,7 +288,6 @@ fia_status fia_get_workspace_size(const fia_tensor* query, const fia_tensor* key
     if (kv_i8) {
         if (value->dtype != FIA_I8 || query->dtype != FIA_BF16) return FIA_ERR_DTYPE;
         if (!prm->dequant_scale_key || !prm->dequant_scale_value) return FIA_ERR_NULLPTR;
-        if (block_table) return FIA_ERR_PARAM;          // no page attention with pseudo-quant
     } else {
         if (key->dtype != query->dtype || value->dtype != query->dtype) return FIA_ERR_DTYPE;
         if (any_quant) return FIA_ERR_PARAM;
@@ -585,10 +584,30 @@ fia_status fia_get_workspace_size(const fia_tensor* query, const fia_tensor* key
     int64_t tok_stride = 0;
     if (kv_i8) {
         if (layout == LAYOUT_TND || gq.S > kDecodeHeads) return FIA_ERR_PARAM;   // query S <= 16
-        if (!dec_kernel || mask) return FIA_ERR_UNSUPPORTED;
+        // key_quant_mode / value_quant_mode (v2 parameter description and the
+        // kv pseudo-quant constraints): 0..5 at query S 1, where the two modes
+        // are equal except key 0 with value 1; only 0 and 1, and equal, at
+        // query S > 1, where page attention is not allowed either.  Block size
+        // with an int8 cache: a multiple of 32 (page attention scenario).
         const int64_t km = prm->key_quant_mode, vm = prm->value_quant_mode;
-        if ((km != 0 && km != 1) || (vm != 0 && vm != 1)) return FIA_ERR_PARAM;
-        // per channel: bf16 [KV_N, D] or [KV_N * D]; per token: fp32 [B, KV_S'], KV_S' >= S_kv
+        if (km < 0 || km > 5 || vm < 0 || vm > 5) return FIA_ERR_PARAM;
+        if (decode) {
+            if (km != vm && !(km == 0 && vm == 1)) return FIA_ERR_PARAM;
+            if (paged && prm->block_size % 32 != 0) return FIA_ERR_PARAM;
+        } else {
+            if (km > 1 || km != vm || paged) return FIA_ERR_PARAM;
+        }
+        // per-tensor / per-head modes and scales managed by page attention
+        if (km > 1) return FIA_ERR_UNSUPPORTED;
+        if (!dec_kernel || mask) return FIA_ERR_UNSUPPORTED;
+        // per channel: bf16 [KV_N, D] or [KV_N * D]; per token: fp32 [B, KV_S'],
+        // KV_S' >= the key's S (paged: the longest kv length), indexed by the
+        // logical kv position
+        int64_t tok_need = Skv;
+        if (paged) {
+            tok_need = 0;
+            for (int64_t x : lkv) tok_need = std::max(tok_need, x);
+        }
         auto check = [&](const fia_tensor* t, int64_t md, int64_t* stride) -> fia_status {
             if (!t->data) return FIA_ERR_NULLPTR;
             if (md == 0) {
@@ -596,7 +615,7 @@ fia_status fia_get_workspace_size(const fia_tensor* query, const fia_tensor* key
                 if (!dims_are(t, {KVN, gq.D}) && !dims_are(t, {KVN * gq.D})) return FIA_ERR_SHAPE;
             } else {
                 if (t->dtype != FIA_F32) return FIA_ERR_DTYPE;
-                if (t->ndim != 2 || t->dims[0] != B || t->dims[1] < Skv) return FIA_ERR_SHAPE;
+                if (t->ndim != 2 || t->dims[0] != B || t->dims[1] < tok_need) return FIA_ERR_SHAPE;
                 *stride = t->dims[1];
             }
             return FIA_OK;
@@ -611,6 +630,11 @@ fia_status fia_get_workspace_size(const fia_tensor* query, const fia_tensor* key
         if ((st = check(prm->dequant_scale_key, km, &ks)) != FIA_OK) return st;
         if ((st = check(prm->dequant_scale_value, vm, &vs)) != FIA_OK) return st;
         if (km == 1 && vm == 1 && ks != vs) return FIA_ERR_SHAPE;
+        // equal modes: the two scales (and the two offsets) take one shape
+        if (km == vm && !same(prm->dequant_scale_key, prm->dequant_scale_value)) return FIA_ERR_SHAPE;
+        if (km == vm && prm->dequant_offset_key && prm->dequant_offset_value &&
+            !same(prm->dequant_offset_key, prm->dequant_offset_value))
+            return FIA_ERR_SHAPE;
         if (prm->dequant_offset_key) {
             if (!prm->dequant_offset_key->data) return FIA_ERR_NULLPTR;
             if (!same(prm->dequant_offset_key, prm->dequant_scale_key)) return FIA_ERR_SHAPE;
@@ -1155,11 +1179,9 @@ static fia_status run_common(void* ws, uint64_t ws_size, fia_plan* p, void* stre
     if (bsa != (p->kind == KIND_BSA) && p->kind != KIND_EMPTY) return FIA_ERR_PARAM;
     if (p->kind == KIND_EMPTY) return FIA_OK;
     if (ws_size < p->workspace_bytes || (!ws && p->workspace_bytes)) return FIA_ERR_WORKSPACE;
-    if (p->tables_bytes && !p->dev_tables) {
-        // phase 1 ran where no device was visible; upload now
-        p->dev_tables = upload_tables(p->host_tables.data(), p->tables_bytes);
-        if (!p->dev_tables) return FIA_ERR_HIP;
-    }
+    // phase 1 ran where no device was visible: there is no schedule on a
+    // device, and phase 2 neither allocates nor copies
+    if (p->tables_bytes && !p->dev_tables) return FIA_ERR_HIP;
     unsigned char* w = (unsigned char*)ws;
     const unsigned char* tb = (const unsigned char*)p->dev_tables;
     int rc = 0;

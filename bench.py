@@ -2,28 +2,36 @@
 """Benchmark of the MI355X fused inference attention forward.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2]
-                    [--secondary c1,c3,c4,c5,paged_prefill,mtp_decode,int8_decode,fp8_bsa,mla_decode,mla_shared_kv]
+                    [--secondary c1,c3,c4,c5,paged_prefill,mtp_decode,int8_decode,...]
 
 One step is one fia_run (phase 2) of the headline workload: the GQA causal
 prefill, bf16, B=4, Q_N=32, KV_N=8, max S=4096, D=128, BSND, per-batch
 lengths uniform in [1024, 4096] (seeded).  Inputs are resident in HBM before
 the timed region; the plan (phase 1, host validation + schedule upload) is
-built once and its host time is reported separately.  `value` is
-algorithmic TFLOP/s: 2 * (D_qk + D_v) flops per allowed (query, key) pair,
-pairs counted exactly from the lengths and the mask mode (masked pairs and
-skipped tiles are not counted).
+built once and the C planner call's own time is reported separately
+(`phase1_us`), beside the wrapper's time with torch's allocations of the
+outputs and workspace.  `value` is algorithmic TFLOP/s: 2 * (D_qk + D_v)
+flops per allowed (query, key) pair, pairs counted exactly from the lengths
+and the mask mode (masked pairs and skipped tiles are not counted).  The
+headline's input tensors (205 MB with padding; the valid rows read are 98 MB)
+fit in the 256 MB MALL (Infinity Cache), so repeated runs read them from
+there rather than from HBM; each line states its input tensor bytes and
+whether they fit.
 
 The other workloads (dense causal fp16 prefill, paged GQA decode, varlen TND
 prefill, block-sparse prefill, chunked prefill against a paged cache,
-multi-token decode against a paged cache, decode against an int8 KV cache,
-block-sparse prefill with FP8 inputs) are
+multi-token decode against a paged cache, decode against a contiguous and a
+paged int8 KV cache, block-sparse prefill with FP8 inputs, MLA decode) are
 timed the same way and reported under "secondary"; the decode lines are in
 GB/s of algorithmic bytes (every KV byte of every kv head once, plus q, out,
 lse, the block-table entries and the dequant scales read).
 
 The JSON line carries the roofline of the headline kernel (achieved from HIP
 events on the stream the kernel runs on) and the fp64 CPU oracle timed on a
-bounded sample of the same workload on this host.
+bounded sample of the same workload on this host (`cpu_baseline`), plus the
+oracle on a sample of the paged decode workload in GB/s with all host
+threads and with one, and the smallest prefill workload on one thread
+(`cpu_baseline_more`).
 """
 from __future__ import annotations
 
@@ -155,12 +163,46 @@ def time_plan(plan, steps: int, warmup: int):
 
 
 def build_plan(name, case):
+    """Phase 1 on the case, twice: the first plan of a process also pays
+    one-time set-up (the code object's load on the device); the second is
+    what a caller that re-plans every step pays.  Returns the second plan,
+    its C planner call's own time (validation, schedule, the synchronous
+    upload of the schedule), the whole wrapper's time (which adds torch's
+    allocations of out, lse and workspace) and the first call's C time."""
     from fia_gpu import bsa_plan, fia_plan, to_dev
     to_dev(case)
+    make = bsa_plan if name in ("c5", "fp8_bsa") else fia_plan
+    first = make(case)
+    first_us = first.phase1_s * 1e6
+    first.close()
     t0 = time.perf_counter()
-    plan = bsa_plan(case) if name in ("c5", "fp8_bsa") else fia_plan(case)
+    plan = make(case)
     t1 = time.perf_counter()
-    return plan, (t1 - t0) * 1e6
+    return plan, plan.phase1_s * 1e6, (t1 - t0) * 1e6, first_us
+
+
+DECODE_WORKLOADS = ("c3", "mtp_decode", "int8_decode", "int8_paged_decode", "mla_decode", "mla_shared_kv")
+MALL_BYTES = 256 << 20        # MI355X Infinity Cache (MALL)
+
+
+def input_bytes(case) -> int:
+    """Bytes of every input tensor of the run (q, k, v, pools, tables, masks,
+    scales; padding rows included), for the statement of what fits in the
+    MALL."""
+    import torch
+    n = 0
+    for t in (case.q, case.k, case.v, getattr(case, "atten_mask", None),
+              getattr(case, "block_table", None), getattr(case, "block_mask", None)):
+        if t is not None:
+            n += t.numel() * t.element_size()
+    if getattr(case, "meta", {}).get("v_is_k"):
+        n -= case.v.numel() * case.v.element_size()
+    for extra in ("quant", "fp8", "rope"):
+        d = getattr(case, extra, None) or {}
+        for t in d.values():
+            if isinstance(t, torch.Tensor):
+                n += t.numel() * t.element_size()
+    return n
 
 
 def measure(name, steps, warmup):
@@ -168,11 +210,15 @@ def measure(name, steps, warmup):
     import workloads as W
     case = W.WORKLOADS[name](device="cuda")
     torch.cuda.synchronize()
-    plan, phase1_us = build_plan(name, case)
+    plan, phase1_us, plan_total_us, first_us = build_plan(name, case)
     wall, ev = time_plan(plan, steps, warmup)
+    inb = input_bytes(case)
     res = {"workload": case.name, "steps": steps, "ms_per_step": wall * 1e3,
-           "kernel_ms": ev * 1e3, "phase1_us": round(phase1_us, 1)}
-    if name in ("c3", "mtp_decode", "int8_decode", "mla_decode", "mla_shared_kv"):
+           "kernel_ms": ev * 1e3, "phase1_us": round(phase1_us, 1),
+           "plan_with_allocations_us": round(plan_total_us, 1),
+           "phase1_first_in_process_us": round(first_us, 1), "input_tensor_bytes": inb,
+           "inputs_fit_mall": inb <= MALL_BYTES}
+    if name in DECODE_WORKLOADS:
         nbytes = decode_bytes(case)
         res.update(value=nbytes / wall / 1e9, unit="GB/s", algorithmic_bytes=nbytes,
                    roofline={"bound": "hbm", "achieved": nbytes / ev / 1e9, "peak": PEAK_HBM_GBS,
@@ -198,6 +244,72 @@ def measure(name, steps, warmup):
     del case
     torch.cuda.empty_cache()
     return res
+
+
+def cpu_baseline_decode(name="c3", target_s=8.0, threads=None, case=None):
+    """The fp64 oracle on a seeded sample of (batch, head) rows of a decode
+    workload; each row is credited with its share of the workload's
+    algorithmic bytes (its kv head's cache divided over the G heads that
+    share it, plus its q / out / lse bytes and table entries), so the rate is
+    in the GB/s of the decode metric."""
+    import numpy as np
+    import oracle
+    import workloads as W
+    case = case if case is not None else W.WORKLOADS[name](device="cpu")
+    total = decode_bytes(case)
+    rows_all = case.B * case.QN
+    lkv = case.lkv.astype(np.int64)
+    G = case.QN // case.KVN
+    per_b = lkv * case.KVN * (case.Dqk + case.Dv) * case.k.element_size()  # cache bytes of batch b
+    # share of each row: its batch's cache / QN (= kv head cache / G), rest evenly
+    rest = (total - int(per_b.sum())) / rows_all
+    rng = np.random.default_rng(98)
+    before = oracle.num_threads()
+    if threads:
+        oracle.set_threads(threads)
+    used = oracle.num_threads()
+    try:
+        def rows_of(n):
+            return [(int(rng.integers(case.B)), int(rng.integers(case.QN)), 0) for _ in range(n)]
+
+        def bytes_of(rows):
+            return sum(per_b[b] / case.QN + rest for b, _, _ in rows)
+
+        pilot = rows_of(32)
+        t0 = time.perf_counter()
+        oracle.attention(case, rows=pilot)
+        dt = time.perf_counter() - t0
+        n = int(min(rows_all * 4, max(32, 32 * target_s / max(dt, 1e-3))))
+        rows = rows_of(n)
+        t0 = time.perf_counter()
+        oracle.attention(case, rows=rows)
+        dt = time.perf_counter() - t0
+    finally:
+        oracle.set_threads(before)
+    return {"value": float(bytes_of(rows) / dt / 1e9), "unit": "GB/s", "cores": used, "kind": "oracle",
+            "seconds": round(dt, 2), "G": G,
+            "sample": f"{n} seeded random (batch, head) rows of {case.name}, fp64, "
+                      f"each credited with its share of the algorithmic bytes"}
+
+
+def cpu_baseline_c1_single_thread():
+    """The fp64 oracle on the whole dense causal fp16 workload, one thread."""
+    import oracle
+    import workloads as W
+    case = W.WORKLOADS["c1"](device="cpu")
+    before = oracle.num_threads()
+    oracle.set_threads(1)
+    try:
+        reps, t0 = 0, time.perf_counter()
+        while reps < 3 or time.perf_counter() - t0 < 1.0:
+            oracle.attention(case)
+            reps += 1
+        dt = (time.perf_counter() - t0) / reps
+    finally:
+        oracle.set_threads(before)
+    flops = 2 * (case.Dqk + case.Dv) * allowed_pairs_fia(case)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+            "ms_per_run": round(dt * 1e3, 3), "sample": f"the whole of {case.name}, {reps} runs"}
 
 
 def cpu_baseline(name="c2", target_s=15.0):
@@ -244,8 +356,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="c2",
                     help="headline workload (c2) or one of: c1, c3, c4, c5, paged_prefill, mtp_decode, "
-                         "int8_decode, fp8_bsa, mla_decode, mla_shared_kv")
-    ap.add_argument("--secondary", default="c1,c3,c4,c5,paged_prefill,mtp_decode,int8_decode,fp8_bsa,mla_decode,mla_shared_kv",
+                         "int8_decode, int8_paged_decode, fp8_bsa, mla_decode, mla_shared_kv")
+    ap.add_argument("--secondary", default="c1,c3,c4,c5,paged_prefill,mtp_decode,int8_decode,int8_paged_decode,fp8_bsa,mla_decode,mla_shared_kv",
                     help="comma list of other workloads to time ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -268,10 +380,10 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"calibrate_copy_bytes": n}))
         return
-    from attention_fia_fwd_amd import _abi
-    if not os.path.exists(_abi.LIB_PATH):
-        from attention_fia_fwd_amd.build import build
-        build()
+    # rebuild when a source is newer than the library, so a stale binary is
+    # never measured
+    from attention_fia_fwd_amd.build import build
+    build(force=False)
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     props = torch.cuda.get_device_properties(0)
 
@@ -282,6 +394,14 @@ def main():
         print(f"# {name}: {json.dumps(secondary[name])}", file=sys.stderr, flush=True)
 
     cpu = None if args.no_cpu_baseline else cpu_baseline(args.workload if args.workload in ("c2",) else "c2")
+    cpu_more = None
+    if not args.no_cpu_baseline:
+        import workloads as W
+        c3 = W.WORKLOADS["c3"](device="cpu")
+        cpu_more = {"c3": cpu_baseline_decode("c3", case=c3),
+                    "c3_single_thread": cpu_baseline_decode("c3", target_s=4.0, threads=1, case=c3),
+                    "c1_single_thread": cpu_baseline_c1_single_thread()}
+        print(f"# cpu baselines: {json.dumps(cpu_more)}", file=sys.stderr, flush=True)
     is_decode = args.workload == "c3"
     line = {
         "metric": "prefill TFLOP/s (% bf16 MFMA peak); paged decode KV GB/s (% HBM peak)",
@@ -298,10 +418,15 @@ def main():
         "data": "synthetic (seeded N(0,1) inputs of the workload's shapes and length mix)",
         "config": {"workload": head["workload"], "kernel_ms": head["kernel_ms"],
                    "phase1_us": head["phase1_us"],
+                   "plan_with_allocations_us": head["plan_with_allocations_us"],
+                   "phase1_first_in_process_us": head["phase1_first_in_process_us"],
+                   "input_tensor_bytes": head["input_tensor_bytes"],
+                   "inputs_resident_in_mall": head["inputs_fit_mall"],
                    "device": getattr(props, "gcnArchName", props.name),
                    "compute_units": props.multi_processor_count},
         "roofline": head["roofline"],
         "cpu_baseline": cpu,
+        "cpu_baseline_more": cpu_more,
         "secondary": secondary,
     }
     if is_decode:

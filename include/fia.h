@@ -34,8 +34,8 @@
  *     (per-batch offsets and the tile / split order, tens of bytes per tile)
  *     into device memory the plan owns, on the current device, with a
  *     synchronous copy; fia_plan_destroy frees them.  Where no device is
- *     visible, phase 1 still validates and sizes, and the upload happens at
- *     the first run.
+ *     visible, phase 1 still validates and sizes, but the plan cannot run:
+ *     phase 2 then returns FIA_ERR_HIP (it never uploads or allocates).
  *   - Phase 2 only enqueues kernels on `stream` (a hipStream_t; NULL = the
  *     default stream): it allocates nothing, copies nothing and does not
  *     synchronize.  The workspace holds scratch of one run (decode partial
@@ -126,13 +126,20 @@ typedef struct fia_params {
     const int64_t* actual_seq_kvlen;
     int64_t        n_actual_seq_kvlen;
     /* KV pseudo-quantization (kv pseudo-quant parameters and their
-     * constraints, v2 page): int8 key and value with a bf16 query and output,
-     * a contiguous KV cache (no block_table) and query S <= 16 (S > 1:
-     * sparse_mode 3, or 0 without a mask, with G * S <= 16).  A cached value x
-     * stands for scale * (x + offset).  key_quant_mode / value_quant_mode:
+     * constraints, v2 page): int8 key and value with a bf16 query and output
+     * and query S <= 16 (S > 1: sparse_mode 3, or 0 without a mask, with
+     * G * S <= 16, contiguous KV only).  At query S 1 the cache may also be
+     * paged (block_table, block_size a multiple of 32, either pool layout;
+     * page attention scenario of the query S 1 constraints).  A cached value
+     * x stands for scale * (x + offset).  key_quant_mode / value_quant_mode:
      *   0  per channel: scale / offset bf16 [KV_N, D] or [KV_N * D];
-     *   1  per token:   scale / offset fp32 [B, KV_S'] with KV_S' >= the
-     *      key's S (both per token: one shape for key and value).
+     *   1  per token:   scale / offset fp32 [B, KV_S'], indexed by the
+     *      logical kv position, KV_S' >= the key's S (paged: >= the longest
+     *      actual_seq_kvlen); both per token: one shape for key and value.
+     * The two modes must be equal, except key 0 with value 1 at query S 1
+     * (FIA_ERR_PARAM otherwise); modes 2..5 (per tensor / per head, and the
+     * scales managed by page attention) are legal at query S 1 and return
+     * FIA_ERR_UNSUPPORTED; at query S > 1 only 0 and 1 are legal.
      * Offsets are optional (NULL = 0) and take their scale's shape and dtype.
      * Both scales are required for int8 key/value and must be NULL for
      * fp16/bf16 key/value (FIA_ERR_PARAM).  The plan keeps the pointers. */

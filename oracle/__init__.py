@@ -78,6 +78,8 @@ def lib():
         _lib.oracle_read_half.restype = ctypes.c_double
         _lib.oracle_read_half.argtypes = [ctypes.c_uint16, ctypes.c_int]
         _lib.oracle_num_threads.restype = ctypes.c_int
+        _lib.oracle_set_threads.argtypes = [ctypes.c_int]
+        _lib.oracle_set_threads.restype = None
         _lib.oracle_read_e4m3fn.restype = ctypes.c_double
         _lib.oracle_read_e4m3fn.argtypes = [ctypes.c_uint8]
     return _lib
@@ -85,6 +87,11 @@ def lib():
 
 def num_threads() -> int:
     return lib().oracle_num_threads()
+
+
+def set_threads(n: int) -> None:
+    """Threads of the oracle's loops over output rows (for timing)."""
+    lib().oracle_set_threads(int(n))
 
 
 def read_half(bits: int, dtype: torch.dtype) -> float:

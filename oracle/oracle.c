@@ -425,6 +425,18 @@ int oracle_bsa_compact(const uint8_t* mask, int64_t B, int64_t N, int64_t nqb, i
     return 0;
 }
 
+/* Threads of the OpenMP loops over output rows (n >= 1); a timing knob only. */
+void oracle_set_threads(int n)
+{
+#ifdef _OPENMP
+    extern void omp_set_num_threads(int);
+    if (n >= 1)
+        omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 int oracle_num_threads(void)
 {
 #ifdef _OPENMP

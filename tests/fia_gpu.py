@@ -158,3 +158,40 @@ def gather_rows(case, out, lse, rows):
             go.append(o[b, i, h])
             gl.append(l[b, h, i] if l is not None else 0)
     return np.array(go), np.array(gl)
+
+
+def head_rows(case, heads, batches=None):
+    """Every (b, h, i) of the given query heads (and batches, default all):
+    whole heads of the output, each row below its batch's query length."""
+    lq = np.ones(case.B, dtype=np.int64) if getattr(case, "decode", False) else (
+        case.lq if case.lq is not None else np.full(case.B, case.Sq))
+    bs = range(case.B) if batches is None else batches
+    return [(b, h, i) for b in bs for h in heads for i in range(int(lq[b]))]
+
+
+def seeded_subset(n, k, seed):
+    """k distinct indices of range(n), sorted, from a seeded generator."""
+    rng = np.random.default_rng(seed)
+    return sorted(int(x) for x in rng.choice(n, size=min(k, n), replace=False))
+
+
+def compare_rows(case, out, lse, rows, ref_o, ref_l, dtype=None):
+    """Element-wise comparison of the listed rows (ref_o [n, Dv], ref_l [n])
+    at the output / LSE tolerances; +inf rows must match exactly and hold
+    out = 0.  Returns (max out err, max lse err)."""
+    dtype = dtype or case.dtype
+    if dtype == torch.float8_e4m3fn:
+        dtype = torch.bfloat16
+    go, gl = gather_rows(case, out, lse, rows)
+    assert np.all(np.isfinite(go)), "non-finite output"
+    err = float(np.max(np.abs(go - ref_o))) if go.size else 0.0
+    assert err <= TOL_OUT[dtype], f"{case.name}: max |out - oracle| = {err}"
+    lerr = 0.0
+    if lse is not None:
+        inf_ref = np.isinf(ref_l)
+        assert np.array_equal(np.isposinf(gl), inf_ref), f"{case.name}: +inf rows differ"
+        if (~inf_ref).any():
+            lerr = float(np.max(np.abs(gl[~inf_ref] - ref_l[~inf_ref])))
+        assert lerr <= TOL_LSE, f"{case.name}: max |lse - oracle| = {lerr}"
+        assert np.all(go[inf_ref] == 0)
+    return err, lerr

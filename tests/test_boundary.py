@@ -266,7 +266,7 @@ def test_int8_kv_validation():
             lk = np.array([S, S], dtype=np.int64)
             keep.append(lk)
             p.actual_seq_kvlen, p.n_actual_seq_kvlen = lk.ctypes.data, 2
-        return _phase1(q, k, k, p, bt=bt)[0]
+        return _phase1(q, k, k, p, bt=bt, out=torch.zeros(q.shape, dtype=torch.bfloat16))[0]
 
     assert code() == _abi.FIA_OK
     assert code(ks=tok, vs=tok, km=1, vm=1) == _abi.FIA_OK
@@ -274,20 +274,47 @@ def test_int8_kv_validation():
     assert code(ks=ch.reshape(-1), vs=ch.reshape(-1)) == _abi.FIA_OK
     assert code(q=q.half()) == _abi.FIA_ERR_DTYPE                 # query must be bf16
     assert code(ks=None) == _abi.FIA_ERR_NULLPTR
+    # mode pairs (key_quant_mode description): equal, or key 0 with value 1
     assert code(km=2) == _abi.FIA_ERR_PARAM
+    assert code(ks=tok, km=1) == _abi.FIA_ERR_PARAM               # key 1 with value 0
+    assert code(km=6, vm=6) == _abi.FIA_ERR_PARAM
+    assert code(km=-1, vm=-1) == _abi.FIA_ERR_PARAM
+    # per tensor / per head, and scales managed by page attention: legal at
+    # query S 1, not provided
+    for m in (2, 3, 4, 5):
+        assert code(km=m, vm=m) == _abi.FIA_ERR_UNSUPPORTED, m
     assert code(ks=ch.float()) == _abi.FIA_ERR_DTYPE              # per channel: bf16
-    assert code(ks=tok.to(torch.bfloat16), km=1) == _abi.FIA_ERR_DTYPE
+    assert code(ks=tok.to(torch.bfloat16), vs=tok, km=1, vm=1) == _abi.FIA_ERR_DTYPE
     assert code(ks=torch.ones(KVN, D + 1, dtype=torch.bfloat16)) == _abi.FIA_ERR_SHAPE
-    assert code(ks=torch.ones(B, S - 1), km=1) == _abi.FIA_ERR_SHAPE
+    assert code(ks=torch.ones(B, S - 1), vs=tok, km=1, vm=1) == _abi.FIA_ERR_SHAPE
     assert code(ks=tok, vs=torch.ones(B, S + 3), km=1, vm=1) == _abi.FIA_ERR_SHAPE
     assert code(ko=torch.ones(KVN, D)) == _abi.FIA_ERR_SHAPE      # offset: its scale's dtype
-    # no page attention with pseudo-quant
-    pool = torch.zeros(2, KVN, 128, D, dtype=torch.int8)
-    assert code(k=pool, bt=torch.zeros(B, 1, dtype=torch.int32), block_size=128) == _abi.FIA_ERR_PARAM
+    # page attention with an int8 cache at query S 1 (block size 32-aligned),
+    # either pool layout; per-token scales cover the longest kv length
+    bt = torch.zeros(B, 2, dtype=torch.int32)
+    for pool in (torch.zeros(4, KVN, 32, D, dtype=torch.int8), torch.zeros(4, 32, KVN * D, dtype=torch.int8)):
+        assert code(k=pool, bt=bt, block_size=32) == _abi.FIA_OK
+        assert code(k=pool, bt=bt, block_size=32, ks=tok, vs=tok, km=1, vm=1) == _abi.FIA_OK
+        assert code(k=pool, bt=bt, block_size=32, vs=tok, vm=1) == _abi.FIA_OK
+        assert code(k=pool, bt=bt, block_size=32, ks=tok[:, :S - 1].contiguous(), vs=tok[:, :S - 1].contiguous(),
+                    km=1, vm=1) == _abi.FIA_ERR_SHAPE
+    pool16 = torch.zeros(6, KVN, 16, D, dtype=torch.int8)
+    assert code(k=pool16, bt=torch.zeros(B, 3, dtype=torch.int32), block_size=16) == _abi.FIA_ERR_PARAM
     # query S <= 16; G * S > 16 is not provided
     assert code(q=torch.zeros(B, QN, 17, D, dtype=torch.bfloat16), mode=3) == _abi.FIA_ERR_PARAM
     assert code(q=torch.zeros(B, QN, 5, D, dtype=torch.bfloat16), mode=3) == _abi.FIA_ERR_UNSUPPORTED
-    assert code(q=torch.zeros(B, QN, 2, D, dtype=torch.bfloat16), mode=3) == _abi.FIA_OK
+    q2 = torch.zeros(B, QN, 2, D, dtype=torch.bfloat16)
+    assert code(q=q2, mode=3) == _abi.FIA_OK
+    assert code(q=q2, ks=tok, vs=tok, km=1, vm=1, mode=3) == _abi.FIA_OK
+    # query S > 1: modes equal (key 0 with value 1 is a query S 1 exception),
+    # 0 or 1 only, and no page attention
+    assert code(q=q2, vs=tok, vm=1, mode=3) == _abi.FIA_ERR_PARAM
+    assert code(q=q2, km=2, vm=2, mode=3) == _abi.FIA_ERR_PARAM
+    pool128 = torch.zeros(2, KVN, 128, D, dtype=torch.int8)
+    assert code(q=q2, k=pool128, bt=torch.zeros(B, 1, dtype=torch.int32), block_size=128,
+                mode=3) == _abi.FIA_ERR_PARAM
+    # equal modes: one shape for the two scales
+    assert code(vs=ch.reshape(-1)) == _abi.FIA_ERR_SHAPE
     # dequant tensors with fp16/bf16 key/value
     kb = torch.zeros(B, KVN, S, D, dtype=torch.bfloat16)
     assert code(k=kb) == _abi.FIA_ERR_PARAM
@@ -372,6 +399,23 @@ def test_run_rejects_small_workspace_without_touching_the_gpu():
     assert fia.fia_run(1 << 20, ws - 1, plan, 0) == _abi.FIA_ERR_WORKSPACE
     # a fused-attention plan is not a block-sparse plan
     assert fia.bsa_run(1 << 20, ws, plan, 0) == _abi.FIA_ERR_PARAM
+    fia.fia_plan_destroy(plan)
+
+
+def test_run_without_a_device_at_phase1_fails_without_allocating():
+    # phase 1 with no device visible validates and sizes but uploads no
+    # schedule; phase 2 then returns FIA_ERR_HIP instead of allocating
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a device is visible: phase 1 uploads the schedule")
+    B, QN, KVN, D = 2, 8, 2, 128
+    q = torch.zeros(B, QN, 1, D, dtype=torch.bfloat16)
+    k = torch.zeros(B, KVN, 5000, D, dtype=torch.bfloat16)
+    p = _params(num_heads=QN, num_key_value_heads=KVN)
+    o = torch.zeros_like(q)
+    st, ws, plan = fia.fia_get_workspace_size(fia.describe(q), fia.describe(k), fia.describe(k),
+                                              None, None, p, fia.describe(o), None)
+    assert st == _abi.FIA_OK and ws > 0
+    assert fia.fia_run(1 << 20, ws, plan, 0) == _abi.FIA_ERR_HIP
     fia.fia_plan_destroy(plan)
 
 
@@ -528,7 +572,7 @@ def test_product_path_does_not_touch_the_oracle():
                 if isinstance(node, (ast.Import, ast.ImportFrom)):
                     names = [a.name for a in node.names] + [getattr(node, "module", None) or ""]
                     if "oracle" in names:
-                        assert fn.name == "cpu_baseline", fn.name
+                        assert fn.name.startswith("cpu_baseline"), fn.name
     top = [n for n in tree.body if isinstance(n, (ast.Import, ast.ImportFrom))]
     assert not any("oracle" in [a.name for a in n.names] + [getattr(n, "module", None) or ""] for n in top)
 

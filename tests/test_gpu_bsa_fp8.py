@@ -8,7 +8,8 @@ import torch
 
 import oracle
 import workloads as W
-from fia_gpu import bsa_plan, compare, gather_rows, run, sample_rows, say, to_dev, TOL_LSE, TOL_OUT
+from fia_gpu import (bsa_plan, compare, compare_rows, gather_rows, head_rows, run, sample_rows, say,
+                     seeded_subset, to_dev, TOL_LSE, TOL_OUT)
 
 pytestmark = pytest.mark.gpu
 
@@ -78,17 +79,16 @@ def test_bsa_fp8_tnd():
     check(case)
 
 
-def test_workload_fp8_block_sparse_full_sampled():
+def test_workload_fp8_block_sparse_whole_heads():
+    # two seeded query heads, every row of each (32768 rows per head)
     case = W.fp8_block_sparse(device="cuda")
-    say(f"[full] {case.name}")
-    rows = sample_rows(case, 96, seed=31)
+    heads = seeded_subset(case.QN, 2, seed=31)
+    rows = head_rows(case, heads)
+    say(f"[full] {case.name}: heads {heads}, every row")
     ref_o, ref_l = oracle.block_sparse(case, rows=rows)
     plan = bsa_plan(case)
     out, lse = run(plan)
-    go, gl = gather_rows(case, out, lse, rows)
-    err = float(np.max(np.abs(go - ref_o)))
-    lerr = float(np.max(np.abs(gl - ref_l)))
-    say(f"[full] {case.name}: max out err {err:.3e}, max lse err {lerr:.3e}")
-    assert err <= TOL_OUT[torch.bfloat16] and lerr <= TOL_LSE
+    err, lerr = compare_rows(case, out, lse, rows, ref_o, ref_l)
+    say(f"[full] {case.name}: {len(rows)} rows, max out err {err:.3e}, max lse err {lerr:.3e}")
     assert torch.isfinite(out.float()).all()
     plan.close()

@@ -10,7 +10,8 @@ import torch
 
 import oracle
 import workloads as W
-from fia_gpu import compare, fia_plan, gather_rows, run, sample_rows, say, to_dev, TOL_LSE, TOL_OUT
+from fia_gpu import (compare, compare_rows, fia_plan, gather_rows, head_rows, run, sample_rows, say,
+                     seeded_subset, to_dev, TOL_LSE, TOL_OUT)
 
 pytestmark = pytest.mark.gpu
 
@@ -70,18 +71,17 @@ def test_mla_zero_and_negative_scale(scale):
 
 @pytest.mark.parametrize("make", [W.mla_decode_bf16, W.mla_decode_shared_kv_bf16],
                          ids=["separate_value", "value_is_key"])
-def test_mla_full_size_workload_sampled(make):
+def test_mla_full_size_workload_whole_batches(make):
+    # two seeded batches, every one of their 128 query heads
     case = make(device="cuda")
-    say(f"[mla] {case.name} (sampled rows)")
-    rows = sample_rows(case, 48, seed=31, decode=True)
+    batches = seeded_subset(case.B, 2, seed=31)
+    rows = head_rows(case, range(case.QN), batches=batches)
+    say(f"[mla] {case.name}: batches {batches}, every head")
     ref_o, ref_l = oracle.attention(case, rows=rows)
     p = fia_plan(case)
     out, lse = run(p)
-    go, gl = gather_rows(case, out, lse, rows)
-    err = float(np.max(np.abs(go - ref_o)))
-    lerr = float(np.max(np.abs(gl - ref_l)))
-    say(f"[mla] {case.name}: max out err {err:.3e}, max lse err {lerr:.3e}")
-    assert err <= TOL_OUT[case.dtype] and lerr <= TOL_LSE
+    err, lerr = compare_rows(case, out, lse, rows, ref_o, ref_l)
+    say(f"[mla] {case.name}: {len(rows)} rows, max out err {err:.3e}, max lse err {lerr:.3e}")
     assert torch.isfinite(out).all()
     p.close()
 

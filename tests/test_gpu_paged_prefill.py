@@ -11,8 +11,8 @@ import torch
 
 import oracle
 import workloads as W
-from fia_gpu import (compare, fia_plan, gather_rows, run, sample_rows, say, to_dev, TOL_LSE,
-                     TOL_OUT)
+from fia_gpu import (compare, compare_rows, fia_plan, gather_rows, head_rows, run, sample_rows,
+                     say, seeded_subset, to_dev, TOL_LSE, TOL_OUT)
 
 pytestmark = pytest.mark.gpu
 
@@ -156,25 +156,28 @@ def test_paged_prefill_is_invariant_to_pool_permutation():
     pb.close()
 
 
-def _full_sampled(case, n_rows, seed):
-    say(f"[full] {case.name}")
-    rows = sample_rows(case, n_rows, seed=seed)
+def test_workload_paged_chunked_prefill_whole_heads():
+    # four seeded query heads, every row of every batch
+    case = W.paged_chunked_prefill_bf16(device="cuda")
+    heads = seeded_subset(case.QN, 4, seed=11)
+    rows = head_rows(case, heads)
+    say(f"[full] {case.name}: heads {heads}, every row")
     ref_o, ref_l = oracle.attention(case, rows=rows)
-    to_dev(case)
     plan = fia_plan(case)
     out, lse = run(plan)
-    go, gl = gather_rows(case, out, lse, rows)
-    err = float(np.max(np.abs(go - ref_o)))
-    lerr = float(np.max(np.abs(gl - ref_l)))
+    err, lerr = compare_rows(case, out, lse, rows, ref_o, ref_l)
     say(f"[full] {case.name}: {len(rows)} rows, max out err {err:.3e}, max lse err {lerr:.3e}")
-    assert err <= TOL_OUT[case.dtype] and lerr <= TOL_LSE
     assert torch.isfinite(out.float()).all()
     plan.close()
 
 
-def test_workload_paged_chunked_prefill_full_sampled():
-    _full_sampled(W.paged_chunked_prefill_bf16(device="cuda"), 192, 11)
-
-
-def test_workload_paged_mtp_decode_full_sampled():
-    _full_sampled(W.paged_mtp_decode_bf16(device="cuda"), 192, 12)
+def test_workload_paged_mtp_decode_full():
+    # every row of the 4-token decode workload
+    case = W.paged_mtp_decode_bf16(device="cuda")
+    say(f"[full] {case.name}: every row")
+    ref_o, ref_l = oracle.attention(case)
+    plan = fia_plan(case)
+    out, lse = run(plan)
+    err, lerr = compare(case, out, lse, ref_o, ref_l)
+    say(f"[full] {case.name}: max out err {err:.3e}, max lse err {lerr:.3e}")
+    plan.close()

@@ -2,6 +2,7 @@
 the same seeded inputs, element by element, at sizes that span several tiles
 and ragged tails, plus the invariants that hold at any size."""
 import math
+import time
 
 import numpy as np
 import pytest
@@ -9,8 +10,8 @@ import torch
 
 import oracle
 import workloads as W
-from fia_gpu import (bsa_plan, compare, fia_plan, gather_rows, run, sample_rows, say, to_dev,
-                     TOL_OUT, TOL_LSE)
+from fia_gpu import (bsa_plan, compare, compare_rows, fia_plan, gather_rows, head_rows, run,
+                     sample_rows, say, seeded_subset, to_dev, TOL_OUT, TOL_LSE)
 
 pytestmark = pytest.mark.gpu
 
@@ -80,10 +81,9 @@ def test_prefill_gqa_explicit_mask():
 
 
 def _repeat_runs(case, plan, rows, ref_o, ref_l, runs=3):
-    # The prefill and block-sparse workgroups are persistent and take their
-    # tiles from a queue held by the plan, which the last workgroup of a run
-    # resets: every run must compute every tile again.  Outputs are filled
-    # with NaN before each run; each run must match the oracle on the sampled
+    # One plan run several times: the schedule the plan uploaded once is
+    # reused, so every run must write every output row again (outputs are
+    # refilled with NaN before each run), match the oracle on the sampled
     # rows and reproduce the first run bit for bit.
     first = None
     for rep in range(runs):
@@ -382,25 +382,23 @@ def test_workload_c1_mode1_explicit_causal_mask():
     assert (lse1 - lse3).abs().max().item() <= 1e-5
 
 
-def _full_sampled(case, n_rows, seed):
-    say(f"[full] {case.name}")
-    rows = sample_rows(case, n_rows, seed=seed, decode=case.decode)
-    ref_o, ref_l = oracle.attention(case, rows=rows)
+def _full_whole(case):
+    """Every row of the output (padding rows included: out 0, lse +inf)
+    against the oracle, element by element."""
+    say(f"[full] {case.name}: oracle over every row")
+    t0 = time.perf_counter()
+    ref_o, ref_l = oracle.attention(case)
+    say(f"[full] {case.name}: oracle {time.perf_counter() - t0:.1f} s")
     to_dev(case)
     plan = fia_plan(case)
     out, lse = run(plan)
-    go, gl = gather_rows(case, out, lse, rows)
-    err = float(np.max(np.abs(go - ref_o)))
-    lerr = float(np.max(np.abs(gl - ref_l)))
-    say(f"[full] {case.name}: {len(rows)} rows, max out err {err:.3e}, max lse err {lerr:.3e}")
-    assert err <= TOL_OUT[case.dtype] and lerr <= TOL_LSE
-    # properties at every row: finite, rows exist for every valid query
-    assert torch.isfinite(out.float()).all()
+    err, lerr = compare(case, out, lse, ref_o, ref_l)
+    say(f"[full] {case.name}: every row, max out err {err:.3e}, max lse err {lerr:.3e}")
     plan.close()
 
 
-def test_workload_c2_full_sampled():
-    _full_sampled(W.c2_gqa_causal_bf16(device="cuda"), 256, 1)
+def test_workload_c2_full():
+    _full_whole(W.c2_gqa_causal_bf16(device="cuda"))
 
 
 def test_workload_c3_full():
@@ -415,14 +413,16 @@ def test_workload_c3_full():
     plan.close()
 
 
-def test_workload_c4_full_sampled():
-    _full_sampled(W.c4_varlen_tnd_bf16(device="cuda"), 256, 2)
+def test_workload_c4_full():
+    _full_whole(W.c4_varlen_tnd_bf16(device="cuda"))
 
 
-def test_workload_c5_full_sampled():
+def test_workload_c5_whole_heads():
+    # two seeded query heads, every row of each (32768 rows per head)
     case = W.c5_block_sparse_bf16(device="cuda")
-    say(f"[full] {case.name}")
-    rows = sample_rows(case, 96, seed=3)
+    heads = seeded_subset(case.QN, 2, seed=3)
+    say(f"[full] {case.name}: heads {heads}, every row")
+    rows = head_rows(case, heads)
     ref_o, ref_l = oracle.block_sparse(case, rows=rows)
     ridx, rcnt = oracle.bsa_compact(case.block_mask.cpu().numpy(), np.full(1, case.Sq),
                                     np.full(1, case.Skv), case.X, case.Y)
@@ -431,9 +431,7 @@ def test_workload_c5_full_sampled():
     cnt, idx, nqb, nkb = plan.schedule()
     assert np.array_equal(cnt.cpu().numpy(), rcnt.reshape(-1))
     assert np.array_equal(idx.cpu().numpy(), ridx.reshape(-1, nkb))
-    go, gl = gather_rows(case, out, lse, rows)
-    err = float(np.max(np.abs(go - ref_o)))
-    lerr = float(np.max(np.abs(gl - ref_l)))
-    say(f"[full] {case.name}: max out err {err:.3e}, max lse err {lerr:.3e}")
-    assert err <= TOL_OUT[case.dtype] and lerr <= TOL_LSE
+    err, lerr = compare_rows(case, out, lse, rows, ref_o, ref_l)
+    say(f"[full] {case.name}: {len(rows)} rows, max out err {err:.3e}, max lse err {lerr:.3e}")
+    assert torch.isfinite(out.float()).all()
     plan.close()

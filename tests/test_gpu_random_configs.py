@@ -110,7 +110,7 @@ def test_random_paged(seed):
     _check_fia(case)
 
 
-@pytest.mark.parametrize("seed", range(12))
+@pytest.mark.parametrize("seed", range(16))
 def test_random_int8_decode(seed):
     rng = np.random.default_rng(900 + seed)
     KVN = int(rng.choice([1, 2]))
@@ -118,11 +118,22 @@ def test_random_int8_decode(seed):
     G = int(rng.choice([g for g in (1, 2, 4, 8, 16) if g * S <= 16]))
     B = int(rng.integers(1, 4))
     D = int(rng.choice([64, 128]))
-    case = W.make_quant_decode(f"rand_int8_{seed}", layout=str(rng.choice(["BNSD", "BSND", "BSH"])),
-                               B=B, QN=KVN * G, KVN=KVN, D=D, Sq=S, lkv=rng.integers(S, 2500, size=B),
-                               kmode=int(rng.integers(2)), vmode=int(rng.integers(2)),
+    layout = str(rng.choice(["BNSD", "BSND", "BSH"]))
+    lkv = rng.integers(S, 2500, size=B)
+    # legal mode pairs: equal, or key 0 with value 1 at query S 1; a paged
+    # int8 cache (block size a multiple of 32) at query S 1 only
+    if S == 1:
+        km, vm = [(0, 0), (1, 1), (0, 1)][int(rng.integers(3))]
+        paged = bool(rng.random() < 0.5)
+    else:
+        km = vm = int(rng.integers(2))
+        paged = False
+    bs = int(rng.choice([32, 64, 128])) if paged else 0
+    case = W.make_quant_decode(f"rand_int8_{seed}", layout=layout, B=B, QN=KVN * G, KVN=KVN, D=D,
+                               Sq=S, lkv=lkv, kmode=km, vmode=vm,
                                offsets=bool(rng.random() < 0.7), sparse_mode=3 if S > 1 else 0,
-                               seed=910 + seed)
+                               seed=910 + seed, block_size=bs, pool_layout=int(rng.integers(2)),
+                               extra_blocks=2 if paged else 0)
     _check_fia(case)
 
 

@@ -691,6 +691,16 @@ def int8_kv_decode_bf16(device="cpu") -> FiaCase:
                              seed=1008, device=device)
 
 
+def int8_paged_decode_bf16(device="cpu") -> FiaCase:
+    """Decode against a paged int8 KV cache with per-channel scales and
+    offsets: the paged GQA decode shape (B=64, Q_S=1, Q_N=32, KV_N=8, D=128,
+    its KV lengths ~ U{512..32768}), bf16 query, int8 pools
+    (NB, KV_N, 128, 128) addressed through a seeded permutation, LSE on."""
+    return make_quant_decode("int8_paged_decode_perchannel_b64_n32_kv8_d128_bs128", layout="BNSD",
+                             B=64, QN=32, KVN=8, D=128, lkv=c3_lengths(), kmode=0, vmode=0,
+                             block_size=128, pool_layout=0, seed=1011, device=device)
+
+
 def fp8_block_sparse(device="cpu") -> BsaCase:
     """Block-sparse prefill with FP8 (E4M3FN) inputs: B=1, Q_N=32, KV_N=8,
     S=32768, D=128, BNSD, block [128, 256] (the quantization blocks), mask
@@ -732,6 +742,7 @@ WORKLOADS = {
     "paged_prefill": paged_chunked_prefill_bf16,
     "mtp_decode": paged_mtp_decode_bf16,
     "int8_decode": int8_kv_decode_bf16,
+    "int8_paged_decode": int8_paged_decode_bf16,
     "fp8_bsa": fp8_block_sparse,
     "mla_decode": mla_decode_bf16,
     "mla_shared_kv": mla_decode_shared_kv_bf16,
