@@ -26,7 +26,7 @@ import torch
 from . import _abi
 from ._abi import (FIA_OK, bsa_get_workspace_size, bsa_params, bsa_params_init, bsa_run,
                    bsa_schedule_layout, fia_get_workspace_size, fia_params, fia_params_init,
-                   fia_plan_destroy, fia_run, fia_status_string, fia_tensor)
+                   fia_plan_destroy, fia_run, fia_run_noalloc, fia_status_string, fia_tensor)
 
 INT_MAX = 2147483647
 
@@ -159,6 +159,13 @@ class FiaPlan:
             raise FiaError(st, "fia_run")
         return self.out, self.lse
 
+    def run_noalloc(self):
+        """Phase 2 on the library's static device scratch (fia_run_noalloc)."""
+        st = fia_run_noalloc(self.plan, _stream_handle(self.device))
+        if st != FIA_OK:
+            raise FiaError(st, "fia_run_noalloc")
+        return self.out, self.lse
+
     def close(self):
         if self.plan:
             fia_plan_destroy(self.plan)
@@ -231,6 +238,13 @@ class BsaPlan:
                      _stream_handle(self.device))
         if st != FIA_OK:
             raise FiaError(st, "bsa_run")
+        return self.out, self.lse
+
+    def run_noalloc(self):
+        """Phase 2 on the library's static device scratch (fia_run_noalloc)."""
+        st = fia_run_noalloc(self.plan, _stream_handle(self.device))
+        if st != FIA_OK:
+            raise FiaError(st, "fia_run_noalloc")
         return self.out, self.lse
 
     def schedule(self):

@@ -96,6 +96,7 @@ _SIGS = {
                                            ctypes.POINTER(ctypes.c_uint64),
                                            ctypes.POINTER(ctypes.c_int64),
                                            ctypes.POINTER(ctypes.c_int64)]),
+    "fia_run_noalloc": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p]),
     "fia_plan_destroy": (None, [ctypes.c_void_p]),
     "fia_status_string": (ctypes.c_char_p, [ctypes.c_int]),
 }
@@ -162,6 +163,13 @@ def bsa_get_workspace_size(query, key, value, block_sparse_mask, atten_mask, blo
 
 def bsa_run(workspace: int, workspace_size: int, plan: int, stream: int) -> int:
     return lib().bsa_run(workspace or None, workspace_size, plan, stream or None)
+
+
+FIA_NOALLOC_MAX_WORKSPACE = 32 << 20
+
+
+def fia_run_noalloc(plan: int, stream: int) -> int:
+    return lib().fia_run_noalloc(plan, stream or None)
 
 
 def bsa_schedule_layout(plan: int):

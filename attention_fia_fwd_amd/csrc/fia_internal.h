@@ -31,6 +31,9 @@ constexpr int kNumCUs = 256;
 constexpr int kDecodeWavesPerCU = 8;
 // Largest MLA decode workgroup (waves of 16 query rows each).
 constexpr int kMlaMaxWaves = 8;
+// Size of the static device scratch the allocation-free run uses as its
+// workspace (FIA_NOALLOC_MAX_WORKSPACE in fia.h).
+constexpr uint64_t kNoAllocScratchBytes = (uint64_t)32 << 20;
 
 // Per-batch addressing, 24 bytes.  row0 is the first row of batch b on the
 // tensor's row axis: b * S for BNSD/BSND, the cumulative start for TND.
@@ -209,5 +212,8 @@ int launch_decode(const fia_plan& p, const DecodeArgs& a, void* stream);
 int launch_bsa(const fia_plan& p, const AttnArgs& a, void* stream);
 // Device copy of a plan's schedule tables (synchronous); nullptr on failure.
 void* upload_tables(const void* src, uint64_t bytes);
+// Device address of the current device's static scratch array (resolved
+// once per device); nullptr when no device is current or the lookup fails.
+void* noalloc_scratch();
 void free_tables(void* dev);
 }  // namespace fia

@@ -32,6 +32,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 #include <type_traits>
 
 #include "fia_internal.h"
@@ -2293,6 +2294,40 @@ int launch_decode(const fia_plan& p, const DecodeArgs& a, void* stream)
     if (p.Dqk == 64) return bf ? launch_dec<FIA_BF16, 64>(p, a, s) : launch_dec<FIA_F16, 64>(p, a, s);
     if (p.Dqk == 128) return bf ? launch_dec<FIA_BF16, 128>(p, a, s) : launch_dec<FIA_F16, 128>(p, a, s);
     return (int)hipErrorInvalidValue;
+}
+
+// ---------------------------------------------------------------------------
+// Scratch of the allocation-free run: one static device array per GPU the
+// library runs on (it lives until the process ends).  In host code the
+// array's name is only a host-side stand-in; its device address comes from
+// hipGetSymbolAddress, resolved once per device with that device current,
+// and only that address is ever handed to kernels.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void* scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+void* noalloc_scratch()
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        (void)hipGetLastError();
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    if (!scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) {
+            (void)hipGetLastError();
+            return nullptr;
+        }
+        scratch_ptr[dev] = ptr;
+    }
+    return scratch_ptr[dev];
 }
 
 void* upload_tables(const void* src, uint64_t bytes)

@@ -199,6 +199,9 @@ void finish_tables(fia_plan* p)
     p->tables_bytes = align_up(p->host_tables.size(), 256);
     p->host_tables.resize(p->tables_bytes);
     if (p->tables_bytes) p->dev_tables = upload_tables(p->host_tables.data(), p->tables_bytes);
+    // set-up of the allocation-free run: resolve this device's scratch
+    // address now (once per device), not inside a caller's capture
+    if (p->dev_tables) (void)noalloc_scratch();
 }
 
 }  // namespace
@@ -1216,6 +1219,20 @@ fia_status fia_run(void* workspace, uint64_t workspace_size, fia_plan* plan, voi
 fia_status bsa_run(void* workspace, uint64_t workspace_size, fia_plan* plan, void* stream)
 {
     return run_common(workspace, workspace_size, plan, stream, true);
+}
+
+fia_status fia_run_noalloc(fia_plan* plan, void* stream)
+{
+    if (!plan) return FIA_ERR_NULLPTR;
+    if (plan->kind == KIND_EMPTY) return FIA_OK;
+    static_assert(kNoAllocScratchBytes == FIA_NOALLOC_MAX_WORKSPACE, "scratch size");
+    if (plan->workspace_bytes > kNoAllocScratchBytes) return FIA_ERR_WORKSPACE;
+    void* ws = nullptr;
+    if (plan->workspace_bytes) {
+        ws = noalloc_scratch();
+        if (!ws) return FIA_ERR_HIP;
+    }
+    return run_common(ws, kNoAllocScratchBytes, plan, stream, plan->kind == KIND_BSA);
 }
 
 }  // extern "C"

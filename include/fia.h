@@ -295,6 +295,32 @@ fia_status bsa_get_workspace_size(const fia_tensor* query, const fia_tensor* key
 fia_status bsa_run(void* workspace, uint64_t workspace_size, fia_plan* plan, void* stream);
 
 /*
+ * Allocation-free phase 2, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): runs a plan from either phase-1 call, like fia_run / bsa_run,
+ * with the library's own static device scratch of
+ * FIA_NOALLOC_MAX_WORKSPACE bytes as the workspace.  That array exists once
+ * per GPU (each GPU the library runs on holds it until the process ends);
+ * its device address is looked up on the first call on each device, with
+ * that device current.  The call allocates nothing, copies nothing and does
+ * not synchronize; the caller still owns every input and output the plan
+ * names.
+ *   - Plans whose workspace size exceeds FIA_NOALLOC_MAX_WORKSPACE return
+ *     FIA_ERR_WORKSPACE (nothing is launched).
+ *   - Every call on one GPU shares that GPU's scratch, which keeps the last
+ *     call's contents: calls that overlap on one GPU (different streams, or
+ *     work not yet complete on another stream) race and must be ordered by
+ *     the caller.  No kernel needs the scratch cleared: each run writes every
+ *     scratch byte it reads.
+ *   - FIA_ERR_HIP if the scratch address cannot be resolved or a launch
+ *     fails.
+ * bsa_schedule_layout offsets then refer to this scratch, which the caller
+ * cannot address; use bsa_run with an own workspace to inspect a schedule.
+ */
+#define FIA_NOALLOC_MAX_WORKSPACE ((uint64_t)32 << 20)
+fia_status fia_run_noalloc(fia_plan* plan, void* stream);
+
+/*
  * Where bsa_run leaves the compacted block schedule inside the workspace
  * after it has run: int32 cnt[B, N1, nqb] at *cnt_offset and int32
  * idx[B, N1, nqb, nkb] at *idx_offset (byte offsets).  idx lists, per

@@ -402,6 +402,26 @@ def test_run_rejects_small_workspace_without_touching_the_gpu():
     fia.fia_plan_destroy(plan)
 
 
+def test_run_noalloc_status_codes_without_a_gpu():
+    # the allocation-free run refuses a NULL plan, and a plan whose
+    # workspace exceeds the static scratch before it touches any device
+    import workloads as W
+    assert fia.fia_run_noalloc(0, 0) == _abi.FIA_ERR_NULLPTR
+    case = W.make_mla_decode("noalloc_cpu", B=64, QN=128, Sq=1, lkv=[600] * 64, block_size=128, seed=1)
+    p = _params(num_heads=128, num_key_value_heads=1, input_layout=case.layout, block_size=128)
+    kl = np.asarray(case.lkv, dtype=np.int64)
+    p.actual_seq_kvlen, p.n_actual_seq_kvlen = kl.ctypes.data, len(kl)
+    qr, kr = fia.describe(case.rope["query_rope"]), fia.describe(case.rope["key_rope"])
+    p.query_rope, p.key_rope = ctypes.pointer(qr), ctypes.pointer(kr)
+    o = torch.zeros_like(case.q)
+    st, ws, plan = fia.fia_get_workspace_size(fia.describe(case.q), fia.describe(case.k),
+                                              fia.describe(case.v), None, fia.describe(case.block_table),
+                                              p, fia.describe(o), None)
+    assert st == _abi.FIA_OK and ws > _abi.FIA_NOALLOC_MAX_WORKSPACE
+    assert fia.fia_run_noalloc(plan, 0) == _abi.FIA_ERR_WORKSPACE
+    fia.fia_plan_destroy(plan)
+
+
 def test_run_without_a_device_at_phase1_fails_without_allocating():
     # phase 1 with no device visible validates and sizes but uploads no
     # schedule; phase 2 then returns FIA_ERR_HIP instead of allocating
