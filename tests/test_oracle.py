@@ -418,6 +418,44 @@ def _gather_pool(case):
 
 @pytest.mark.parametrize("pool_layout", [0, 1])
 @pytest.mark.parametrize("mode", [0, 3, 4])
+def test_tnd_paged_prefill_equals_contiguous_tnd_after_gather(pool_layout, mode):
+    # TND query with a paged cache (v2 page, TND constraints: page attention
+    # with block size 128 / 512 / 1024, cumulative actual_seq_kvlen): equals
+    # the contiguous TND oracle on the pool gathered batch by batch and
+    # concatenated, bit for bit
+    lq, lkv = [70, 1, 130], [200, 1, 300]
+    mk = "template" if mode in (3, 4) else None
+    case = W.make_paged_prefill(layout="TND", B=3, QN=4, KVN=2, D=16, lq=lq, lkv=lkv,
+                                block_size=128, pool_layout=pool_layout, sparse_mode=mode,
+                                pre_tokens=50, next_tokens=20, mask_kind=mk, extra_blocks=2,
+                                seed=95 + mode + 4 * pool_layout)
+    assert list(case.seq_kvlen_arg()) == list(np.cumsum(lkv))
+    out, lse = oracle.attention(case)
+    kc, vc = _gather_pool(case)                     # [B, KVN, cols * bs, D]
+    kt = torch.cat([kc[b, :, :lkv[b]].permute(1, 0, 2) for b in range(3)])   # [T_kv, KVN, D]
+    vt = torch.cat([vc[b, :, :lkv[b]].permute(1, 0, 2) for b in range(3)])
+    cont = W.make_fia(layout="TND", dtype=torch.bfloat16, B=3, QN=4, KVN=2, Dqk=16, lq=lq, lkv=lkv,
+                      sparse_mode=mode, pre_tokens=50, next_tokens=20, mask_kind=mk, seed=0)
+    cont.q, cont.k, cont.v = case.q, kt.contiguous(), vt.contiguous()
+    oc, lc = oracle.attention(cont)
+    np.testing.assert_array_equal(out, oc)
+    np.testing.assert_array_equal(lse, lc)
+    # and per-sequence runs: each sequence's rows equal a BNSD run of its own
+    start = 0
+    for b in range(3):
+        one = W.make_fia(layout="BNSD", dtype=torch.bfloat16, B=1, QN=4, KVN=2, Sq=lq[b], Skv=lkv[b],
+                         Dqk=16, sparse_mode=mode, pre_tokens=50, next_tokens=20, mask_kind=mk, seed=0)
+        one.q = case.q[start:start + lq[b]].permute(1, 0, 2).unsqueeze(0).contiguous()
+        one.k = kc[b:b + 1, :, :lkv[b]].contiguous()
+        one.v = vc[b:b + 1, :, :lkv[b]].contiguous()
+        o1, l1 = oracle.attention(one)
+        np.testing.assert_array_equal(out[start:start + lq[b]], o1[0].transpose(1, 0, 2))
+        np.testing.assert_array_equal(lse[start:start + lq[b]], l1[0].T)
+        start += lq[b]
+
+
+@pytest.mark.parametrize("pool_layout", [0, 1])
+@pytest.mark.parametrize("mode", [0, 3, 4])
 def test_paged_prefill_equals_contiguous_after_gather(pool_layout, mode):
     # chunked prefill: query chunks shorter than the cached kv
     case = W.make_paged_prefill(layout="BNSD", B=3, QN=4, KVN=2, D=16, Sq=12, lq=[12, 5, 9],

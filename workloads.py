@@ -110,9 +110,10 @@ class FiaCase:
     def seq_kvlen_arg(self):
         if self.lkv is None:
             return None
-        if self.layout == "TND" and self.block_table is None:
+        if self.layout == "TND" and (self.block_table is None or self.rope is None):
             return np.cumsum(self.lkv).astype(np.int64)
-        # (TND with page attention, the MLA case: each batch's own length)
+        # (TND with page attention and a query D of 512, the MLA case: each
+        # batch's own length)
         return self.lkv.astype(np.int64)
 
 
@@ -283,7 +284,8 @@ def make_paged_prefill(name="custom", *, layout="BNSD", dtype=torch.bfloat16, B=
                        mask_kind=None, scale=None, seed=0, device="cpu", extra_blocks=0,
                        table_cols=None, nan_pool=False, return_lse=True) -> FiaCase:
     """Prefill (query S > 1) against a paged KV cache: the query in ``layout``
-    (BNSD/BSND/BSH) with per-batch lengths ``lq`` (None = Sq), K/V in a shared
+    (BNSD/BSND/BSH, or TND with the batches' ``lq`` rows back to back) with
+    per-batch lengths ``lq`` (None = Sq), K/V in a shared
     physical pool addressed through a block table holding a seeded
     permutation of the pool's block ids (unused entries -1).  ``nan_pool``
     fills the pool's unreferenced blocks and the tail rows of each batch's
@@ -304,6 +306,8 @@ def make_paged_prefill(name="custom", *, layout="BNSD", dtype=torch.bfloat16, B=
     for b in range(B):
         table[b, :nblk[b]] = perm[pos:pos + nblk[b]]
         pos += nblk[b]
+    if layout == "TND":
+        Sq = int(lq.sum())
     q = normal_tensor(_shape(layout, B, QN, Sq, D), dtype, ss[STREAM_Q], device)
     pshape = (NB, KVN, block_size, D) if pool_layout == 0 else (NB, block_size, KVN * D)
     k = normal_tensor(pshape, dtype, ss[STREAM_K], device)
