@@ -344,10 +344,9 @@ fia_status fia_get_workspace_size(const fia_tensor* query, const fia_tensor* key
     if (paged) {
         // PageAttention (constraints, page attention scenario).  Query S == 1:
         // block_size a multiple of 16; query S > 1: a multiple of 128 in
-        // [128, 512].  A TND query with a paged cache is not provided.
-        // (MLA with a query D of 512 allows TND: the batch is the count of
-        // actual_seq_qlen, checked against the table below)
-        if (layout == LAYOUT_TND && !mla) return FIA_ERR_UNSUPPORTED;
+        // [128, 512]; a TND query (TND constraints): 128, 512 or 1024, the
+        // batch being the count of actual_seq_qlen (checked against the
+        // table below).
         if (!block_table->data) return FIA_ERR_NULLPTR;
         if (block_table->dtype != FIA_I32) return FIA_ERR_DTYPE;
         if (block_table->ndim != 2) return FIA_ERR_SHAPE;
@@ -357,6 +356,9 @@ fia_status fia_get_workspace_size(const fia_tensor* query, const fia_tensor* key
             // MLA with a query D of 512: block_size 16 or 128 (64 or 128 with
             // sparse_mode 4)
             if (prm->block_size != 16 && prm->block_size != 64 && prm->block_size != 128)
+                return FIA_ERR_PARAM;
+        } else if (layout == LAYOUT_TND) {
+            if (prm->block_size != 128 && prm->block_size != 512 && prm->block_size != 1024)
                 return FIA_ERR_PARAM;
         } else if (!decode && (prm->block_size % 128 != 0 || prm->block_size > 512)) {
             return FIA_ERR_PARAM;
@@ -403,11 +405,18 @@ fia_status fia_get_workspace_size(const fia_tensor* query, const fia_tensor* key
         if ((st = resolve_cumulative(prm->actual_seq_qlen, prm->n_actual_seq_qlen, gq.S, &lq,
                                      &qstart)) != FIA_OK)
             return st;
-        if (paged) {
+        if (paged && mla) {
             // MLA TND with page attention: actual_seq_kvlen holds each batch's
             // own length (D 512 TND constraints), not cumulative sums
             if ((st = resolve_lengths(prm->actual_seq_kvlen, prm->n_actual_seq_kvlen,
                                       prm->n_actual_seq_qlen, Skv, &lkv)) != FIA_OK)
+                return st;
+            if (block_table->dims[0] != prm->n_actual_seq_qlen) return FIA_ERR_SHAPE;
+        } else if (paged) {
+            // other head dims: cumulative as for every TND call; each batch's
+            // pages must fit the table's row (checked with the pool below)
+            if ((st = resolve_cumulative(prm->actual_seq_kvlen, prm->n_actual_seq_kvlen,
+                                         ((int64_t)1 << 40), &lkv, &kvstart)) != FIA_OK)
                 return st;
             if (block_table->dims[0] != prm->n_actual_seq_qlen) return FIA_ERR_SHAPE;
         } else if ((st = resolve_cumulative(prm->actual_seq_kvlen, prm->n_actual_seq_kvlen, Skv, &lkv,

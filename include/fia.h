@@ -108,9 +108,10 @@ typedef struct fia_params {
      * Ignored when the query S is 1 outside TND (decode). */
     int64_t sparse_mode;
     /* PageAttention block size (block_size); 0 = contiguous KV.  With a
-     * block_table and query S == 1 it must be a positive multiple of 16; with
-     * query S > 1 a multiple of 128 in [128, 512] (page attention scenario
-     * constraints of the v2 page). */
+     * block_table and query S == 1 it must be a positive multiple of 16
+     * (int8 key/value: of 32); with query S > 1 a multiple of 128 in
+     * [128, 512]; with a TND query 128, 512 or 1024 (page attention scenario
+     * and TND constraints of the v2 page). */
     int64_t block_size;
     /* inner_precise 0..3 (bit0 precision/performance, bit1 row-invalid
      * correction).  Accepted; softmax is always computed in fp32 and rows
@@ -200,9 +201,10 @@ void fia_params_init(fia_params* p);
  *   block_table  optional int32 [B, >= max blocks per sequence]: PageAttention
  *                block ids (page attention scenario of the v2 page): kv token
  *                j of batch b is row j % block_size of pool block
- *                block_table[b][j / block_size].  Any query S outside TND (a
- *                TND query with a paged cache returns FIA_ERR_UNSUPPORTED,
- *                except for MLA: see query_rope in fia_params).
+ *                block_table[b][j / block_size].  Any query S; with a TND
+ *                query the table has one row per sequence (the count of
+ *                actual_seq_qlen) and actual_seq_kvlen stays cumulative
+ *                (except for MLA: see query_rope in fia_params).
  *                Ids are not checked: each referenced id must be in
  *                [0, blocknum), as the page requires; entries past
  *                ceil(Lkv_b / block_size) are never read.

@@ -214,15 +214,27 @@ def test_paged_decode_validation():
                       (64, _abi.FIA_ERR_PARAM), (640, _abi.FIA_ERR_PARAM)):
         pool2 = torch.zeros(nblk, KVN, bs2, D, dtype=torch.bfloat16)
         assert run(q=q2, pool=pool2, block_size=bs2, bt=torch.zeros(B, 1, dtype=torch.int32)) == code, bs2
-    # a TND query with a paged cache is not provided
-    p = _params(input_layout="TND", num_heads=QN, num_key_value_heads=KVN, block_size=128,
-                sparse_mode=3)
+    # a TND query with a paged cache (TND constraints): block_size 128, 512
+    # or 1024, cumulative actual_seq_kvlen, one table row per sequence
     cq = np.array([3, 7], dtype=np.int64)
-    p.actual_seq_qlen, p.n_actual_seq_qlen = cq.ctypes.data, 2
-    p.actual_seq_kvlen, p.n_actual_seq_kvlen = lkv.ctypes.data, 2
-    qt = torch.zeros(7, QN, D, dtype=torch.bfloat16)
-    pool3 = torch.zeros(nblk, KVN, 128, D, dtype=torch.bfloat16)
-    assert _phase1(qt, pool3, pool3, p, bt=torch.zeros(B, 1, dtype=torch.int32))[0] == _abi.FIA_ERR_UNSUPPORTED
+    ckv = np.array([40, 57], dtype=np.int64)          # kv lengths 40 and 17
+
+    def tnd(bs3, ckv=ckv, rows=B, cols=1, mode=3):
+        p = _params(input_layout="TND", num_heads=QN, num_key_value_heads=KVN, block_size=bs3,
+                    sparse_mode=mode)
+        p.actual_seq_qlen, p.n_actual_seq_qlen = cq.ctypes.data, 2
+        p.actual_seq_kvlen, p.n_actual_seq_kvlen = ckv.ctypes.data, 2
+        qt = torch.zeros(7, QN, D, dtype=torch.bfloat16)
+        pool3 = torch.zeros(nblk, KVN, bs3, D, dtype=torch.bfloat16)
+        return _phase1(qt, pool3, pool3, p, bt=torch.zeros(rows, cols, dtype=torch.int32))[0]
+
+    for bs3, code in ((128, _abi.FIA_OK), (512, _abi.FIA_OK), (1024, _abi.FIA_OK),
+                      (256, _abi.FIA_ERR_PARAM), (384, _abi.FIA_ERR_PARAM), (64, _abi.FIA_ERR_PARAM)):
+        assert tnd(bs3) == code, bs3
+    assert tnd(128, mode=0) == _abi.FIA_OK
+    assert tnd(128, rows=3) == _abi.FIA_ERR_SHAPE                       # rows != sequences
+    assert tnd(128, ckv=np.array([40, 30], dtype=np.int64)) == _abi.FIA_ERR_SHAPE   # not cumulative
+    assert tnd(128, ckv=np.array([40, 300], dtype=np.int64)) == _abi.FIA_ERR_SHAPE  # 260 > 1 block
 
 
 def test_decode_atten_mask_validation():

@@ -52,6 +52,30 @@ def test_paged_prefill_modes(pool_layout, mode):
     check(case)
 
 
+TND_CASES = [
+    # name, block_size, pool_layout, mode, D, QN, KVN, lq, lkv, dtype
+    ("bs128_pl0_m3", 128, 0, 3, 128, 8, 2, [300, 1, 129, 77], [700, 1, 129, 2000], torch.bfloat16),
+    ("bs512_pl1_m0", 512, 1, 0, 128, 4, 4, [64, 200], [5000, 200], torch.bfloat16),
+    ("bs1024_pl0_m4", 1024, 0, 4, 128, 16, 4, [150, 90, 33], [3000, 90, 1500], torch.bfloat16),
+    ("bs1024_pl1_m3_long", 1024, 1, 3, 64, 4, 1, [257, 1000], [70000, 1000], torch.float16),
+    ("bs128_pl1_m3_f16", 128, 1, 3, 64, 2, 2, [5, 333], [5, 4096], torch.float16),
+]
+
+
+@pytest.mark.parametrize("case_args", TND_CASES, ids=[c[0] for c in TND_CASES])
+def test_tnd_paged_prefill(case_args):
+    # a TND query against a paged cache (TND constraints: block size 128,
+    # 512 or 1024, cumulative actual_seq_kvlen); the 70000-token cache spans
+    # more than 64 blocks of 1024 (the kernel's block-id window moves)
+    name, bs, pl, mode, D, QN, KVN, lq, lkv, dtype = case_args
+    case = W.make_paged_prefill(f"tnd_paged_{name}", layout="TND", dtype=dtype, B=len(lq), QN=QN,
+                                KVN=KVN, D=D, lq=lq, lkv=lkv, block_size=bs, pool_layout=pl,
+                                sparse_mode=mode, pre_tokens=120, next_tokens=30,
+                                mask_kind="template" if mode >= 3 else None,
+                                seed=340 + bs // 128 + mode, extra_blocks=2, nan_pool=True)
+    check(case)
+
+
 @pytest.mark.parametrize("layout, bs, dtype, D", [
     ("BSND", 256, torch.float16, 64),
     ("BSH", 384, torch.bfloat16, 128),
