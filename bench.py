@@ -16,7 +16,10 @@ and the mask mode (masked pairs and skipped tiles are not counted).  The
 headline's input tensors (205 MB with padding; the valid rows read are 98 MB)
 fit in the 256 MB MALL (Infinity Cache), so repeated runs read them from
 there rather than from HBM; each line states its input tensor bytes and
-whether they fit.
+whether they fit, and where they fit it also times single runs with the
+inputs evicted first (a 512 MB buffer rewritten before each run).  Beside
+the K-step mean, every line gives the median and the minimum of 20 single
+runs, each between its own HIP events.
 
 The other workloads (dense causal fp16 prefill, paged GQA decode, varlen TND
 prefill, block-sparse prefill, chunked prefill against a paged cache,
@@ -162,6 +165,29 @@ def time_plan(plan, steps: int, warmup: int):
     return wall, ev
 
 
+def sample_launches(plan, n: int = 20, flush=None):
+    """Per-launch HIP event times (ms) of `n` single runs, each bracketed by
+    its own events on the launch stream after a synchronization; with
+    `flush` (a device buffer larger than the 256 MB MALL) the buffer is
+    rewritten before each run so the run starts with its inputs evicted.
+    Returns (median, min)."""
+    import statistics
+    import torch
+    stream = torch.cuda.current_stream()
+    times = []
+    for _ in range(n):
+        if flush is not None:
+            flush.add_(1)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        plan.run()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    return statistics.median(times), min(times)
+
+
 def build_plan(name, case):
     """Phase 1 on the case, twice: the first plan of a process also pays
     one-time set-up (the code object's load on the device); the second is
@@ -213,11 +239,20 @@ def measure(name, steps, warmup):
     plan, phase1_us, plan_total_us, first_us = build_plan(name, case)
     wall, ev = time_plan(plan, steps, warmup)
     inb = input_bytes(case)
+    med, mn = sample_launches(plan)
     res = {"workload": case.name, "steps": steps, "ms_per_step": wall * 1e3,
-           "kernel_ms": ev * 1e3, "phase1_us": round(phase1_us, 1),
+           "kernel_ms": ev * 1e3, "kernel_ms_median": med, "kernel_ms_min": mn,
+           "phase1_us": round(phase1_us, 1),
            "plan_with_allocations_us": round(plan_total_us, 1),
            "phase1_first_in_process_us": round(first_us, 1), "input_tensor_bytes": inb,
            "inputs_fit_mall": inb <= MALL_BYTES}
+    if inb <= MALL_BYTES:
+        # the same runs with the inputs evicted from the MALL first (a 512 MB
+        # buffer rewritten before each run)
+        flush = torch.zeros(2 * MALL_BYTES // 4, dtype=torch.int32, device="cuda")
+        fmed, fmin = sample_launches(plan, flush=flush)
+        del flush
+        res.update(kernel_ms_median_mall_flushed=fmed, kernel_ms_min_mall_flushed=fmin)
     if name in DECODE_WORKLOADS:
         nbytes = decode_bytes(case)
         res.update(value=nbytes / wall / 1e9, unit="GB/s", algorithmic_bytes=nbytes,
@@ -417,6 +452,8 @@ def main():
         "dtype": "fp16" if args.workload == "c1" else "bf16",
         "data": "synthetic (seeded N(0,1) inputs of the workload's shapes and length mix)",
         "config": {"workload": head["workload"], "kernel_ms": head["kernel_ms"],
+                   "kernel_ms_median": head["kernel_ms_median"], "kernel_ms_min": head["kernel_ms_min"],
+                   "kernel_ms_median_mall_flushed": head.get("kernel_ms_median_mall_flushed"),
                    "phase1_us": head["phase1_us"],
                    "plan_with_allocations_us": head["plan_with_allocations_us"],
                    "phase1_first_in_process_us": head["phase1_first_in_process_us"],
