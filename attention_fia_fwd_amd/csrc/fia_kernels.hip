@@ -2075,20 +2075,51 @@ __global__ __launch_bounds__(64) void decode_combine(DecodeArgs a)
     const int64_t orow = (int64_t)sg.q_row0 + t;
     uint16_t* op = (uint16_t*)a.o + (int64_t)b * a.o_sB + (int64_t)h * a.o_sH + orow * a.o_sS;
 
-    float M = -INFINITY;
-    for (int s = 0; s < ns; ++s) M = fmaxf(M, a.part_lse[(slot0 + s) * a.Gc + n]);
+    // the pieces' LSEs 64 at a time (lane i: piece s0 + i), their max by a
+    // wave reduction; the merge itself runs over the pieces in order
+    auto lse_of = [&](int s0) {
+        return s0 + lane < ns ? a.part_lse[(slot0 + s0 + lane) * a.Gc + n] : -INFINITY;
+    };
+    float lv = lse_of(0);
+    float M = lv;
+    for (int s0 = 64; s0 < ns; s0 += 64) M = fmaxf(M, lse_of(s0));
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
     float wsum = 0.f;
     constexpr int PER = D / 64;
     float accv[PER];
 #pragma unroll
     for (int e = 0; e < PER; ++e) accv[e] = 0.f;
     if (M != -INFINITY) {
-        for (int s = 0; s < ns; ++s) {
-            const float ws = __expf(a.part_lse[(slot0 + s) * a.Gc + n] - M);
-            wsum += ws;
-            const float* po = a.part_o + ((slot0 + s) * a.Gc + n) * D + PER * lane;
+        for (int s0 = 0; s0 < ns; s0 += 64) {
+            if (s0 > 0) lv = lse_of(s0);
+            const float wl = __expf(lv - M);
+            const int cnt = min(64, ns - s0);
+            // four pieces' partials loaded together, then merged in order
+            int s = 0;
+            for (; s + 4 <= cnt; s += 4) {
+                float v[4][PER];
 #pragma unroll
-            for (int e = 0; e < PER; ++e) accv[e] += ws * po[e];
+                for (int u = 0; u < 4; ++u) {
+                    const float* po = a.part_o + ((slot0 + s0 + s + u) * a.Gc + n) * D + PER * lane;
+#pragma unroll
+                    for (int e = 0; e < PER; ++e) v[u][e] = po[e];
+                }
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const float ws = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), s + u));
+                    wsum += ws;
+#pragma unroll
+                    for (int e = 0; e < PER; ++e) accv[e] += ws * v[u][e];
+                }
+            }
+            for (; s < cnt; ++s) {
+                const float ws = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), s));
+                wsum += ws;
+                const float* po = a.part_o + ((slot0 + s0 + s) * a.Gc + n) * D + PER * lane;
+#pragma unroll
+                for (int e = 0; e < PER; ++e) accv[e] += ws * po[e];
+            }
         }
     }
     const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
