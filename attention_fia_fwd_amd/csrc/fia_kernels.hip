@@ -233,11 +233,36 @@ __device__ __forceinline__ i32x4 rsrc_advance(i32x4 r, uint32_t d)
     return o;
 }
 
+// Cache policy of the decode kernels' KV-cache loads: nt (streaming).  Each
+// cached K / V byte is read once per run, and with the nt bit a plain
+// 16-byte read of a 4 GiB buffer moves 6.97 TB/s against 6.2 TB/s without
+// it (MI355X).
+constexpr int kStream = 2;
+
 // The same load through the compiler-visible intrinsic (the compiler then
-// orders the LDS reads after it conservatively).
+// orders the LDS reads after it conservatively); AUX is the cache policy.
+template <int AUX = 0>
 __device__ __forceinline__ void dma16_tracked(__amdgpu_buffer_rsrc_t rs, uint16_t* lds_wave, uint32_t voff)
 {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)lds_wave, 16, voff, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)lds_wave, 16, voff, 0, 0, AUX);
+}
+
+// dma16 / dma4 with the streaming (nt) cache policy.
+__device__ __forceinline__ void dma16_nt(i32x4 rs, uint32_t lds_wave, uint32_t voff)
+{
+    const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_wave);
+    uint32_t keep;
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
+                 "buffer_load_dwordx4 %2, %3, 0 offen nt lds\n\ts_mov_b32 m0, %0"
+                 : "=&s"(keep) : "s"(m0v), "v"(voff), "s"(rs) : "memory");
+}
+__device__ __forceinline__ void dma4_nt(i32x4 rs, uint32_t lds_wave, uint32_t voff)
+{
+    const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_wave);
+    uint32_t keep;
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
+                 "buffer_load_dword %2, %3, 0 offen nt lds\n\ts_mov_b32 m0, %0"
+                 : "=&s"(keep) : "s"(m0v), "v"(voff), "s"(rs) : "memory");
 }
 
 // Buffer resource over rows [row0, lkv) of a row-strided tensor (rows of
@@ -1198,14 +1223,14 @@ __global__ __launch_bounds__(64) void decode_split(DecodeArgs a)
 #pragma unroll
                 for (int s = 0; s < NK; ++s)
                     kf[cc][s] = __builtin_bit_cast(
-                        uint4, __builtin_amdgcn_raw_buffer_load_b128(kr, k_voff + 64 * s, 0, 0));
+                        uint4, __builtin_amdgcn_raw_buffer_load_b128(kr, k_voff + 64 * s, 0, kStream));
                 const __amdgpu_buffer_rsrc_t vr = sub_rsrc(vbase, pg, off, tb);
 #pragma unroll
                 for (int u = 0; u < NVI; ++u) {
                     const int r = RPI * u + vr_in;                 // row inside the sub-tile
                     const int R = 16 * cc + r;                     // row inside the step
                     const int chunk = vpc ^ vswz(R);
-                    dma16_tracked(vr, vb + (16 * cc + RPI * u) * D, (uint32_t)((r * tokstride + 8 * chunk) * 2));
+                    dma16_tracked<kStream>(vr, vb + (16 * cc + RPI * u) * D, (uint32_t)((r * tokstride + 8 * chunk) * 2));
                 }
             }
         };
@@ -1527,12 +1552,12 @@ __global__ __launch_bounds__(64) void decode_split_i8(DecodeArgs a)
                 const __amdgpu_buffer_rsrc_t kr = sub_rsrc(kbase, tb);
 #pragma unroll
                 for (int l = 0; l < NKL; ++l)
-                    kf[cc][l] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(kr, k_voff + 16 * l, 0, 0));
+                    kf[cc][l] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(kr, k_voff + 16 * l, 0, kStream));
                 const __amdgpu_buffer_rsrc_t vr = sub_rsrc(vbase, tb);
 #pragma unroll
                 for (int u = 0; u < NVI8; ++u) {
                     const int r = RPI8 * u + vr_in;
-                    dma16_tracked(vr, (uint16_t*)(vb + (16 * cc + RPI8 * u) * D), (uint32_t)(r * tokstride + 16 * vpc));
+                    dma16_tracked<kStream>(vr, (uint16_t*)(vb + (16 * cc + RPI8 * u) * D), (uint32_t)(r * tokstride + 16 * vpc));
                 }
             }
         };
@@ -1824,7 +1849,7 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_decode(DecodeArgs a)
 #pragma unroll
             for (int i = 0; i < ST / NW; ++i) {
                 const int r = NW * i + wid;
-                dma16(r < 16 ? rk0 : rk1, dst + 2u * (uint32_t)(r * D),
+                dma16_nt(r < 16 ? rk0 : rk1, dst + 2u * (uint32_t)(r * D),
                       ((uint32_t)((r & 15) * D) + 8u * (uint32_t)(ln ^ (r & 15))) * 2u);
             }
             // K_rope: 16 loads of 4 bytes per lane, two 128-byte rows each
@@ -1834,7 +1859,7 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_decode(DecodeArgs a)
                 const int r = 2 * u + (ln >> 5);
                 const int pch = (ln & 31) >> 2;      // 16-byte position in the row
                 const uint32_t e = (uint32_t)(8 * (pch ^ ((r >> 1) & 7)) + 2 * (ln & 3));
-                dma4(u < 8 ? rr0 : rr1, dst + 2u * (uint32_t)(ST * D) + 256u * (uint32_t)u,
+                dma4_nt(u < 8 ? rr0 : rr1, dst + 2u * (uint32_t)(ST * D) + 256u * (uint32_t)u,
                      ((uint32_t)((r & 15) * DR) + e) * 2u);
             }
         };
@@ -1848,7 +1873,7 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_decode(DecodeArgs a)
 #pragma unroll
             for (int i = 0; i < ST / NW; ++i) {
                 const int r = NW * i + wid;
-                dma16(r < 16 ? rv0 : rv1, dst + 2u * (uint32_t)(r * D),
+                dma16_nt(r < 16 ? rv0 : rv1, dst + 2u * (uint32_t)(r * D),
                       ((uint32_t)((r & 15) * D) + 8u * (uint32_t)(ln ^ (2 * (r & 7)))) * 2u);
             }
         };
