@@ -1513,18 +1513,16 @@ __global__ __launch_bounds__(64) void decode_split_i8(DecodeArgs a)
         const int my_page = (a.paged && pg_first + lane <= pg_last) ? bt[pg_first + lane] : 0;
         // settle the table load here, not inside the prefetching step loop
         __builtin_amdgcn_s_waitcnt(FIA_VMCNT(0));
-        auto sub_rsrc = [&](const uint8_t* base, int tb) {
-            // rows [tb, t1) (at most 16) of the piece; rows past t1 read as zero
+        // rows [tb, t1) (at most 16) of the piece, which start at row off of
+        // page pg (pg 0 and off = tb for a contiguous cache); rows past t1
+        // read as zero
+        auto sub_rsrc = [&](const uint8_t* base, int pg, int off, int tb) {
             const int nvalid = min(16, t1 - tb);
-            const uint8_t* ptr = base + (int64_t)tb * tokstride;
-            if (a.paged) {
-                const int pg = tb / bs;
-                // a sub-tile past the end reads nothing, not even its table entry
-                const int64_t blk = nvalid > 0 ? __builtin_amdgcn_readlane(my_page, pg - pg_first) : 0;
-                ptr = base + blk * a.p_blk + (int64_t)(tb - pg * bs) * tokstride;
-            }
+            // a sub-tile past the end reads nothing, not even its table entry
+            const int64_t pbase =
+                (a.paged && nvalid > 0) ? (int64_t)__builtin_amdgcn_readlane(my_page, pg - pg_first) * a.p_blk : 0;
             const int64_t bytes = nvalid > 0 ? (int64_t)(nvalid - 1) * tokstride + D : 0;
-            return __builtin_amdgcn_make_buffer_rsrc((void*)ptr, (short)0,
+            return __builtin_amdgcn_make_buffer_rsrc((void*)(base + pbase + (int64_t)off * tokstride), (short)0,
                                                      (int)min(bytes, (int64_t)0x7fffffff), 0x00020000);
         };
         const float* ksrow = KM == 1 ? (const float*)a.k_scale + (int64_t)b * a.tok_stride : nullptr;
@@ -1543,17 +1541,18 @@ __global__ __launch_bounds__(64) void decode_split_i8(DecodeArgs a)
         const uint32_t k_voff = (uint32_t)(n * tokstride + KB * qd);
         const int vr_in = lane / VCH8, vpc = lane % VCH8;
         struct Tok { float ks[8], ko[8], vs[8], vo[8]; };
-        auto issue = [&](int tt0, uint4 (&kf)[2][NKL], uint8_t* vb, Tok& tk) {
+        auto issue = [&](int tt0, int pg0, int off0, int pg1, int off1, uint4 (&kf)[2][NKL], uint8_t* vb, Tok& tk) {
             if constexpr (KM == 1) { tok8(ksrow, tt0, tk.ks); tok8(korow, tt0, tk.ko); }
             if constexpr (VM == 1) { tok8(vsrow, tt0, tk.vs); tok8(vorow, tt0, tk.vo); }
 #pragma unroll
             for (int cc = 0; cc < 2; ++cc) {
                 const int tb = tt0 + 16 * cc;
-                const __amdgpu_buffer_rsrc_t kr = sub_rsrc(kbase, tb);
+                const int pg = cc ? pg1 : pg0, off = cc ? off1 : off0;
+                const __amdgpu_buffer_rsrc_t kr = sub_rsrc(kbase, pg, off, tb);
 #pragma unroll
                 for (int l = 0; l < NKL; ++l)
                     kf[cc][l] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(kr, k_voff + 16 * l, 0, kStream));
-                const __amdgpu_buffer_rsrc_t vr = sub_rsrc(vbase, tb);
+                const __amdgpu_buffer_rsrc_t vr = sub_rsrc(vbase, pg, off, tb);
 #pragma unroll
                 for (int u = 0; u < NVI8; ++u) {
                     const int r = RPI8 * u + vr_in;
@@ -1588,14 +1587,26 @@ __global__ __launch_bounds__(64) void decode_split_i8(DecodeArgs a)
         const float lazy_raw = kLazy / c;
         const int nsteps = (t1 - t0 + ST - 1) / ST;
 
+        // page and row of the next sub-tile to issue (bs % 32 == 0 and
+        // t0 % 16 == 0, so a 16-token sub-tile never crosses a page)
+        int pg = t0 / bs, off = t0 % bs;
+        auto advance16 = [&](int& p, int& o) {
+            o += 16;
+            if (o >= bs) { o -= bs; ++p; }
+        };
         uint4 kfa[2][NKL], kfb[2][NKL];
         Tok ta, tb_;
         auto step = [&](int st, uint4 (&kcur)[2][NKL], uint4 (&knext)[2][NKL], uint8_t* vcur, uint8_t* vnext,
                         const Tok& tcur, Tok& tnext) {
             const int tt0 = t0 + ST * st;
+            // pg/off point at the first sub-tile of step st + 1 here
             if (st + 1 < nsteps) {
+                int pg1 = pg, off1 = off;
+                advance16(pg1, off1);
                 __builtin_amdgcn_s_waitcnt(FIA_LGKMCNT0);   // widening reads of the other byte buffer done
-                issue(tt0 + ST, knext, vnext, tnext);
+                issue(tt0 + ST, pg, off, pg1, off1, knext, vnext, tnext);
+                pg = pg1; off = off1;
+                advance16(pg, off);
                 // step st landed; the next step's K and V loads (issued after its
                 // per-token values) stay in flight
                 __builtin_amdgcn_s_waitcnt(FIA_VMCNT(2 * (NKL + NVI8)));
@@ -1692,7 +1703,13 @@ __global__ __launch_bounds__(64) void decode_split_i8(DecodeArgs a)
             }
         };
 
-        if (nsteps > 0) issue(t0, kfa, vst0, ta);
+        if (nsteps > 0) {
+            int pg1 = pg, off1 = off;
+            advance16(pg1, off1);
+            issue(t0, pg, off, pg1, off1, kfa, vst0, ta);
+            pg = pg1; off = off1;
+            advance16(pg, off);
+        }
         for (int st = 0; st < nsteps; st += 2) {
             step(st, kfa, kfb, vst0, vst1, ta, tb_);
             if (st + 1 < nsteps) step(st + 1, kfb, kfa, vst1, vst0, tb_, ta);
