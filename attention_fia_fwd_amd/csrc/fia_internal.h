@@ -183,7 +183,6 @@ struct fia_plan {
 
     // Schedule tables: built on the host, uploaded once by phase 1 into a
     // device buffer the plan owns (dev_tables).
-    std::vector<unsigned char> host_tables;
     void* dev_tables = nullptr;
     uint64_t tables_bytes = 0;
     uint64_t workspace_bytes = 0;

@@ -159,30 +159,90 @@ int64_t kv_tiles_of(int32_t mode, bool has_mask, int64_t pre, int64_t next, int6
     return (hi - start + kBlockN - 1) / kBlockN;
 }
 
+// Phase-1 temporaries, kept per thread across calls: a caller that plans
+// every step then reuses their memory instead of taking fresh pages from the
+// allocator each time (the planner's buffers of a few hundred KB otherwise
+// cost more than the planning itself).
+struct WorkTile {
+    int64_t work;                          // kv tiles the tile visits
+    Tile t;
+};
+struct PlanScratch {
+    std::vector<unsigned char> tables;     // host image of the schedule tables
+    std::vector<Tile> tiles, tiles2;
+    std::vector<WorkTile> wt, wt2;
+    std::vector<size_t> idx, pos;
+    std::vector<int32_t> pref;
+};
+PlanScratch& plan_scratch()
+{
+    thread_local PlanScratch s;
+    return s;
+}
+// Buffers grown past 64 MB by one huge plan are released after it.
+void trim_scratch(PlanScratch& s)
+{
+    constexpr size_t kKeep = (size_t)64 << 20;
+    auto trim = [](auto& v) {
+        if (v.capacity() * sizeof(v[0]) > kKeep) std::remove_reference_t<decltype(v)>().swap(v);
+    };
+    trim(s.tables); trim(s.tiles); trim(s.tiles2); trim(s.wt); trim(s.wt2);
+    trim(s.idx); trim(s.pos); trim(s.pref);
+}
+
 // Launch order for n tiles given in priority order: position i runs on XCD
 // i % kNumXcds, so position i takes the first remaining tile that prefers
-// that XCD; when none is left, the first remaining tile of any XCD.
+// that XCD; when none is left, the first remaining tile of any XCD.  The
+// tiles are appended to `out`.
 template <class Get, class Pref>
-std::vector<Tile> xcd_order(size_t n, Get get, Pref pref, size_t first_pos = 0)
+void xcd_order(size_t n, Get get, Pref pref, std::vector<Tile>& out, size_t first_pos = 0)
 {
-    std::vector<std::vector<size_t>> q((size_t)kNumXcds);
-    for (size_t i = 0; i < n; ++i) q[(size_t)pref(i)].push_back(i);
-    std::vector<size_t> head((size_t)kNumXcds, 0);
-    std::vector<Tile> out;
-    out.reserve(n);
+    PlanScratch& S = plan_scratch();
+    // tile indices bucketed by preferred XCD, each bucket in priority order
+    size_t start[kNumXcds + 1] = {};
+    S.pref.resize(n);
+    for (size_t i = 0; i < n; ++i) {
+        S.pref[i] = (int32_t)pref(i);
+        ++start[S.pref[i] + 1];
+    }
+    for (int x = 0; x < kNumXcds; ++x) start[x + 1] += start[x];
+    size_t head[kNumXcds], fill[kNumXcds];
+    for (int x = 0; x < kNumXcds; ++x) head[x] = fill[x] = start[x];
+    S.idx.resize(n);
+    for (size_t i = 0; i < n; ++i) S.idx[fill[S.pref[i]]++] = i;
+    out.reserve(out.size() + n);
     for (size_t pos = 0; pos < n; ++pos) {
         size_t x = (first_pos + pos) % (size_t)kNumXcds;
-        if (head[x] == q[x].size()) {
+        if (head[x] == start[x + 1]) {
             size_t best = n;
             for (size_t y = 0; y < (size_t)kNumXcds; ++y)
-                if (head[y] < q[y].size() && q[y][head[y]] < best) {
-                    best = q[y][head[y]];
+                if (head[y] < start[y + 1] && S.idx[head[y]] < best) {
+                    best = S.idx[head[y]];
                     x = y;
                 }
         }
-        out.push_back(get(q[x][head[x]++]));
+        out.push_back(get(S.idx[head[x]++]));
     }
-    return out;
+}
+
+// Stable sort of the work tiles by work, largest first (a counting sort;
+// std::stable_sort when the counts are large).
+void sort_longest_first(std::vector<WorkTile>& v)
+{
+    if (v.size() < 2) return;
+    int64_t kmax = 0;
+    for (const WorkTile& e : v) kmax = std::max<int64_t>(kmax, e.work);
+    if (kmax > ((int64_t)1 << 20)) {
+        std::stable_sort(v.begin(), v.end(), [](const WorkTile& x, const WorkTile& y) { return x.work > y.work; });
+        return;
+    }
+    PlanScratch& S = plan_scratch();
+    S.pos.assign((size_t)kmax + 2, 0);
+    for (const WorkTile& e : v) ++S.pos[(size_t)(kmax - e.work) + 1];
+    for (size_t k = 1; k < S.pos.size(); ++k) S.pos[k] += S.pos[k - 1];
+    S.wt2.resize(v.size());
+    for (const WorkTile& e : v) S.wt2[S.pos[(size_t)(kmax - e.work)]++] = e;
+    v.swap(S.wt2);
 }
 
 template <class T>
@@ -194,14 +254,18 @@ uint64_t put(std::vector<unsigned char>& buf, uint64_t off, const std::vector<T>
     return off + bytes;
 }
 
+// Uploads the host image of the tables (the thread's scratch) into device
+// memory the plan owns.
 void finish_tables(fia_plan* p)
 {
-    p->tables_bytes = align_up(p->host_tables.size(), 256);
-    p->host_tables.resize(p->tables_bytes);
-    if (p->tables_bytes) p->dev_tables = upload_tables(p->host_tables.data(), p->tables_bytes);
+    PlanScratch& S = plan_scratch();
+    p->tables_bytes = align_up(S.tables.size(), 256);
+    S.tables.resize(p->tables_bytes);
+    if (p->tables_bytes) p->dev_tables = upload_tables(S.tables.data(), p->tables_bytes);
     // set-up of the allocation-free run: resolve this device's scratch
     // address now (once per device), not inside a caller's capture
     if (p->dev_tables) (void)noalloc_scratch();
+    trim_scratch(S);
 }
 
 }  // namespace
@@ -806,11 +870,13 @@ fia_status fia_get_workspace_size(const fia_tensor* query, const fia_tensor* key
         p->n_waves = d.n_waves;
         p->n_pieces = d.n_pieces;
         p->off_batch = 0;
-        uint64_t end = put(p->host_tables, 0, segs);
+        std::vector<unsigned char>& tb = plan_scratch().tables;
+        tb.clear();
+        uint64_t end = put(tb, 0, segs);
         p->off_pieces = align_up(end, 256);
-        end = put(p->host_tables, p->off_pieces, pieces);
+        end = put(tb, p->off_pieces, pieces);
         p->off_waves = align_up(end, 256);
-        put(p->host_tables, p->off_waves, wave_first);
+        put(tb, p->off_waves, wave_first);
         finish_tables(p.get());
         const uint64_t np = std::max<uint64_t>(1, pieces.size());
         p->off_part_o = 0;
@@ -900,16 +966,25 @@ fia_status fia_get_workspace_size(const fia_tensor* query, const fia_tensor* key
     while (hg < kDenseWaves && G % (2 * hg) == 0) hg *= 2;
     a.hg = (int32_t)hg;
     const int64_t rows_per = 32 * kDenseWaves / hg;
-    struct W { int64_t work; Tile t; };
-    std::vector<W> tl;
-    std::vector<Tile> zero_fill;
+    PlanScratch& S = plan_scratch();
+    std::vector<WorkTile>& tl = S.wt;
+    tl.clear();
+    std::vector<Tile>& tiles = S.tiles;    // zero-fill workgroups, then the ordered rest
+    tiles.clear();
     const int64_t zrows = std::max<int64_t>(1, ((int64_t)256 << 10) / (QN * Dv * 2));
+    {
+        size_t n = 0;
+        for (int64_t b = 0; b < B; ++b)
+            n += (size_t)((std::min<int64_t>(lq[(size_t)b], layout == LAYOUT_TND ? lq[(size_t)b] : gq.S) +
+                           rows_per - 1) / rows_per);
+        tl.reserve(n * (size_t)(QN / hg));
+    }
     for (int64_t b = 0; b < B; ++b) {
         const int64_t rows = layout == LAYOUT_TND ? lq[(size_t)b] : gq.S;
         const int64_t zfrom = std::min(rows, (lq[(size_t)b] + rows_per - 1) / rows_per * rows_per);
         for (int64_t z0 = zfrom; z0 < rows; z0 += zrows)
-            zero_fill.push_back(Tile{(int32_t)b, -1, (int32_t)z0, (int32_t)std::min(z0 + zrows, rows),
-                                     bi[(size_t)b]});
+            tiles.push_back(Tile{(int32_t)b, -1, (int32_t)z0, (int32_t)std::min(z0 + zrows, rows),
+                                 bi[(size_t)b]});
         for (int64_t q0 = 0; q0 < zfrom; q0 += rows_per) {
             const int64_t q1 = std::min<int64_t>(q0 + rows_per, rows);
             const int64_t w = kv_tiles_of(mode, mask != nullptr, a.pre, a.next, lq[(size_t)b],
@@ -918,19 +993,18 @@ fia_status fia_get_workspace_size(const fia_tensor* query, const fia_tensor* key
                 tl.push_back({w, Tile{(int32_t)b, (int32_t)h, (int32_t)q0, (int32_t)q1, bi[(size_t)b]}});
         }
     }
-    std::stable_sort(tl.begin(), tl.end(), [](const W& x, const W& y) { return x.work > y.work; });
-    std::vector<Tile> tiles = zero_fill;
-    const std::vector<Tile> ordered =
-        xcd_order(tl.size(), [&](size_t i) { return tl[i].t; },
-                  [&](size_t i) { return (int)((tl[i].t.h / (QN / KVN)) % kNumXcds); }, zero_fill.size());
-    tiles.insert(tiles.end(), ordered.begin(), ordered.end());
+    sort_longest_first(tl);
+    const size_t n_zero = tiles.size();
+    xcd_order(tl.size(), [&](size_t i) { return tl[i].t; },
+              [&](size_t i) { return (int)((tl[i].t.h / (QN / KVN)) % kNumXcds); }, tiles, n_zero);
     if (tiles.size() > (size_t)INT32_MAX) return FIA_ERR_UNSUPPORTED;
     p->n_tiles = (int64_t)tiles.size();
     a.n_tiles = (int32_t)tiles.size();
     p->off_batch = 0;
-    uint64_t end = put(p->host_tables, 0, bi);
+    S.tables.clear();
+    uint64_t end = put(S.tables, 0, bi);
     p->off_tiles = align_up(end, 256);
-    put(p->host_tables, p->off_tiles, tiles);
+    put(S.tables, p->off_tiles, tiles);
     finish_tables(p.get());
     p->workspace_bytes = 0;                  // prefill needs no scratch
     *workspace_size = p->workspace_bytes;
@@ -1141,7 +1215,9 @@ fia_status bsa_get_workspace_size(const fia_tensor* query, const fia_tensor* key
     }
     // One tile per (batch, q block, 128-row slice of the block, head); a tile
     // never straddles two q blocks.  Padded layouts also cover padding rows.
-    std::vector<Tile> tiles;
+    PlanScratch& S = plan_scratch();
+    std::vector<Tile>& tiles = S.tiles;
+    tiles.clear();
     for (int64_t b = 0; b < B; ++b) {
         const int64_t rows = layout == LAYOUT_TND ? lq[(size_t)b] : gq.S;
         for (int64_t qb = 0; qb * X < rows; ++qb) {
@@ -1156,14 +1232,16 @@ fia_status bsa_get_workspace_size(const fia_tensor* query, const fia_tensor* key
     if (tiles.size() > (size_t)INT32_MAX) return FIA_ERR_UNSUPPORTED;
     // The workgroups of one kv head go to launch positions on one XCD (the
     // tiles of a kv head's GQA group then share that XCD's L2).
-    tiles = xcd_order(tiles.size(), [&](size_t i) { return tiles[i]; },
-                      [&](size_t i) { return (int)((tiles[i].h / (N1 / N2)) % kNumXcds); });
-    p->n_tiles = (int64_t)tiles.size();
-    a.n_tiles = (int32_t)tiles.size();
+    S.tiles2.clear();
+    xcd_order(tiles.size(), [&](size_t i) { return tiles[i]; },
+              [&](size_t i) { return (int)((tiles[i].h / (N1 / N2)) % kNumXcds); }, S.tiles2);
+    p->n_tiles = (int64_t)S.tiles2.size();
+    a.n_tiles = (int32_t)S.tiles2.size();
     p->off_batch = 0;
-    uint64_t end = put(p->host_tables, 0, bi);
+    S.tables.clear();
+    uint64_t end = put(S.tables, 0, bi);
     p->off_tiles = align_up(end, 256);
-    put(p->host_tables, p->off_tiles, tiles);
+    put(S.tables, p->off_tiles, S.tiles2);
     finish_tables(p.get());
     p->off_cnt = 0;
     p->off_idx = align_up(p->off_cnt + (uint64_t)p->n_rows * 4, 256);
