@@ -169,7 +169,7 @@ struct WorkTile {
 };
 struct PlanScratch {
     std::vector<unsigned char> tables;     // host image of the schedule tables
-    std::vector<Tile> tiles, tiles2;
+    std::vector<Tile> tiles;
     std::vector<WorkTile> wt, wt2;
     std::vector<size_t> idx, pos;
     std::vector<int32_t> pref;
@@ -186,16 +186,16 @@ void trim_scratch(PlanScratch& s)
     auto trim = [](auto& v) {
         if (v.capacity() * sizeof(v[0]) > kKeep) std::remove_reference_t<decltype(v)>().swap(v);
     };
-    trim(s.tables); trim(s.tiles); trim(s.tiles2); trim(s.wt); trim(s.wt2);
+    trim(s.tables); trim(s.tiles); trim(s.wt); trim(s.wt2);
     trim(s.idx); trim(s.pos); trim(s.pref);
 }
 
 // Launch order for n tiles given in priority order: position i runs on XCD
 // i % kNumXcds, so position i takes the first remaining tile that prefers
 // that XCD; when none is left, the first remaining tile of any XCD.  The
-// tiles are appended to `out`.
+// tiles are written to out[0, n).
 template <class Get, class Pref>
-void xcd_order(size_t n, Get get, Pref pref, std::vector<Tile>& out, size_t first_pos = 0)
+void xcd_order(size_t n, Get get, Pref pref, Tile* out, size_t first_pos = 0)
 {
     PlanScratch& S = plan_scratch();
     // tile indices bucketed by preferred XCD, each bucket in priority order
@@ -210,7 +210,6 @@ void xcd_order(size_t n, Get get, Pref pref, std::vector<Tile>& out, size_t firs
     for (int x = 0; x < kNumXcds; ++x) head[x] = fill[x] = start[x];
     S.idx.resize(n);
     for (size_t i = 0; i < n; ++i) S.idx[fill[S.pref[i]]++] = i;
-    out.reserve(out.size() + n);
     for (size_t pos = 0; pos < n; ++pos) {
         size_t x = (first_pos + pos) % (size_t)kNumXcds;
         if (head[x] == start[x + 1]) {
@@ -221,8 +220,16 @@ void xcd_order(size_t n, Get get, Pref pref, std::vector<Tile>& out, size_t firs
                     x = y;
                 }
         }
-        out.push_back(get(S.idx[head[x]++]));
+        out[pos] = get(S.idx[head[x]++]);
     }
+}
+
+// The table image gets `n` tiles at byte offset `off` (256-aligned); returns
+// where they go.
+Tile* tile_slots(std::vector<unsigned char>& buf, uint64_t off, size_t n)
+{
+    buf.resize(off + n * sizeof(Tile));
+    return reinterpret_cast<Tile*>(buf.data() + off);
 }
 
 // Stable sort of the work tiles by work, largest first (a counting sort;
@@ -969,7 +976,7 @@ fia_status fia_get_workspace_size(const fia_tensor* query, const fia_tensor* key
     PlanScratch& S = plan_scratch();
     std::vector<WorkTile>& tl = S.wt;
     tl.clear();
-    std::vector<Tile>& tiles = S.tiles;    // zero-fill workgroups, then the ordered rest
+    std::vector<Tile>& tiles = S.tiles;    // the zero-fill workgroups (launched first)
     tiles.clear();
     const int64_t zrows = std::max<int64_t>(1, ((int64_t)256 << 10) / (QN * Dv * 2));
     {
@@ -994,17 +1001,18 @@ fia_status fia_get_workspace_size(const fia_tensor* query, const fia_tensor* key
         }
     }
     sort_longest_first(tl);
-    const size_t n_zero = tiles.size();
-    xcd_order(tl.size(), [&](size_t i) { return tl[i].t; },
-              [&](size_t i) { return (int)((tl[i].t.h / (QN / KVN)) % kNumXcds); }, tiles, n_zero);
-    if (tiles.size() > (size_t)INT32_MAX) return FIA_ERR_UNSUPPORTED;
-    p->n_tiles = (int64_t)tiles.size();
-    a.n_tiles = (int32_t)tiles.size();
+    const size_t n_zero = tiles.size(), n_all = n_zero + tl.size();
+    if (n_all > (size_t)INT32_MAX) return FIA_ERR_UNSUPPORTED;
+    p->n_tiles = (int64_t)n_all;
+    a.n_tiles = (int32_t)n_all;
     p->off_batch = 0;
     S.tables.clear();
     uint64_t end = put(S.tables, 0, bi);
     p->off_tiles = align_up(end, 256);
-    put(S.tables, p->off_tiles, tiles);
+    Tile* slots = tile_slots(S.tables, p->off_tiles, n_all);
+    std::copy(tiles.begin(), tiles.end(), slots);
+    xcd_order(tl.size(), [&](size_t i) { return tl[i].t; },
+              [&](size_t i) { return (int)((tl[i].t.h / (QN / KVN)) % kNumXcds); }, slots + n_zero, n_zero);
     finish_tables(p.get());
     p->workspace_bytes = 0;                  // prefill needs no scratch
     *workspace_size = p->workspace_bytes;
@@ -1232,16 +1240,15 @@ fia_status bsa_get_workspace_size(const fia_tensor* query, const fia_tensor* key
     if (tiles.size() > (size_t)INT32_MAX) return FIA_ERR_UNSUPPORTED;
     // The workgroups of one kv head go to launch positions on one XCD (the
     // tiles of a kv head's GQA group then share that XCD's L2).
-    S.tiles2.clear();
-    xcd_order(tiles.size(), [&](size_t i) { return tiles[i]; },
-              [&](size_t i) { return (int)((tiles[i].h / (N1 / N2)) % kNumXcds); }, S.tiles2);
-    p->n_tiles = (int64_t)S.tiles2.size();
-    a.n_tiles = (int32_t)S.tiles2.size();
+    p->n_tiles = (int64_t)tiles.size();
+    a.n_tiles = (int32_t)tiles.size();
     p->off_batch = 0;
     S.tables.clear();
     uint64_t end = put(S.tables, 0, bi);
     p->off_tiles = align_up(end, 256);
-    put(S.tables, p->off_tiles, S.tiles2);
+    xcd_order(tiles.size(), [&](size_t i) { return tiles[i]; },
+              [&](size_t i) { return (int)((tiles[i].h / (N1 / N2)) % kNumXcds); },
+              tile_slots(S.tables, p->off_tiles, tiles.size()));
     finish_tables(p.get());
     p->off_cnt = 0;
     p->off_idx = align_up(p->off_cnt + (uint64_t)p->n_rows * 4, 256);
