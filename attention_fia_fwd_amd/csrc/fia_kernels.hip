@@ -9,7 +9,9 @@
 //                   share of all (batch, kv head, head chunk) token streams;
 //                   the GQA heads sharing a kv head are the 16 columns of
 //                   v_mfma_f32_16x16x32, so every K/V byte is read once;
-//                   pages are gathered through the block table.
+//                   pages are gathered through the block table.  The
+//                   decode kernels read the cache with the streaming (nt)
+//                   cache policy: each byte is read once per run.
 //   decode_split_i8 decode against an int8 KV cache (per-channel or
 //                   per-token scale and offset), the same column layout.
 //   decode_combine  merges the pieces of one (batch, head) by their LSE.
