@@ -33,7 +33,10 @@
  *   - Phase 1 launches no kernel.  It uploads the plan's schedule tables
  *     (per-batch offsets and the tile / split order, tens of bytes per tile)
  *     into device memory the plan owns, on the current device, with a
- *     synchronous copy; fia_plan_destroy frees them.  Where no device is
+ *     synchronous copy; fia_plan_destroy frees them.  Its host temporaries
+ *     live in per-thread buffers that keep their capacity between calls (a
+ *     buffer past 64 MB is released after the call), so phase-1 calls on
+ *     different threads may run at the same time.  Where no device is
  *     visible, phase 1 still validates and sizes, but the plan cannot run:
  *     phase 2 then returns FIA_ERR_HIP (it never uploads or allocates).
  *   - Phase 2 only enqueues kernels on `stream` (a hipStream_t; NULL = the
