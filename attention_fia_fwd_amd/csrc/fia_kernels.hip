@@ -1398,7 +1398,7 @@ __global__ __launch_bounds__(64) void decode_split(DecodeArgs a)
 __device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
 
 template <int D, int KM, int VM>
-__global__ __launch_bounds__(64) void decode_split_i8(DecodeArgs a)
+__global__ __launch_bounds__(64, 2) void decode_split_i8(DecodeArgs a)
 {
     constexpr int ST = kDecodeStep;       // 32 tokens per step
     constexpr int NK = D / 32;            // k-steps of S^T = K Q^T
@@ -1414,8 +1414,9 @@ __global__ __launch_bounds__(64) void decode_split_i8(DecodeArgs a)
     using O = Ops<FIA_BF16>;                 // Q K^T
     using OV = Ops<FIA_F16>;                 // P V
     __shared__ __attribute__((aligned(16))) uint16_t vbuf[ST * D];   // widened x (fp16), swizzled
-    __shared__ __attribute__((aligned(16))) uint8_t vst0[ST * D];    // bytes as loaded
+    __shared__ __attribute__((aligned(16))) uint8_t vst0[ST * D];    // bytes as loaded (three steps)
     __shared__ __attribute__((aligned(16))) uint8_t vst1[ST * D];
+    __shared__ __attribute__((aligned(16))) uint8_t vst2[ST * D];
 
     const int lane = threadIdx.x;
     const int n = lane & 15, qd = lane >> 4;
@@ -1596,25 +1597,34 @@ __global__ __launch_bounds__(64) void decode_split_i8(DecodeArgs a)
             o += 16;
             if (o >= bs) { o -= bs; ++p; }
         };
-        uint4 kfa[2][NKL], kfb[2][NKL];
-        Tok ta, tb_;
-        auto step = [&](int st, uint4 (&kcur)[2][NKL], uint4 (&knext)[2][NKL], uint8_t* vcur, uint8_t* vnext,
-                        const Tok& tcur, Tok& tnext) {
+        // AHEAD steps in flight (two, or one with per-token K values, whose
+        // registers would not fit a third set): AHEAD + 1 K register sets and
+        // byte buffers in rotation; step st issues step st + AHEAD into the
+        // set step st - 1 used.
+        constexpr int AHEAD = KM == 1 ? 1 : 2;
+        uint4 kfa[2][NKL], kfb[2][NKL], kfc[2][NKL];
+        Tok ta, tb_, tc;
+        auto issue_next = [&](int tt0, uint4 (&kf)[2][NKL], uint8_t* vb, Tok& tk) {
+            int pg1 = pg, off1 = off;
+            advance16(pg1, off1);
+            issue(tt0, pg, off, pg1, off1, kf, vb, tk);
+            pg = pg1; off = off1;
+            advance16(pg, off);
+        };
+        auto step = [&](int st, uint4 (&kcur)[2][NKL], uint4 (&knn)[2][NKL], uint8_t* vcur, uint8_t* vnn,
+                        const Tok& tcur, Tok& tnn) {
             const int tt0 = t0 + ST * st;
-            // pg/off point at the first sub-tile of step st + 1 here
-            if (st + 1 < nsteps) {
-                int pg1 = pg, off1 = off;
-                advance16(pg1, off1);
-                __builtin_amdgcn_s_waitcnt(FIA_LGKMCNT0);   // widening reads of the other byte buffer done
-                issue(tt0 + ST, pg, off, pg1, off1, knext, vnext, tnext);
-                pg = pg1; off = off1;
-                advance16(pg, off);
-                // step st landed; the next step's K and V loads (issued after its
-                // per-token values) stay in flight
-                __builtin_amdgcn_s_waitcnt(FIA_VMCNT(2 * (NKL + NVI8)));
-            } else {
-                __builtin_amdgcn_s_waitcnt(FIA_VMCNT(0));
+            // pg/off point at the first sub-tile of step st + AHEAD here
+            if (st + AHEAD < nsteps) {
+                __builtin_amdgcn_s_waitcnt(FIA_LGKMCNT0);   // widening reads of step st - 1's bytes done
+                issue_next(tt0 + AHEAD * ST, knn, vnn, tnn);
             }
+            // step st landed; the K and V loads of the (at most AHEAD) later
+            // steps stay in flight (per-token values are loaded before each
+            // step's K and V, so with them this waits for some of those too)
+            if (AHEAD == 2 && st + 2 < nsteps) __builtin_amdgcn_s_waitcnt(FIA_VMCNT(4 * (NKL + NVI8)));
+            else if (st + 1 < nsteps) __builtin_amdgcn_s_waitcnt(FIA_VMCNT(2 * (NKL + NVI8)));
+            else __builtin_amdgcn_s_waitcnt(FIA_VMCNT(0));
             __syncthreads();
             // widen this step's V bytes (signed) into the fp16 layout
 #pragma unroll
@@ -1705,16 +1715,19 @@ __global__ __launch_bounds__(64) void decode_split_i8(DecodeArgs a)
             }
         };
 
-        if (nsteps > 0) {
-            int pg1 = pg, off1 = off;
-            advance16(pg1, off1);
-            issue(t0, pg, off, pg1, off1, kfa, vst0, ta);
-            pg = pg1; off = off1;
-            advance16(pg, off);
-        }
-        for (int st = 0; st < nsteps; st += 2) {
-            step(st, kfa, kfb, vst0, vst1, ta, tb_);
-            if (st + 1 < nsteps) step(st + 1, kfb, kfa, vst1, vst0, tb_, ta);
+        if (nsteps > 0) issue_next(t0, kfa, vst0, ta);
+        if constexpr (AHEAD == 2) {
+            if (nsteps > 1) issue_next(t0 + ST, kfb, vst1, tb_);
+            for (int st = 0; st < nsteps; st += 3) {
+                step(st, kfa, kfc, vst0, vst2, ta, tc);
+                if (st + 1 < nsteps) step(st + 1, kfb, kfa, vst1, vst0, tb_, ta);
+                if (st + 2 < nsteps) step(st + 2, kfc, kfb, vst2, vst1, tc, tb_);
+            }
+        } else {
+            for (int st = 0; st < nsteps; st += 2) {
+                step(st, kfa, kfb, vst0, vst1, ta, tb_);
+                if (st + 1 < nsteps) step(st + 1, kfb, kfa, vst1, vst0, tb_, ta);
+            }
         }
 
         const float lt = quad_sum(l);
