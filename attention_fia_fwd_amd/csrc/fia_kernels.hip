@@ -1634,11 +1634,20 @@ __global__ __launch_bounds__(64, 2) void decode_split_i8(DecodeArgs a)
                 const uint4 raw = *(const uint4*)(vcur + r * D + 16 * c8);
                 const uint32_t w4[4] = {raw.x, raw.y, raw.z, raw.w};
                 uint32_t pk[8];
+                // x = u - 128 with u = x ^ 0x80: the fp16 bit pattern 0x6400 | u
+                // is 1024 + u exactly, and one packed fp16 add of -1152 leaves x
+                // (integers below 2048 are exact in fp16)
+                const f16x2 bias = {(_Float16)-1152.0f, (_Float16)-1152.0f};
 #pragma unroll
                 for (int e4 = 0; e4 < 4; ++e4) {
-                    const int w = (int)w4[e4];
-                    pk[2 * e4] = OV::pack2((float)((w << 24) >> 24), (float)((w << 16) >> 24));
-                    pk[2 * e4 + 1] = OV::pack2((float)((w << 8) >> 24), (float)(w >> 24));
+                    const uint32_t u = w4[e4] ^ 0x80808080u;
+                    // v_perm_b32 byte selectors: 0..3 take bytes of u (second
+                    // source), 4 takes 0x64 (first source); result bytes high to
+                    // low: 0x64, u1, 0x64, u0 (and u3, u2)
+                    const uint32_t lo2 = __builtin_amdgcn_perm(0x64646464u, u, 0x04010400u);
+                    const uint32_t hi2 = __builtin_amdgcn_perm(0x64646464u, u, 0x04030402u);
+                    pk[2 * e4] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, lo2) + bias);
+                    pk[2 * e4 + 1] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, hi2) + bias);
                 }
                 *(uint4*)(vbuf + r * D + 8 * ((2 * c8) ^ vswz(r))) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
                 *(uint4*)(vbuf + r * D + 8 * ((2 * c8 + 1) ^ vswz(r))) = make_uint4(pk[4], pk[5], pk[6], pk[7]);
