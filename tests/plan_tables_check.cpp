@@ -6,7 +6,8 @@
 //            the padding rows of every batch; the workgroups of one XCD bucket
 //            (kv head mod 8) appear in non-increasing kv-tile order;
 //   decode:  the pieces of each segment are contiguous, 16-aligned at their
-//            start, and cover exactly the segment's kv range; the waves' piece
+//            start, and cover exactly the segment's kv range (for the MLA
+//            sliding band from the first key any row can see); the waves' piece
 //            ranges are monotone and cover every piece; no wave's token load
 //            exceeds the common quota.
 // Prints one line per failure and "all ok" at the end; the exit status is the
@@ -201,6 +202,73 @@ static void check_decode(const char* name, int B, int QN, int KVN, const std::ve
     fia_plan_destroy(plan);
 }
 
+// MLA decode (query D 512 + rope 64, one kv head, paged), BNSD query of S
+// tokens; sparse_mode 0 (S 1), 3, or 4 with pre_tokens `pre` (keys below
+// Lkv - S - pre are outside every row's band and are not scheduled)
+static void check_mla(const char* name, int B, int QN, int S, const std::vector<int64_t>& L, int bs, int mode,
+                      int64_t pre)
+{
+    int64_t maxb = 1, nb = 0;
+    for (int64_t x : L) {
+        maxb = std::max<int64_t>(maxb, (x + bs - 1) / bs);
+        nb += (x + bs - 1) / bs;
+    }
+    fia_tensor q = T(FIA_BF16, {B, QN, S, 512}), o = q, qr = T(FIA_BF16, {B, QN, S, 64});
+    fia_tensor k = T(FIA_BF16, {std::max<int64_t>(nb, 1), bs, 512}), kr = T(FIA_BF16, {std::max<int64_t>(nb, 1), bs, 64});
+    fia_tensor lse = T(FIA_F32, {B, QN, S, 1}), bt = T(FIA_I32, {B, maxb});
+    fia_tensor tmpl = T(FIA_U8, {2048, 2048});
+    fia_params p;
+    fia_params_init(&p);
+    p.input_layout = "BNSD";
+    p.num_heads = QN;
+    p.num_key_value_heads = 1;
+    p.scale_value = 0.04;
+    p.block_size = bs;
+    p.sparse_mode = mode;
+    if (mode == 4) {
+        p.pre_tokens = pre;
+        p.next_tokens = 0;
+    }
+    p.return_softmax_lse = 1;
+    p.actual_seq_kvlen = L.data();
+    p.n_actual_seq_kvlen = B;
+    p.query_rope = &qr;
+    p.key_rope = &kr;
+    uint64_t ws = 0;
+    fia_plan* plan = nullptr;
+    g_tables.clear();
+    const fia_status st = fia_get_workspace_size(&q, &k, &k, mode >= 3 ? &tmpl : nullptr, &bt, &p, &o, &lse, &ws,
+                                                 &plan);
+    EXPECT(st == FIA_OK, "phase 1 status %d", (int)st);
+    const fia::DecodeArgs& d = plan->dec;
+    const int nseg = B * d.nhc, np = (int)plan->n_pieces, nw = (int)plan->n_waves;
+    EXPECT(d.mla_nw >= 2 && 16 * d.mla_nw >= d.Gc && d.Gc * d.nhc >= QN * S, "MLA chunking");
+    const fia::DecSeg* seg = (const fia::DecSeg*)(g_tables.data() + plan->off_batch);
+    const fia::DecPiece* pc = (const fia::DecPiece*)(g_tables.data() + plan->off_pieces);
+    const int32_t* wf = (const int32_t*)(g_tables.data() + plan->off_waves);
+    for (int sidx = 0; sidx < nseg; ++sidx) {
+        const int b = sidx / d.nhc;
+        const int64_t first =
+            mode == 4 ? std::min<int64_t>(L[b], std::max<int64_t>(0, L[b] - S - pre)) / 16 * 16 : 0;
+        if (first >= L[b]) {
+            EXPECT(seg[sidx].count == 0, "segment %d with no visible key has pieces", sidx);
+            continue;
+        }
+        int64_t at = first;
+        for (int i = seg[sidx].first; i < seg[sidx].first + seg[sidx].count; ++i) {
+            EXPECT(pc[i].seg == sidx && pc[i].t0 == at && pc[i].t1 > pc[i].t0 && pc[i].t0 % 16 == 0,
+                   "segment %d piece %d [%d, %d) at %lld", sidx, i, pc[i].t0, pc[i].t1, (long long)at);
+            EXPECT((pc[i].t1 - 1) / bs - pc[i].t0 / bs < 64, "piece %d spans more than 64 pages", i);
+            at = pc[i].t1;
+        }
+        EXPECT(at == L[b], "segment %d covers [%lld, %lld) of %lld", sidx, (long long)first, (long long)at,
+               (long long)L[b]);
+    }
+    EXPECT(np == 0 || (wf[0] == 0 && wf[nw] == np), "wave ranges do not cover the pieces");
+    EXPECT(nw <= 256, "more MLA workgroups (%d) than CUs", nw);
+    fia_plan_destroy(plan);
+}
+
 int main()
 {
     check_prefill("causal GQA, padded", 4, 32, 8, 4096, 3, {2700, 2151, 1117, 2011});
@@ -228,6 +296,10 @@ int main()
         std::snprintf(nm, sizeof nm, "random decode %d", r);
         check_decode(nm, B, KVN * G, KVN, L, bss[g() % 3]);
     }
+    check_mla("MLA decode, 128 heads", 6, 128, 1, {8192, 600, 16384, 17, 0, 3000}, 128, 0, 0);
+    check_mla("MLA, 4 tokens causal, 16-token pages", 3, 32, 4, {2000, 90, 5000}, 16, 3, 0);
+    check_mla("MLA sliding band", 4, 64, 2, {5000, 100, 4097, 1}, 128, 4, 1000);
+    check_mla("MLA band wider than the cache", 2, 16, 1, {700, 3000}, 64, 4, 100000);
     if (!failures) std::printf("all ok\n");
     return failures;
 }
