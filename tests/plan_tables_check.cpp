@@ -5,6 +5,8 @@
 //            one workgroup; zero-fill workgroups come first and cover exactly
 //            the padding rows of every batch; the workgroups of one XCD bucket
 //            (kv head mod 8) appear in non-increasing kv-tile order;
+//   block-sparse: every (batch, head, 128-row slice of a q block) is one
+//            workgroup and no workgroup straddles two q blocks;
 //   decode:  the pieces of each segment are contiguous, 16-aligned at their
 //            start, and cover exactly the segment's kv range (for the MLA
 //            sliding band from the first key any row can see); the waves' piece
@@ -269,6 +271,53 @@ static void check_mla(const char* name, int B, int QN, int S, const std::vector<
     fia_plan_destroy(plan);
 }
 
+// block-sparse prefill, BNSD, block shape [X, Y], lengths L (query = kv)
+static void check_bsa(const char* name, int B, int N1, int N2, int S, int X, int Y, const std::vector<int64_t>& L)
+{
+    const int D = 128;
+    fia_tensor q = T(FIA_BF16, {B, N1, S, D}), k = T(FIA_BF16, {B, N2, S, D}), o = q;
+    fia_tensor lse = T(FIA_F32, {B, N1, S, 1});
+    fia_tensor mask = T(FIA_U8, {B, N1, (S + X - 1) / X, (S + Y - 1) / Y});
+    bsa_params p;
+    bsa_params_init(&p);
+    p.q_input_layout = "BNSD";
+    p.kv_input_layout = "BNSD";
+    p.num_heads = N1;
+    p.num_key_value_heads = N2;
+    p.scale_value = 0.1;
+    p.block_shape[0] = X;
+    p.block_shape[1] = Y;
+    p.actual_seq_lengths = L.data();
+    p.n_actual_seq_lengths = B;
+    p.actual_seq_lengths_kv = L.data();
+    p.n_actual_seq_lengths_kv = B;
+    p.softmax_lse_flag = 1;
+    uint64_t ws = 0;
+    fia_plan* plan = nullptr;
+    g_tables.clear();
+    const fia_status st = bsa_get_workspace_size(&q, &k, &k, &mask, nullptr, nullptr, &p, &o, &lse, &ws, &plan);
+    EXPECT(st == FIA_OK, "phase 1 status %d", (int)st);
+    const int n = (int)plan->n_tiles;
+    const fia::Tile* t = n ? (const fia::Tile*)(g_tables.data() + plan->off_tiles) : nullptr;
+    std::map<std::tuple<int, int, int>, int> seen;
+    for (int i = 0; i < n; ++i) {
+        EXPECT(t[i].h >= 0 && t[i].q1 > t[i].q0 && t[i].q1 - t[i].q0 <= 128 && t[i].q0 / X == (t[i].q1 - 1) / X,
+               "entry %d rows [%d, %d) straddle a q block or exceed 128 rows", i, t[i].q0, t[i].q1);
+        ++seen[{t[i].b, t[i].h, t[i].q0}];
+    }
+    int expect = 0;
+    for (int b = 0; b < B; ++b)
+        for (int qb = 0; qb * X < S; ++qb)
+            for (int q0 = qb * X; q0 < std::min(S, (qb + 1) * X); q0 += 128)
+                for (int h = 0; h < N1; ++h) {
+                    ++expect;
+                    const int times = seen[std::make_tuple(b, h, q0)];
+                    EXPECT(times == 1, "batch %d head %d rows %d scheduled %d times", b, h, q0, times);
+                }
+    EXPECT(expect == n, "%d entries for %d (batch, head, row slice) items", n, expect);
+    fia_plan_destroy(plan);
+}
+
 int main()
 {
     check_prefill("causal GQA, padded", 4, 32, 8, 4096, 3, {2700, 2151, 1117, 2011});
@@ -300,6 +349,9 @@ int main()
     check_mla("MLA, 4 tokens causal, 16-token pages", 3, 32, 4, {2000, 90, 5000}, 16, 3, 0);
     check_mla("MLA sliding band", 4, 64, 2, {5000, 100, 4097, 1}, 128, 4, 1000);
     check_mla("MLA band wider than the cache", 2, 16, 1, {700, 3000}, 64, 4, 100000);
+    check_bsa("block-sparse [128, 128]", 2, 8, 2, 1000, 128, 128, {1000, 333});
+    check_bsa("block-sparse [256, 512]", 1, 4, 4, 3000, 256, 512, {2999});
+    check_bsa("block-sparse [64, 128]", 3, 6, 3, 700, 64, 128, {700, 1, 650});
     if (!failures) std::printf("all ok\n");
     return failures;
 }

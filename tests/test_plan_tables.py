@@ -4,8 +4,9 @@ The planner (attention_fia_fwd_amd/csrc/fia_plan.cpp) is compiled with
 stand-ins for its device hooks together with tests/plan_tables_check.cpp,
 which captures the table image phase 1 would upload and checks that every
 prefill row block is scheduled exactly once, that the zero-fill items cover
-exactly the padding rows, that each XCD bucket is in longest-first order, and
-that the decode pieces of every segment (GQA decode, MLA decode with and
+exactly the padding rows, that each XCD bucket is in longest-first order, that
+every block-sparse (batch, head, row slice) is one workgroup inside one q block,
+and that the decode pieces of every segment (GQA decode, MLA decode with and
 without the sliding band) tile its kv range exactly within the per-wave quota
 (the invariants the GPU parity tests rely on)."""
 import os
