@@ -2,7 +2,8 @@
 in per-thread buffers that are reused from call to call.  These tests build
 plans of every kind interleaved with each other and from several threads at
 once, and check that each plan's runs are bitwise identical to those of the
-same plan built alone, first in the process."""
+same plan built alone, first in the process; and that independent plans run
+at the same time on two streams give the same bits as run alone."""
 import threading
 
 import pytest
@@ -113,4 +114,35 @@ def test_plans_built_on_several_threads_at_once():
     assert not errors, errors
     for name, p in built.items():
         _same(_outputs(p), ref[name])
+        p.close()
+
+
+def test_plans_run_concurrently_on_two_streams():
+    """Independent plans (each with its own workspace) in flight at the same
+    time on two streams of default priority: every run equals the plan's run
+    alone on the default stream, bitwise.  Outputs are refilled with NaN
+    before each round, so each round must write every element."""
+    cases = _cases()
+    for _, c in cases:
+        to_dev(c)
+    plans = [(name, _plan(c)) for name, c in cases]
+    ref = {}
+    for name, p in plans:
+        say(f"[streams] alone: {name}")
+        ref[name] = _outputs(p)
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for rnd in range(4):
+        for _, p in plans:
+            p.out.fill_(float("nan"))
+            if p.lse is not None:
+                p.lse.fill_(float("nan"))
+        torch.cuda.synchronize()
+        say(f"[streams] round {rnd}: {len(plans)} plans on two streams")
+        for i, (_, p) in enumerate(plans[::-1] if rnd % 2 else plans):
+            with torch.cuda.stream(streams[i % 2]):
+                p.run()
+        torch.cuda.synchronize()
+        for name, p in plans:
+            _same((p.out, p.lse), ref[name])
+    for _, p in plans:
         p.close()
