@@ -210,31 +210,6 @@ __device__ __forceinline__ void dma16_burst(i32x4 rs, uint32_t lds_base, const u
                      : "s"(m0v), "v"(voff[0]), "v"(voff[1]), "v"(voff[2]), "v"(voff[3]), "s"(rs) : "memory");
 }
 
-// 4 bytes per lane from a buffer resource straight into LDS: lane i writes
-// lds_wave + 4 i (the same ordering contract as dma16).
-__device__ __forceinline__ void dma4(i32x4 rs, uint32_t lds_wave, uint32_t voff)
-{
-    const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_wave);
-    uint32_t keep;
-    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
-                 "buffer_load_dword %2, %3, 0 offen lds\n\ts_mov_b32 m0, %0"
-                 : "=&s"(keep) : "s"(m0v), "v"(voff), "s"(rs) : "memory");
-}
-
-// The same resource moved `d` bytes further (fewer valid bytes, never < 0);
-// offsets past the valid range still read as zero.
-__device__ __forceinline__ i32x4 rsrc_advance(i32x4 r, uint32_t d)
-{
-    const uint64_t addr = ((uint64_t)(uint32_t)r.x | ((uint64_t)((uint32_t)r.y & 0xffffu) << 32)) + d;
-    // wave-uniform values: readfirstlane keeps them in SGPRs
-    i32x4 o;
-    o.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)addr);
-    o.y = __builtin_amdgcn_readfirstlane((int)((uint32_t)(addr >> 32) & 0xffffu));
-    o.z = __builtin_amdgcn_readfirstlane((int)((uint32_t)r.z > d ? (uint32_t)r.z - d : 0u));
-    o.w = r.w;
-    return o;
-}
-
 // Cache policy of the decode kernels' KV-cache loads: nt (streaming).  Each
 // cached K / V byte is read once per run, and with the nt bit a plain
 // 16-byte read of a 4 GiB buffer moves 6.97 TB/s against 6.2 TB/s without
@@ -249,7 +224,8 @@ __device__ __forceinline__ void dma16_tracked(__amdgpu_buffer_rsrc_t rs, uint16_
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)lds_wave, 16, voff, 0, 0, AUX);
 }
 
-// dma16 / dma4 with the streaming (nt) cache policy.
+// dma16 with the streaming (nt) cache policy, and its 4-byte form (lane i
+// writes lds_wave + 4 i).
 __device__ __forceinline__ void dma16_nt(i32x4 rs, uint32_t lds_wave, uint32_t voff)
 {
     const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_wave);

@@ -40,7 +40,6 @@ from __future__ import annotations
 
 import argparse
 import json
-import math
 import os
 import sys
 import time
@@ -87,7 +86,7 @@ def allowed_pairs_fia(case) -> int:
 def allowed_pairs_bsa(case) -> int:
     import numpy as np
     m = case.block_mask.detach().cpu().numpy() != 0
-    B, N, nqb, nkb = m.shape
+    B, _, nqb, nkb = m.shape
     lq = case.lq if case.lq is not None else np.full(B, case.Sq)
     lkv = case.lkv if case.lkv is not None else np.full(B, case.Skv)
     total = 0

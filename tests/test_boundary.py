@@ -55,11 +55,6 @@ def test_status_strings():
         assert fia.fia_status_string(s).startswith(["FIA_OK", "FIA_ERR"][s > 0])
 
 
-def _desc(shape, dtype=torch.bfloat16):
-    t = torch.zeros(shape, dtype=dtype)
-    return t, fia.describe(t)
-
-
 def _params(**kw):
     p = fia.fia_params()
     fia.fia_params_init(p)
@@ -473,8 +468,6 @@ def test_bsa_validation():
     assert _bsa_phase1(q, k, k, m, num_heads=4, num_key_value_heads=2)[0] == _abi.FIA_OK
     assert _bsa_phase1(q, k, k, torch.zeros(1, 4, 3, 2, dtype=torch.uint8), num_heads=4,
                        num_key_value_heads=2)[0] == _abi.FIA_ERR_SHAPE
-    st = _bsa_phase1(q, k, k, m, num_heads=4, num_key_value_heads=2)
-    bad = fia.bsa_params()
     for field, val, code in [("inner_precise", 0, _abi.FIA_ERR_PARAM),
                              ("mask_type", 1, _abi.FIA_ERR_PARAM),
                              ("pre_tokens", 5, _abi.FIA_ERR_PARAM),
@@ -482,10 +475,8 @@ def test_bsa_validation():
         kw = dict(num_heads=4, num_key_value_heads=2)
         kw[field] = val
         assert _bsa_phase1(q, k, k, m, **kw)[0] == code, field
-    # Y must be a multiple of 128
+    # a head dim outside {64, 128}
     p_shape = dict(num_heads=4, num_key_value_heads=2)
-    pp = fia.bsa_params()
-    fia.bsa_params_init(pp)
     q2 = torch.zeros(1, 4, 300, 96, dtype=torch.bfloat16)
     k2 = torch.zeros(1, 2, 260, 96, dtype=torch.bfloat16)
     assert _bsa_phase1(q2, k2, k2, m, **p_shape)[0] == _abi.FIA_ERR_UNSUPPORTED

@@ -8,8 +8,7 @@ import torch
 
 import oracle
 import workloads as W
-from fia_gpu import (bsa_plan, compare, compare_rows, gather_rows, head_rows, run, sample_rows, say,
-                     seeded_subset, to_dev, TOL_LSE, TOL_OUT)
+from fia_gpu import bsa_plan, compare, compare_rows, head_rows, run, say, seeded_subset, to_dev
 
 pytestmark = pytest.mark.gpu
 

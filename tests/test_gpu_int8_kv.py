@@ -2,7 +2,6 @@
 the HIP path through the C ABI against the fp64 oracle on the same seeded
 inputs, each cached value standing for scale * (x + offset) per channel or
 per token."""
-import numpy as np
 import pytest
 import torch
 

@@ -3,15 +3,13 @@ V and K_rope pools) against the fp64 oracle: query layouts, both pool
 layouts, block sizes 16 and 128, Q_N from 1 to 128, query S 1..16 with
 bottom-right causal masking, kv lengths 0, 1 and ragged, NaN in every pool
 row that must not be read, zero and negative scales, and the full-size
-workload on sampled rows."""
-import numpy as np
+workload on whole batches (every head)."""
 import pytest
 import torch
 
 import oracle
 import workloads as W
-from fia_gpu import (compare, compare_rows, fia_plan, gather_rows, head_rows, run, sample_rows, say,
-                     seeded_subset, to_dev, TOL_LSE, TOL_OUT)
+from fia_gpu import compare, compare_rows, fia_plan, head_rows, run, say, seeded_subset, to_dev
 
 pytestmark = pytest.mark.gpu
 

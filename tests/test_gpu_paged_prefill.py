@@ -11,8 +11,8 @@ import torch
 
 import oracle
 import workloads as W
-from fia_gpu import (compare, compare_rows, fia_plan, gather_rows, head_rows, run, sample_rows,
-                     say, seeded_subset, to_dev, TOL_LSE, TOL_OUT)
+from fia_gpu import (compare, compare_rows, fia_plan, head_rows, run, say, seeded_subset, to_dev,
+                     TOL_LSE, TOL_OUT)
 
 pytestmark = pytest.mark.gpu
 

@@ -1,7 +1,6 @@
 """GPU parity: the HIP path (through the C ABI) against the fp64 oracle on
 the same seeded inputs, element by element, at sizes that span several tiles
 and ragged tails, plus the invariants that hold at any size."""
-import math
 import time
 
 import numpy as np

@@ -98,7 +98,7 @@ def dense_reference(case):
 
 def oracle_per_batch(case, out, lse):
     """Split oracle outputs into per-batch [QN, Lq, Dv] / [QN, Lq]."""
-    B, QN = case.B, case.QN
+    B = case.B
     lq = case.lq if case.lq is not None else np.full(B, case.Sq)
     res_o, res_l = [], []
     if case.layout == "TND":
@@ -177,7 +177,7 @@ def test_single_key_returns_that_value_exactly():
     # causal row 0 sees only key 0; band pre=next=0 sees only key i + delta
     case = W.make_fia(layout="BNSD", dtype=torch.bfloat16, B=1, QN=2, Sq=6, Skv=9, Dqk=16,
                       sparse_mode=4, pre_tokens=0, next_tokens=0, lq=[6], lkv=[9], seed=5)
-    out, lse = oracle.attention(case)
+    out, _ = oracle.attention(case)
     v = case.v.to(torch.float64).numpy()
     for h in range(2):
         for i in range(6):
