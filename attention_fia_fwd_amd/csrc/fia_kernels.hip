@@ -1,8 +1,9 @@
 // gfx950 (CDNA4) kernels of the fused inference attention forward.
 //
 //   attn_fwd        prefill and block-sparse prefill: one workgroup of 4
-//                   waves per 128 query rows of one head; K and V tiles of 64
-//                   tokens staged through LDS (double buffered); S^T = K Q^T
+//                   waves per 32-row block of up to 4 query heads of one GQA
+//                   group (block-sparse: 128 rows of one head); K and V tiles
+//                   of 64 tokens staged through LDS (double buffered); S^T = K Q^T
 //                   and O^T = V^T P^T on v_mfma_f32_32x32x16_{bf16,f16}; fp32
 //                   online softmax in registers; optional LSE.
 //   decode_split    decode: one wave per resident slot, each with an equal
@@ -96,24 +97,7 @@ struct Ops<FIA_F16> {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-
-
-// ---------------------------------------------------------------------------
-// Prefill / block-sparse attention.
-//
-// Workgroup: 4 waves, 128 query rows of one head; wave w owns rows
-// q0 + 32w .. q0 + 32w + 31.  Per 64-token kv tile:
-//   S^T (64 x 32 per wave) = K Q^T   two 32x32 MFMA tiles, Q in registers,
-//                                    K read from LDS (row-major, padded rows)
-//   online softmax on the S^T accumulators: lane (row, half) holds 32 of the
-//   row's 64 scores; the two halves exchange max and sum once.
-//   O^T (D_v x 32) += V^T P^T         P straight from the S^T registers as the
-//                                    B operand; V read from a row-major LDS
-//                                    tile with the gfx950 transpose read.
-// The kv index set of the B operand slots (from the S^T accumulator layout)
-// and of the A operand slots (from the transposed V reads) is the same, so
-// the contraction pairs each P value with its V row.
-// ---------------------------------------------------------------------------
+// Helpers of the prefill, block-sparse and decode kernels.
 typedef short s16x4 __attribute__((__vector_size__(4 * sizeof(short))));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
@@ -263,11 +247,12 @@ __device__ __forceinline__ float vmax(float x, float y) { return __builtin_eleme
 // ---------------------------------------------------------------------------
 // Prefill / block-sparse attention.
 //
-// Workgroup: 4 waves, 128 query rows of one head (a block-sparse tile never
-// straddles two q blocks); wave w owns rows q0 + 32w .. q0 + 32w + 31.  Per
-// 64-token kv tile (the q block's list for block-sparse):
+// Workgroup: 4 waves of 32 query rows each, over hg heads of one GQA group
+// (block-sparse: hg = 1, 128 rows of one head; a tile never straddles two q
+// blocks).  Per 64-token kv tile (the q block's list for block-sparse):
 //   S^T (64 x 32 per wave) = K Q^T   two 32x32 MFMA tiles, Q in registers,
-//                                    K read from LDS
+//                                    K read from LDS (16-byte chunks
+//                                    XOR-swizzled by row)
 //   online softmax on the S^T accumulators: lane (row, half) holds 32 of the
 //   row's 64 scores; the two halves exchange max and sum once.
 //   O^T (D_v x 32) += V^T P^T         P straight from the S^T registers as the
@@ -1375,8 +1360,8 @@ __global__ __launch_bounds__(64) void decode_split(DecodeArgs a)
 //                  sv_d (O_d + ov_d).
 // K comes straight into registers (lane (token n, quarter qd) holds the
 // contiguous d range [KB qd, KB qd + KB) of its row; Q uses the same d order);
-// V rows go direct-to-LDS as bytes and are widened into the swizzled bf16
-// layout the transposed reads of the 16-bit decode kernel use.
+// V rows go direct-to-LDS as bytes and are widened to fp16 into the swizzled
+// 16-bit layout the transposed reads of the 16-bit decode kernel use.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
 
