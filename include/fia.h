@@ -14,7 +14,9 @@
  *     a contiguous or (outside TND) paged KV cache;
  *   - decode (query S == 1 outside TND) against a contiguous or paged KV cache,
  *     with an optional per-(batch, kv token) mask; multi-token decode (query
- *     S up to 16, sparse_mode 3) takes the same split-KV path;
+ *     S up to 16, sparse_mode 3 or 0 without a mask) takes the same split-KV
+ *     path while the G * S (head, token) rows of a kv head number at most 16,
+ *     the prefill path beyond that;
  *   - block-sparse prefill (page "aclnnBlockSparseAttentionV2"), where a
  *     block mask selects the KV blocks each Q block attends to.
  *
@@ -230,8 +232,9 @@ fia_status fia_get_workspace_size(const fia_tensor* query, const fia_tensor* key
 /*
  * Phase 2: run `plan` on `stream` (a hipStream_t, NULL = default) with a
  * device workspace of at least the planned size (may be NULL when that size
- * is 0).  Returns FIA_ERR_WORKSPACE if it is too small, FIA_ERR_HIP if a copy
- * or launch fails.  The plan may be run any number of times.
+ * is 0).  Returns FIA_ERR_WORKSPACE if it is too small, FIA_ERR_HIP if a
+ * launch fails or phase 1 ran where no device was visible.  The plan may be
+ * run any number of times.
  */
 fia_status fia_run(void* workspace, uint64_t workspace_size, fia_plan* plan, void* stream);
 
@@ -306,8 +309,9 @@ fia_status bsa_run(void* workspace, uint64_t workspace_size, fia_plan* plan, voi
  * with the library's own static device scratch of
  * FIA_NOALLOC_MAX_WORKSPACE bytes as the workspace.  That array exists once
  * per GPU (each GPU the library runs on holds it until the process ends);
- * its device address is looked up on the first call on each device, with
- * that device current.  The call allocates nothing, copies nothing and does
+ * its device address is looked up once per device, with that device
+ * current: by the first phase-1 call that uploads a plan there, else by the
+ * first call of this function there.  The call allocates nothing, copies nothing and does
  * not synchronize; the caller still owns every input and output the plan
  * names.
  *   - Plans whose workspace size exceeds FIA_NOALLOC_MAX_WORKSPACE return
