@@ -182,3 +182,81 @@ def test_random_mla_decode(seed):
                              Sq=S, lq=lq, lkv=lkv, block_size=bs, pool_layout=int(rng.integers(2)),
                              seed=1110 + seed, extra_blocks=1, nan_pool=True)
     _check_fia(case)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_tnd_band_and_paged(seed):
+    # TND queries: the bottom-right band (sparse_mode 4) on a contiguous cache,
+    # or a paged cache with block size 128, 512 or 1024 (TND constraints)
+    rng = np.random.default_rng(1200 + seed)
+    dtype = torch.bfloat16 if rng.random() < 0.6 else torch.float16
+    KVN = int(rng.choice([1, 2]))
+    G = int(rng.choice([1, 2, 4, 8]))
+    B = int(rng.integers(1, 5))
+    pre, nxt = int(rng.integers(0, 400)), int(rng.integers(0, 200))
+    if seed % 2 == 0:
+        Dqk, Dv = [(64, 64), (128, 128), (192, 128)][rng.integers(3)]
+        lq = rng.integers(1, 400, size=B)
+        lkv = lq + rng.integers(0, 300, size=B)
+        case = W.make_fia(f"rand_tnd_band_{seed}", layout="TND", dtype=dtype, B=B, QN=KVN * G, KVN=KVN,
+                          Dqk=Dqk, Dv=Dv, sparse_mode=4, pre_tokens=pre, next_tokens=nxt, lq=lq,
+                          lkv=lkv, seed=1210 + seed, mask_kind="template")
+    else:
+        mode = int(rng.choice([0, 3, 4]))
+        lq = rng.integers(1, 300, size=B)
+        lkv = lq + rng.integers(0, 3000, size=B)
+        case = W.make_paged_prefill(f"rand_tnd_paged_{seed}", layout="TND", dtype=dtype, B=B,
+                                    QN=KVN * G, KVN=KVN, D=int(rng.choice([64, 128])), lq=lq, lkv=lkv,
+                                    block_size=(128, 512, 1024)[(seed // 2) % 3],
+                                    pool_layout=int(rng.integers(2)), sparse_mode=mode,
+                                    pre_tokens=pre if mode == 4 else W.INT_MAX,
+                                    next_tokens=nxt if mode == 4 else W.INT_MAX,
+                                    mask_kind="template" if mode else None, seed=1210 + seed,
+                                    extra_blocks=2, nan_pool=True)
+    _check_fia(case)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_mla_variants(seed):
+    # MLA decode beyond the plain form: the bottom-right band (sparse_mode 4,
+    # block size 64 or 128), TND queries, and value passed as the key tensor
+    rng = np.random.default_rng(1300 + seed)
+    kind = seed % 3
+    QN = int(rng.choice([1, 2, 4, 8, 16, 32, 64, 128]))
+    B = int(rng.integers(1, 4))
+    dtype = torch.bfloat16 if rng.random() < 0.6 else torch.float16
+    vk = kind == 2 or bool(rng.random() < 0.3)
+    if kind == 0:
+        S = (1, 2, 4)[(seed // 3) % 3]
+        lkv = rng.integers(S, 2500, size=B)
+        band = (int(rng.integers(0, 1500)), int(rng.choice([0, 1, 5])))
+        case = W.make_mla_decode(f"rand_mla_band_{seed}", dtype=dtype, B=B, QN=QN, Sq=S, lkv=lkv,
+                                 block_size=int(rng.choice([64, 128])), band=band,
+                                 pool_layout=int(rng.integers(2)), seed=1310 + seed,
+                                 extra_blocks=2, nan_pool=True)
+    elif kind == 1:
+        lq = rng.integers(1, 17, size=B)
+        lkv = rng.integers(0, 2500, size=B)
+        case = W.make_mla_decode(f"rand_mla_tnd_{seed}", layout="TND", dtype=dtype, B=B, QN=QN, lq=lq,
+                                 lkv=lkv, block_size=int(rng.choice([16, 128])), pool_layout=1,
+                                 seed=1310 + seed, extra_blocks=2, nan_pool=True)
+    else:
+        S = int(rng.choice([1, 1, 2, 3, 8, 16]))
+        lkv = rng.integers(0, 2500, size=B)
+        case = W.make_mla_decode(f"rand_mla_vk_{seed}", layout=str(rng.choice(["BSND", "BNSD", "BSH"])),
+                                 dtype=dtype, B=B, QN=QN, Sq=S, lkv=lkv,
+                                 block_size=int(rng.choice([16, 128])), pool_layout=int(rng.integers(2)),
+                                 seed=1310 + seed, extra_blocks=2, nan_pool=True)
+    if vk:
+        case.v = case.k
+    say(f"[rand] {case.name} layout={case.layout} QN={QN} B={B} Sq={case.Sq} mode={case.sparse_mode} "
+        f"band=({case.pre_tokens},{case.next_tokens}) lq={None if case.lq is None else list(case.lq)} "
+        f"lkv={list(case.lkv)} bs={case.block_size} value=key={vk} dtype={dtype}")
+    ref = oracle.attention(case)
+    to_dev(case)
+    if vk:
+        case.v = case.k                  # one device tensor for both
+    p = fia_plan(case)
+    out, lse = run(p)
+    compare(case, out, lse, *ref)
+    p.close()
