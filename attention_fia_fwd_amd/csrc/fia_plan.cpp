@@ -32,7 +32,30 @@ int64_t numel(const fia_tensor* t)
     return n;
 }
 
-bool valid_rank(const fia_tensor* t) { return t->ndim >= 1 && t->ndim <= 8; }
+// A descriptor the planner can do arithmetic on: rank 1..8, every dim in
+// [0, 2^31), and the product of its non-zero dims at most 2^48 elements, so
+// no product of its dims overflows int64.
+bool valid_rank(const fia_tensor* t)
+{
+    if (t->ndim < 1 || t->ndim > 8) return false;
+    int64_t vol = 1;
+    for (int i = 0; i < t->ndim; ++i) {
+        const int64_t d = t->dims[i];
+        if (d < 0 || d > kIntMax) return false;
+        if (d == 0) continue;
+        if (vol > (((int64_t)1 << 48) / d)) return false;
+        vol *= d;
+    }
+    return true;
+}
+
+// Every optional descriptor that is given passes valid_rank.
+bool valid_optional(std::initializer_list<const fia_tensor*> ts)
+{
+    for (const fia_tensor* t : ts)
+        if (t && !valid_rank(t)) return false;
+    return true;
+}
 
 bool is_half(int32_t d) { return d == FIA_F16 || d == FIA_BF16; }
 
@@ -333,11 +356,15 @@ fia_status fia_get_workspace_size(const fia_tensor* query, const fia_tensor* key
                                   const fia_tensor* softmax_lse, uint64_t* workspace_size,
                                   fia_plan** plan_out)
 {
+    if (plan_out) *plan_out = nullptr;
+    if (workspace_size) *workspace_size = 0;
     if (!query || !key || !value || !prm || !attention_out || !workspace_size || !plan_out)
         return FIA_ERR_NULLPTR;
-    *plan_out = nullptr;
-    *workspace_size = 0;
     if (!valid_rank(query) || !valid_rank(key) || !valid_rank(value) || !valid_rank(attention_out))
+        return FIA_ERR_SHAPE;
+    if (!valid_optional({atten_mask, block_table, softmax_lse, prm->dequant_scale_key,
+                         prm->dequant_scale_value, prm->dequant_offset_key, prm->dequant_offset_value,
+                         prm->query_rope, prm->key_rope}))
         return FIA_ERR_SHAPE;
 
     std::unique_ptr<fia_plan> p(new fia_plan());
@@ -1027,13 +1054,16 @@ fia_status bsa_get_workspace_size(const fia_tensor* query, const fia_tensor* key
                                   const fia_tensor* softmax_lse, uint64_t* workspace_size,
                                   fia_plan** plan_out)
 {
+    if (plan_out) *plan_out = nullptr;
+    if (workspace_size) *workspace_size = 0;
     if (!query || !key || !value || !prm || !attention_out || !workspace_size || !plan_out)
         return FIA_ERR_NULLPTR;
-    *plan_out = nullptr;
-    *workspace_size = 0;
     if (!block_sparse_mask) return FIA_ERR_NULLPTR;
     if (!valid_rank(query) || !valid_rank(key) || !valid_rank(value) ||
         !valid_rank(attention_out) || !valid_rank(block_sparse_mask))
+        return FIA_ERR_SHAPE;
+    if (!valid_optional({softmax_lse, prm->dequant_scale_query, prm->dequant_scale_key,
+                         prm->dequant_scale_value}))
         return FIA_ERR_SHAPE;
     // Constraints of the block-sparse page: no atten_mask, no paged cache,
     // fixed mask_type / inner_precise / pre / next.
@@ -1085,7 +1115,7 @@ fia_status bsa_get_workspace_size(const fia_tensor* query, const fia_tensor* key
     const int64_t N2 = prm->num_key_value_heads == 0 ? N1 : prm->num_key_value_heads;
     if (N1 <= 0 || N2 <= 0 || N1 < N2 || N1 % N2 != 0) return FIA_ERR_PARAM;
     const int64_t X = prm->block_shape[0], Y = prm->block_shape[1];
-    if (X <= 0 || Y <= 0 || Y % 128 != 0) return FIA_ERR_PARAM;
+    if (X <= 0 || Y <= 0 || X > kIntMax || Y > kIntMax || Y % 128 != 0) return FIA_ERR_PARAM;
     const bool have_q = prm->actual_seq_lengths != nullptr;
     const bool have_kv = prm->actual_seq_lengths_kv != nullptr;
     if (have_q != have_kv) return FIA_ERR_PARAM;

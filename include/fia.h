@@ -49,6 +49,11 @@
  *   - Results are deterministic: no atomics, fixed reduction order; two runs
  *     of one plan give bitwise identical outputs ("aclnnFusedInferAttention
  *     ScoreV5", constraints: deterministic computation).
+ *   - Every descriptor passed, required or optional, has rank 1..8, dims in
+ *     [0, 2^31) and at most 2^48 elements over its non-zero dims;
+ *     otherwise phase 1 returns FIA_ERR_SHAPE.
+ *   - A phase-1 call that fails sets *plan to NULL and *workspace_size to 0
+ *     (where those pointers are given) and owns nothing afterwards.
  *   - Errors are returned as fia_status; nothing is printed.
  */
 #ifndef FIA_H_
@@ -248,7 +253,7 @@ typedef struct bsa_params {
     int64_t num_heads;             /* N1 (query heads)                            */
     int64_t num_key_value_heads;   /* N2; N1 >= N2, N1 % N2 == 0; 0 = N1          */
     double  scale_value;           /* default 1.0                                 */
-    int64_t block_shape[2];        /* [X, Y]: X > 0, Y > 0 and Y % 128 == 0       */
+    int64_t block_shape[2];        /* [X, Y]: 0 < X, Y < 2^31 and Y % 128 == 0    */
     /* Host int64 arrays, both or neither; required for TND (cumulative). */
     const int64_t* actual_seq_lengths;
     int64_t        n_actual_seq_lengths;

@@ -609,3 +609,62 @@ def test_binding_fails_loudly_without_the_library(tmp_path):
             _abi.lib()
     finally:
         _abi._lib, _abi.LIB_PATH = saved
+
+
+def test_descriptor_bounds_and_cleared_outputs():
+    # every descriptor: rank 1..8, dims in [0, 2^31), at most 2^48 elements
+    # over its non-zero dims (FIA_ERR_SHAPE otherwise, also for optional ones)
+    q = torch.zeros(1, 4, 64, 64, dtype=torch.bfloat16)
+    k = torch.zeros(1, 2, 64, 64, dtype=torch.bfloat16)
+    out = torch.zeros_like(q)
+    lse = torch.zeros(1, 4, 64, 1, dtype=torch.float32)
+    p = _params(num_heads=4, num_key_value_heads=2, return_softmax_lse=1)
+
+    def call(mutate_q=None, mutate_lse=None):
+        dq, dl = fia.describe(q), fia.describe(lse)
+        if mutate_q:
+            mutate_q(dq)
+        if mutate_lse:
+            mutate_lse(dl)
+        st, _, plan = fia.fia_get_workspace_size(dq, fia.describe(k), fia.describe(k), None, None, p,
+                                                 fia.describe(out), dl)
+        fia.fia_plan_destroy(plan)
+        return st
+
+    assert call() == _abi.FIA_OK
+
+    def neg(d):
+        d.dims[2] = -64
+
+    def big(d):
+        d.dims[2] = 1 << 31
+
+    def vol(d):
+        d.ndim, d.dims[0], d.dims[1], d.dims[2], d.dims[3], d.dims[4] = 5, 1 << 20, 1 << 20, 1 << 10, 1, 1
+
+    def rank9(d):
+        d.ndim = 9
+
+    def rank0(d):
+        d.ndim = 0
+
+    for m in (neg, big, vol, rank9, rank0):
+        assert call(mutate_q=m) == _abi.FIA_ERR_SHAPE, m.__name__
+        assert call(mutate_lse=m) == _abi.FIA_ERR_SHAPE, m.__name__
+    # a failed phase 1 leaves no plan and a zero size, even when it fails on a
+    # missing argument
+    ws = ctypes.c_uint64(99)
+    plan = ctypes.c_void_p(12345)
+    st = _abi.lib().fia_get_workspace_size(ctypes.byref(fia.describe(q)), ctypes.byref(fia.describe(k)), None,
+                                           None, None, ctypes.byref(p), ctypes.byref(fia.describe(out)),
+                                           None, ctypes.byref(ws), ctypes.byref(plan))
+    assert st == _abi.FIA_ERR_NULLPTR and plan.value is None and ws.value == 0
+
+
+def test_bsa_block_shape_bounds():
+    q = torch.zeros(1, 4, 300, 128, dtype=torch.bfloat16)
+    k = torch.zeros(1, 2, 260, 128, dtype=torch.bfloat16)
+    m = torch.zeros(1, 4, 1, 1, dtype=torch.uint8)
+    for X, Y in [(1 << 31, 128), (128, 1 << 31), ((1 << 63) - 1, 128)]:
+        kw = dict(num_heads=4, num_key_value_heads=2, block_shape=(X, Y))
+        assert _bsa_phase1(q, k, k, m, **kw)[0] == _abi.FIA_ERR_PARAM, (X, Y)
