@@ -568,6 +568,11 @@ fia_status fia_get_workspace_size(const fia_tensor* query, const fia_tensor* key
 
     // ----- mask -----
     const int32_t mode = (int32_t)prm->sparse_mode;
+    // pre/next as band bounds: with sequence axes below 2^29, a bound past
+    // +-2^30 is the same as an infinite one, so both are clamped there once
+    // (no arithmetic below sees the int64 extremes)
+    const int64_t pre_c = std::max<int64_t>(-((int64_t)1 << 30), std::min<int64_t>((int64_t)1 << 30, prm->pre_tokens));
+    const int64_t next_c = std::max<int64_t>(-((int64_t)1 << 30), std::min<int64_t>((int64_t)1 << 30, prm->next_tokens));
     const uint8_t* mask = nullptr;
     int64_t mask_bstride = 0, mask_rstride = 0;
     if (!decode) {
@@ -827,7 +832,7 @@ fia_status fia_get_workspace_size(const fia_tensor* query, const fia_tensor* key
         // Lkv - Lq - pre are outside every row's band), 16-aligned
         auto first_token = [&](int64_t b) -> int64_t {
             if (!(mla && mode == 4)) return 0;
-            const int64_t lo = lkv[(size_t)b] - lq[(size_t)b] - std::min<int64_t>(prm->pre_tokens, (int64_t)1 << 40);
+            const int64_t lo = lkv[(size_t)b] - lq[(size_t)b] - pre_c;
             return std::min(lkv[(size_t)b], std::max<int64_t>(0, lo)) / 16 * 16;
         };
         int64_t total = 0;
@@ -887,8 +892,8 @@ fia_status fia_get_workspace_size(const fia_tensor* query, const fia_tensor* key
         int64_t blo = -band_lim, bhi = band_lim;
         if (mla && mode == 3) bhi = 0;
         if (mla && mode == 4) {
-            blo = std::max(-band_lim, std::min(band_lim, -prm->pre_tokens));
-            bhi = std::max(-band_lim, std::min(band_lim, prm->next_tokens));
+            blo = -pre_c;
+            bhi = next_c;
         }
         d.band_lo = (int32_t)blo;
         d.band_hi = (int32_t)bhi;
@@ -938,11 +943,8 @@ fia_status fia_get_workspace_size(const fia_tensor* query, const fia_tensor* key
     // Modes 1, 2 and 3 ignore pre/next; mode 0 without a mask ignores them
     // (sparse_mode parameter description).  With S < 2^29 a band bound past
     // +-2^30 is the same as an infinite one, so the kernel works in int32.
-    const int64_t band_lim = (int64_t)1 << 30;
-    a.pre = (mode == 4 || (mode == 0 && mask)) ? prm->pre_tokens : kIntMax;
-    a.next = (mode == 4 || (mode == 0 && mask)) ? prm->next_tokens : kIntMax;
-    a.pre = std::max(-band_lim, std::min(band_lim, a.pre));
-    a.next = std::max(-band_lim, std::min(band_lim, a.next));
+    a.pre = (mode == 4 || (mode == 0 && mask)) ? pre_c : (int64_t)1 << 30;
+    a.next = (mode == 4 || (mode == 0 && mask)) ? next_c : (int64_t)1 << 30;
     a.QN = (int32_t)QN;
     a.KVN = (int32_t)KVN;
     a.G = (int32_t)(QN / KVN);

@@ -97,7 +97,7 @@ struct Case {
 static void base_case(Case& c)
 {
     fia_params_init(&c.p);
-    const int kind = (int)pick(6);
+    const int kind = (int)pick(10);
     const int B = 1 + (int)pick(4), QN = 8, KVN = 2, S = 1 + (int)pick(300), D = coin(0.5) ? 64 : 128;
     const int dt = coin(0.5) ? FIA_BF16 : FIA_F16;
     c.p.num_heads = QN;
@@ -171,6 +171,20 @@ static void base_case(Case& c)
         c.p.key_quant_mode = c.p.value_quant_mode = (int64_t)pick(2);
         if (c.p.key_quant_mode == 0) c.ks = c.vs = T(FIA_BF16, {KVN, D});
         else c.ks = c.vs = T(FIA_F32, {B, 2048});
+        if (coin(0.4)) {   // paged pool, query S 1
+            c.p.block_size = 64;
+            c.k = c.v = T(FIA_I8, {128, KVN, 64, D});
+            c.bt = T(FIA_I32, {B, 32});
+            c.has_bt = true;
+        } else if (coin(0.4)) {   // multi-token, G * S <= 16, bottom-right causal
+            const int Sq = 1 + (int)pick(4);
+            c.q = T(FIA_BF16, {B, QN, Sq, D});
+            c.out = c.q;
+            c.lse = T(FIA_F32, {B, QN, Sq, 1});
+            c.p.sparse_mode = 3;
+            c.mask = T(FIA_U8, {2048, 2048});
+            c.has_mask = Sq > 1;
+        }
         c.ko = c.vo = c.ks;
         c.has_ks = c.has_vs = true;
         c.has_ko = c.has_vo = coin(0.5);
@@ -197,6 +211,57 @@ static void base_case(Case& c)
         c.lkv.assign((size_t)B, (int64_t)pick(4096));
         c.has_lkv = true;
         if (Sq > 1) { c.p.sparse_mode = 3; c.mask = T(FIA_U8, {2048, 2048}); c.has_mask = true; }
+        if (coin(0.4)) {   // bottom-right band, also at query S 1
+            c.p.sparse_mode = 4;
+            c.p.pre_tokens = (int64_t)pick(3000);
+            c.p.next_tokens = (int64_t)pick(3);
+            c.mask = T(FIA_U8, {2048, 2048});
+            c.has_mask = coin(0.7);
+        }
+        break;
+    }
+    case 6: {   // MLA decode with a TND query: 1..16 tokens per batch
+        const int MQN = 1 << pick(8);
+        c.p.input_layout = "TND";
+        c.p.num_heads = MQN;
+        c.p.num_key_value_heads = 1;
+        int64_t t = 0;
+        for (int b = 0; b < B; ++b) {
+            t += 1 + (int64_t)pick(16);
+            c.lq.push_back(t);
+            c.lkv.push_back((int64_t)pick(4096));
+        }
+        c.has_lq = c.has_lkv = true;
+        c.q = T(dt, {t, MQN, 512});
+        c.qr = T(dt, {t, MQN, 64});
+        c.out = c.q;
+        c.lse = T(FIA_F32, {t, MQN, 1});
+        c.k = c.v = T(dt, {128, 128, 512});
+        c.kr = T(dt, {128, 128, 64});
+        c.has_qr = c.has_kr = true;
+        c.p.block_size = 128;
+        c.bt = T(FIA_I32, {B, 32});
+        c.has_bt = true;
+        c.p.sparse_mode = coin(0.5) ? 3 : 0;
+        if (c.p.sparse_mode == 3) { c.mask = T(FIA_U8, {2048, 2048}); c.has_mask = true; }
+        break;
+    }
+    case 7: {   // TND prefill with D_qk 192, D_v 128
+        c.p.input_layout = "TND";
+        int64_t t = 0;
+        for (int b = 0; b < B; ++b) { t += 1 + (int64_t)pick(200); c.lq.push_back(t); }
+        c.lkv = c.lq;
+        c.has_lq = c.has_lkv = true;
+        c.q = T(dt, {t, QN, 192});
+        c.k = T(dt, {t, KVN, 192});
+        c.v = T(dt, {t, KVN, 128});
+        c.out = T(dt, {t, QN, 128});
+        c.lse = T(FIA_F32, {t, QN, 1});
+        c.p.sparse_mode = (int64_t)pick(5);
+        c.mask = T(FIA_U8, {2048, 2048});
+        c.has_mask = c.p.sparse_mode >= 2;
+        c.p.pre_tokens = (int64_t)pick(300);
+        c.p.next_tokens = (int64_t)pick(300);
         break;
     }
     default: {  // multi-token decode / prefill against a paged cache
@@ -367,15 +432,24 @@ static void bsa_case(long it)
     int64_t X = 128, Y = fp8 ? (coin(0.5) ? 256 : 512) : 128;
     p.block_shape[0] = X;
     p.block_shape[1] = Y;
-    fia_tensor q = T(dt, {B, N1, S, Dd}), k = T(dt, {B, N2, S, Dd}), v = k;
+    const int lay = (int)pick(3);   // BNSD, BSND, TND
+    const int64_t T_ = (int64_t)B * S;
+    fia_tensor q = lay == 0 ? T(dt, {B, N1, S, Dd}) : lay == 1 ? T(dt, {B, S, N1, Dd}) : T(dt, {T_, N1, Dd});
+    fia_tensor k = lay == 0 ? T(dt, {B, N2, S, Dd}) : lay == 1 ? T(dt, {B, S, N2, Dd}) : T(dt, {T_, N2, Dd});
+    fia_tensor v = k;
     fia_tensor m = T(FIA_U8, {B, N1, (S + X - 1) / X, (S + Y - 1) / Y});
-    fia_tensor out = T(fp8 ? FIA_BF16 : dt, {B, N1, S, Dd});
-    fia_tensor lse = T(FIA_F32, {B, N1, S, 1});
+    fia_tensor out = q;
+    out.dtype = fp8 ? FIA_BF16 : dt;
+    fia_tensor lse = lay == 2 ? T(FIA_F32, {T_, N1, 1}) : T(FIA_F32, {B, N1, S, 1});
     fia_tensor sq = T(FIA_F32, {B, N1, (S + 127) / 128, 1});
     fia_tensor sk = T(FIA_F32, {B, N2, (S + Y - 1) / Y, 1});
     fia_tensor am = T(FIA_U8, {2048, 2048}), bt = T(FIA_I32, {B, 8});
     std::vector<int64_t> lq((size_t)B, S), lkv((size_t)B, S);
-    bool has_len = coin(0.5), has_am = false, has_bt = false, has_lse = true;
+    if (lay == 2)   // TND: cumulative
+        for (int b = 0; b < B; ++b) lq[(size_t)b] = lkv[(size_t)b] = (int64_t)(b + 1) * S;
+    const char* lname = lay == 0 ? "BNSD" : lay == 1 ? "BSND" : "TND";
+    p.q_input_layout = p.kv_input_layout = lname;
+    bool has_len = lay == 2 || coin(0.5), has_am = false, has_bt = false, has_lse = true;
     bool has_sq = fp8, has_sk = fp8, has_sv = fp8;
     const char* layouts[] = {"BNSD", "BSND", "TND", "BSH", "", nullptr};
     const int muts = (int)pick(4);
