@@ -71,7 +71,9 @@ _lib = None
 def lib():
     global _lib
     if _lib is None:
-        _lib = ctypes.CDLL(build())
+        # FIA_ORACLE_LIB: an already built copy of oracle.c to load instead
+        # (the sanitizer check of the pins builds one)
+        _lib = ctypes.CDLL(os.environ.get("FIA_ORACLE_LIB") or build())
         _lib.oracle_attention.restype = ctypes.c_int
         _lib.oracle_block_sparse.restype = ctypes.c_int
         _lib.oracle_bsa_compact.restype = ctypes.c_int
